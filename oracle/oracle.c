@@ -1,0 +1,358 @@
+/*
+ * oracle.c -- plain CPU fp64 reference of selector-driven top-k sparse attention.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or constant with the HIP library, and the HIP library never calls it.
+ *
+ * It writes the definitions out directly, in double precision, from the exact
+ * fp32 / bf16 input values, with no blocking, fusion or reordering:
+ *
+ *   compress  K~_j = mean of the keys of block j (g consecutive tokens, one KV
+ *             head): the parameter-free mean pooling of keys that InfLLM-V2
+ *             uses (SparDA summary, Method).  L2SUM: each key divided by its
+ *             L2 norm, then the g keys summed (LSA deep-read, §2.2).  Blocks do
+ *             not overlap (stride = kernel = g).  A last partial block is the
+ *             mean over the tokens it has.  A zero key contributes zero to L2SUM.
+ *
+ *   select    one score per candidate block and GQA group: the group's query
+ *             heads summed, dotted with K~_j, over sqrt(d) (SparDA summary,
+ *             Method: one selector head per GQA group; LSA deep-read, §2.4:
+ *             the heads summed into one index query).  Candidates are the blocks
+ *             that lie wholly at or before the selection position p_sel and
+ *             hold at least one token outside the init/window set F(p_sel).
+ *             The k best by (score descending, block index ascending) are kept
+ *             and written in ascending block order.  With shared selection
+ *             (S3R review, sparse drafting: one selection reused by k drafts)
+ *             a sequence has one row at p_sel = first query position - 1, and
+ *             its score query sums every query of the sequence as well.
+ *
+ *   attend    softmax over the attended set only, o = sum_t softmax(l)_t v_t
+ *             with l_t = scale * q.k_t (PulseCol, §3.1 Eq. (1) and Eq. (2)
+ *             with M(S) = 0 on the set and -inf elsewhere; S3R review, sparse
+ *             drafting formula).  The set is the union of the init tokens, the
+ *             local window [p_sel - w + 1, p] and the tokens of the selected
+ *             blocks, cut at the query position p (SparDA summary, Method:
+ *             init tokens, sliding window and top-k blocks merged into one
+ *             sparse attention).
+ *
+ * Element types: 0 = fp32, 1 = bf16 given as raw 16-bit patterns.
+ * Layouts: Q [sum M_b, Hq, d]; K, V [sum N_b, Hkv, d]; K~ [Hkv, batch, nb_max, d];
+ * selection tables [Hkv, rows, kcap].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_MEAN 0
+#define OR_L2SUM 1
+
+static double elem(const void *base, int dtype, int64_t i)
+{
+    if (dtype == OR_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int or_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* First query position of sequence b: q_pos0[b], else right-aligned N_b - M_b. */
+static int64_t first_query_pos(int b, const int32_t *cu_q, const int32_t *cu_k, const int32_t *q_pos0)
+{
+    if (q_pos0)
+        return q_pos0[b];
+    return (int64_t)(cu_k[b + 1] - cu_k[b]) - (int64_t)(cu_q[b + 1] - cu_q[b]);
+}
+
+static int seq_of_query(int64_t i, int batch, const int32_t *cu_q)
+{
+    int b = 0;
+    while (b + 1 < batch && i >= cu_q[b + 1])
+        b++;
+    return b;
+}
+
+/* ---------------------------------------------------------------- compress */
+
+int or_compress(int batch, int h_kv, int d, const int32_t *cu_k, int g, int pool, int dtype,
+                const void *k, int64_t nb_max, double *k_cmp)
+{
+    if (g < 1 || d < 1)
+        return 1;
+    int64_t n_items = (int64_t)h_kv * batch * nb_max;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t it = 0; it < n_items; it++) {
+        int64_t j = it % nb_max;
+        int b = (int)((it / nb_max) % batch);
+        int c = (int)(it / (nb_max * batch));
+        int64_t n_b = cu_k[b + 1] - cu_k[b];
+        int64_t t0 = j * g, t1 = (j + 1) * (int64_t)g;
+        double *out = k_cmp + it * d;
+        if (t1 > n_b)
+            t1 = n_b;
+        for (int e = 0; e < d; e++)
+            out[e] = 0.0;
+        if (t0 >= n_b)
+            continue;
+        for (int64_t t = t0; t < t1; t++) {
+            int64_t row = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;
+            double scale = 1.0;
+            if (pool == OR_L2SUM) {
+                double ss = 0.0;
+                for (int e = 0; e < d; e++) {
+                    double x = elem(k, dtype, row + e);
+                    ss += x * x;
+                }
+                scale = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+            }
+            for (int e = 0; e < d; e++)
+                out[e] += elem(k, dtype, row + e) * scale;
+        }
+        if (pool == OR_MEAN)
+            for (int e = 0; e < d; e++)
+                out[e] /= (double)(t1 - t0);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ select */
+
+typedef struct {
+    double s;
+    int32_t j;
+} cand;
+
+/* Higher score first; equal scores: lower block index first. */
+static int cand_order(const void *a, const void *b)
+{
+    const cand *x = (const cand *)a, *y = (const cand *)b;
+    if (x->s > y->s)
+        return -1;
+    if (x->s < y->s)
+        return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static int int_order(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Token t (t <= p_sel) is in F(p_sel) = [0, min(n_init, p_sel + 1)) U [max(0, p_sel - w + 1), p_sel]. */
+static int in_fixed_set(int64_t t, int64_t p_sel, int n_init, int window)
+{
+    if (t < 0 || t > p_sel)
+        return 0;
+    return t < n_init || t >= p_sel - window + 1;
+}
+
+int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
+              const int32_t *q_pos0, int g, int topk, const int32_t *topk_per_seq, int n_init,
+              int window, int shared, int dtype, const void *q_sel, const double *k_cmp,
+              int64_t nb_max, const void *k, int64_t n_req, const int64_t *req_row,
+              const int32_t *req_kvh, int kcap, int32_t *out_idx, int32_t *out_n, double *out_sk,
+              double *out_sk1, double *out_floor, int32_t *out_ncand)
+{
+    int G = h_q / h_kv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_req; r++) {
+        int64_t row = req_row[r];
+        int c = req_kvh[r];
+        int b;
+        int64_t qa, qb, p_sel;
+        if (shared) {
+            b = (int)row;
+            qa = cu_q[b];
+            qb = cu_q[b + 1];
+            p_sel = first_query_pos(b, cu_q, cu_k, q_pos0) - 1;
+        } else {
+            b = seq_of_query(row, batch, cu_q);
+            qa = row;
+            qb = row + 1;
+            p_sel = first_query_pos(b, cu_q, cu_k, q_pos0) + (row - cu_q[b]);
+        }
+        int64_t n_b = cu_k[b + 1] - cu_k[b];
+        int64_t nb_b = (n_b + g - 1) / g;
+
+        /* score query: every row query, every head of group c, summed */
+        double *qs = (double *)calloc((size_t)d, sizeof(double));
+        for (int64_t i = qa; i < qb; i++)
+            for (int h = c * G; h < (c + 1) * G; h++)
+                for (int e = 0; e < d; e++)
+                    qs[e] += elem(q_sel, dtype, (i * h_q + h) * (int64_t)d + e);
+        double qnorm = 0.0;
+        for (int e = 0; e < d; e++)
+            qnorm += qs[e] * qs[e];
+        qnorm = sqrt(qnorm);
+
+        cand *cs = (cand *)malloc(sizeof(cand) * (size_t)(nb_b > 0 ? nb_b : 1));
+        int64_t nc = 0;
+        double kmax = 0.0;
+        for (int64_t j = 0; j < nb_b; j++) {
+            int64_t t0 = j * g, t1 = (j + 1) * (int64_t)g - 1;
+            if (t1 > n_b - 1)
+                t1 = n_b - 1;
+            if (t1 > p_sel)
+                continue; /* not wholly visible */
+            int outside_f = 0;
+            for (int64_t t = t0; t <= t1; t++)
+                if (!in_fixed_set(t, p_sel, n_init, window))
+                    outside_f = 1;
+            if (!outside_f)
+                continue; /* wholly inside init/window */
+            double dot = 0.0, kn = 0.0;
+            for (int e = 0; e < d; e++) {
+                double kv;
+                if (g == 1)
+                    kv = elem(k, dtype, ((cu_k[b] + j) * h_kv + c) * (int64_t)d + e);
+                else
+                    kv = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];
+                dot += qs[e] * kv;
+                kn += kv * kv;
+            }
+            if (sqrt(kn) > kmax)
+                kmax = sqrt(kn);
+            cs[nc].s = dot / sqrt((double)d);
+            cs[nc].j = (int32_t)j;
+            nc++;
+        }
+        qsort(cs, (size_t)nc, sizeof(cand), cand_order);
+        int64_t kr = topk_per_seq ? topk_per_seq[b] : topk;
+        int64_t ns = kr < nc ? kr : nc;
+        if (ns > kcap) {
+            bad |= 1;
+            ns = kcap;
+        }
+        int32_t *dst = out_idx + r * (int64_t)kcap;
+        for (int64_t s = 0; s < ns; s++)
+            dst[s] = cs[s].j;
+        qsort(dst, (size_t)ns, sizeof(int32_t), int_order);
+        for (int64_t s = ns; s < kcap; s++)
+            dst[s] = -1;
+        out_n[r] = (int32_t)ns;
+        if (out_ncand)
+            out_ncand[r] = (int32_t)nc;
+        if (out_sk)
+            out_sk[r] = ns >= 1 ? cs[ns - 1].s : NAN;
+        if (out_sk1)
+            out_sk1[r] = nc > ns ? cs[ns].s : NAN;
+        if (out_floor)
+            out_floor[r] = 1e-6 * qnorm * kmax / sqrt((double)d);
+        free(cs);
+        free(qs);
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------ attend */
+
+int or_attend(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
+              const int32_t *q_pos0, int g, int n_init, int window, int shared, double scale,
+              int dtype, const void *q, const void *k, const void *v, const int32_t *idx,
+              const int32_t *n_idx, int64_t idx_rows, int kcap, int64_t n_req,
+              const int64_t *req_q, const int32_t *req_h, double *out, double *lse,
+              int64_t *out_count, uint8_t *out_mask, int64_t mask_stride)
+{
+    int G = h_q / h_kv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_req; r++) {
+        int64_t i = req_q[r];
+        int h = req_h[r], c = h / G;
+        int b = seq_of_query(i, batch, cu_q);
+        int64_t q0 = first_query_pos(b, cu_q, cu_k, q_pos0);
+        int64_t p = q0 + (i - cu_q[b]);
+        int64_t p_sel = shared ? q0 - 1 : p;
+        int64_t row = shared ? b : i;
+        int64_t n_b = cu_k[b + 1] - cu_k[b];
+        int64_t nb_b = (n_b + g - 1) / g;
+
+        uint8_t *sel = (uint8_t *)calloc((size_t)(nb_b > 0 ? nb_b : 1), 1);
+        const int32_t *lst = idx + ((int64_t)c * idx_rows + row) * kcap;
+        int32_t nl = n_idx[(int64_t)c * idx_rows + row];
+        for (int32_t s = 0; s < nl && s < kcap; s++)
+            if (lst[s] >= 0 && lst[s] < nb_b)
+                sel[lst[s]] = 1;
+
+        /* attended set A: t <= p and (init or window or selected block) */
+        int64_t limit = p < n_b - 1 ? p : n_b - 1;
+        uint8_t *in_a = (uint8_t *)calloc((size_t)(limit + 1 > 0 ? limit + 1 : 1), 1);
+        int64_t count = 0;
+        for (int64_t t = 0; t <= limit; t++) {
+            int member = t < n_init || t >= p_sel - window + 1 || sel[t / g];
+            in_a[t] = (uint8_t)member;
+            count += member;
+        }
+
+        const int64_t qoff = (i * h_q + h) * (int64_t)d;
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(limit + 1 > 0 ? limit + 1 : 1));
+        double m = -INFINITY;
+        for (int64_t t = 0; t <= limit; t++) {
+            if (!in_a[t])
+                continue;
+            int64_t koff = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;
+            double dot = 0.0;
+            for (int e = 0; e < d; e++)
+                dot += elem(q, dtype, qoff + e) * elem(k, dtype, koff + e);
+            logit[t] = scale * dot;
+            if (logit[t] > m)
+                m = logit[t];
+        }
+        double den = 0.0;
+        double *o = out + r * (int64_t)d;
+        for (int e = 0; e < d; e++)
+            o[e] = 0.0;
+        for (int64_t t = 0; t <= limit; t++) {
+            if (!in_a[t])
+                continue;
+            double wgt = exp(logit[t] - m);
+            int64_t voff = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;
+            den += wgt;
+            for (int e = 0; e < d; e++)
+                o[e] += wgt * elem(v, dtype, voff + e);
+        }
+        for (int e = 0; e < d; e++)
+            o[e] = count ? o[e] / den : 0.0;
+        if (lse)
+            lse[r] = count ? m + log(den) : -INFINITY;
+        if (out_count)
+            out_count[r] = count;
+        if (out_mask) {
+            uint8_t *mk = out_mask + r * mask_stride;
+            memset(mk, 0, (size_t)mask_stride);
+            for (int64_t t = 0; t <= limit && t < mask_stride; t++)
+                mk[t] = in_a[t];
+        }
+        free(logit);
+        free(in_a);
+        free(sel);
+    }
+    return 0;
+}

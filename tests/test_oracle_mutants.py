@@ -1,0 +1,73 @@
+"""Plant mistakes in copies of oracle.c (on the CPU) and check that the pins
+catch each one: a dropped term, a wrong sign or index, an off-by-one edge, a
+transposed operand.  A mutant that passes every pin would mean the pins leave
+that part of the oracle unchecked."""
+import json
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "mean_divisor": ("out[e] /= (double)(t1 - t0);", "out[e] /= (double)(t1 - t0 + 1);"),
+    "l2_no_normalise": ("scale = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;", "scale = 1.0;"),
+    "compress_head0": ("int64_t row = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;",
+                       "int64_t row = ((cu_k[b] + t) * h_kv) * (int64_t)d;"),
+    "score_drops_head": ("for (int h = c * G; h < (c + 1) * G; h++)",
+                         "for (int h = c * G; h < (c + 1) * G - 1; h++)"),
+    "score_wrong_block": ("kv = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];",
+                          "kv = k_cmp[(((int64_t)c * batch + b) * nb_max + (j > 0 ? j - 1 : j)) * d + e];"),
+    "ties_to_higher": ("return (x->j > y->j) - (x->j < y->j);", "return (x->j < y->j) - (x->j > y->j);"),
+    "ascending_scores": ("if (x->s > y->s)\n        return -1;", "if (x->s < y->s)\n        return -1;"),
+    "visibility_off_by_one": ("if (t1 > p_sel)\n                continue;", "if (t1 > p_sel + 1)\n                continue;"),
+    "fixed_window_off_by_one": ("return t < n_init || t >= p_sel - window + 1;",
+                                "return t < n_init || t >= p_sel - window;"),
+    "attend_window_off_by_one": ("int member = t < n_init || t >= p_sel - window + 1 || sel[t / g];",
+                                 "int member = t < n_init || t >= p_sel - window + 2 || sel[t / g];"),
+    "attend_init_short": ("int member = t < n_init || t",
+                          "int member = t < n_init - 1 || t"),
+    "shared_psel": ("p_sel = first_query_pos(b, cu_q, cu_k, q_pos0) - 1;",
+                    "p_sel = first_query_pos(b, cu_q, cu_k, q_pos0);"),
+    "no_scale": ("logit[t] = scale * dot;", "logit[t] = dot;"),
+    "logit_uses_v": ("dot += elem(q, dtype, qoff + e) * elem(k, dtype, koff + e);",
+                     "dot += elem(q, dtype, qoff + e) * elem(v, dtype, koff + e);"),
+    "wrong_kv_head": ("int h = req_h[r], c = h / G;", "int h = req_h[r], c = h % h_kv;"),
+    "unweighted_v": ("o[e] += wgt * elem(v, dtype, voff + e);", "o[e] += elem(v, dtype, voff + e);"),
+}
+
+RUNNER = r"""
+import json, sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import pins
+failed = []
+for p in pins.ALL:
+    try:
+        p()
+    except Exception as e:
+        failed.append(p.__name__)
+print(json.dumps(failed))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    find, repl = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site not unique/present: {name}"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(find, repl))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", str(so),
+                           str(mut), "-lm"])
+    env = dict(os.environ, ORACLE_LIB=str(so), OMP_NUM_THREADS="4")
+    out = subprocess.run([sys.executable, "-c", RUNNER, ROOT, HERE], env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    failed = json.loads(out.stdout.strip().splitlines()[-1])
+    assert failed, f"mutant {name} passed every pin"

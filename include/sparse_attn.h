@@ -1,0 +1,163 @@
+/*
+ * sparse_attn.h -- C ABI of selector-driven top-k block-sparse attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One pass of the method is three calls on one HIP stream:
+ *
+ *   sparse_attn_compress  pool the keys of every block of `block` consecutive
+ *                         tokens, per KV head: the mean (the parameter-free
+ *                         mean pooling InfLLM-V2 uses; SparDA summary, Method)
+ *                         or the sum of L2-normalised keys (LSA deep-read, §2.2,
+ *                         4 keys pooled into one).
+ *   sparse_attn_select    score every candidate block with the query heads of a
+ *                         GQA group summed into one selector query,
+ *                         s_j = (sum_h q_h) . K~_j / sqrt(d) (SparDA summary,
+ *                         Method: one selector head per GQA group; LSA
+ *                         deep-read, §2.3-§2.4: one index table shared by all
+ *                         heads), keep the top-k, ties to the lower index.
+ *   sparse_attn_fwd       softmax attention restricted to the union of the init
+ *                         (sink) tokens, the local window and the selected blocks
+ *                         (PulseCol, §3.1 Eq. (1)-(2); S3R review, sparse drafting
+ *                         formula; SparDA summary, Method), online softmax with
+ *                         fp32 accumulation.
+ *
+ * Definitions used by every call (positions are 0-based, per sequence):
+ *   query i of sequence b sits at p = q0_b + i, q0_b = q_pos0[b] or N_b - M_b;
+ *   selection position p_sel = p (per-query selection), or q0_b - 1 for the one
+ *     row of sequence b when shared_selection = 1 (S3R drafts: the history up
+ *     to the verification boundary is selected once and reused by every draft);
+ *   block j = tokens [j*g, min((j+1)*g, N_b) - 1] = [j*g, e_j];
+ *   F(p_sel) = [0, min(n_init, p_sel+1)) U [max(0, p_sel-window+1), p_sel];
+ *   candidates C = { j : e_j <= p_sel and block j is not wholly inside F };
+ *   selected S = the first min(k, |C|) of C ordered by (score desc, j asc);
+ *   attended set A(p) = { t <= p : t < n_init, or t >= p_sel-window+1, or t in
+ *     a block of S }.
+ *
+ * Conventions:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates or frees device memory and keeps no state between calls.
+ *   - Q/K/V/O and k_cmp must be 16-byte aligned; all are row-major with the
+ *     head dimension contiguous.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Scalar and shape arguments are checked on the host before any HIP call;
+ *     a failed check returns a status and enqueues nothing.  Device-resident
+ *     contents (cu_seqlens monotone, q_pos0[b] + M_b <= N_b, topk_per_seq[b] <=
+ *     topk, finite inputs) are the caller's contract and are not checked.
+ *   - Nothing throws across the ABI.  sparse_attn_last_error() returns the
+ *     detail of the calling thread's last failure.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_ABI_VERSION 1
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1, /* bad scalar, shape, pointer or alignment            */
+    SA_ERR_UNSUPPORTED = 2, /* valid but not built (e.g. head_dim not 64 or 128)  */
+    SA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required          */
+    SA_ERR_DEVICE = 4       /* a HIP launch or runtime call failed                 */
+} sa_status;
+
+typedef enum sa_dtype { SA_DTYPE_F32 = 0, SA_DTYPE_BF16 = 1 } sa_dtype;
+typedef enum sa_pool { SA_POOL_MEAN = 0, SA_POOL_L2SUM = 1 } sa_pool;
+
+typedef struct sa_params {
+    int32_t batch;             /* B >= 1 sequences                                      */
+    int32_t h_q, h_kv;         /* query / KV heads; h_q % h_kv == 0, G = h_q / h_kv <= 64 */
+    int32_t head_dim;          /* d: 64 or 128                                          */
+    int32_t max_q, max_k;      /* max over b of M_b and N_b (grid sizing)               */
+    int64_t total_q, total_k;  /* sum M_b and sum N_b: rows of Q/O and of K/V           */
+    const int32_t *cu_seqlens_q; /* device [batch+1], packed query offsets, [0] = 0     */
+    const int32_t *cu_seqlens_k; /* device [batch+1], packed key offsets, [0] = 0       */
+    const int32_t *q_pos0;     /* device [batch] absolute position of query 0, or NULL  */
+    int32_t block;             /* g >= 1 tokens per pooled block (g = 1: token level)   */
+    int32_t pool;              /* sa_pool                                               */
+    int32_t topk;              /* k >= 0 blocks per row; the row capacity of `idx`      */
+    const int32_t *topk_per_seq; /* device [batch] per-sequence k (each <= topk), or NULL */
+    int32_t n_init;            /* sink tokens >= 0                                      */
+    int32_t window;            /* local window in tokens >= 1                           */
+    int32_t shared_selection;  /* 0: one row per query; 1: one row per sequence         */
+    float softmax_scale;       /* attention logit scale; 0 => 1/sqrt(head_dim)          */
+    int32_t dtype;             /* sa_dtype of Q, K, V and O                             */
+    void *timing_events[2];    /* optional hipEvent_t pair: when both are set,
+                                  sparse_attn_fwd records [0] right before and [1]
+                                  right after its main attention kernel on `stream`  */
+} sa_params;
+
+/* SPARSE_ATTN_ABI_VERSION of the built library. */
+int sparse_attn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *sparse_attn_status_string(sa_status s);
+
+/* Detail of the calling thread's last non-OK status ("" if none); never NULL. */
+const char *sparse_attn_last_error(void);
+
+/* Host-only check of every scalar and shape field; touches no device. */
+sa_status sparse_attn_validate(const sa_params *p);
+
+/* Bytes of device workspace that sparse_attn_select and sparse_attn_fwd need
+ * for these parameters (either pointer may be NULL).  0 means none needed. */
+sa_status sparse_attn_workspace_size(const sa_params *p, size_t *select_bytes, size_t *fwd_bytes);
+
+/* Pool the keys (SparDA summary, Method: InfLLM-V2 mean pooling of keys; LSA
+ * deep-read, §2.2: L2-normalise, then sum consecutive keys).
+ *   k      [total_k, h_kv, d] of dtype
+ *   k_cmp  [h_kv, batch, nbmax, d] fp32, nbmax = ceil(max_k / block); block j of
+ *          sequence b holds the mean (SA_POOL_MEAN) or the sum of k/|k|_2
+ *          (SA_POOL_L2SUM, a zero key adds zero) over the block's tokens, the
+ *          last block of a sequence over the tokens it has.  Rows
+ *          j >= ceil(N_b / block) are not written. */
+sa_status sparse_attn_compress(const sa_params *p, const void *k, float *k_cmp, void *stream);
+
+/* Recompute only the last n_tail_blocks pooled blocks of every sequence (the
+ * ones a decode step that appends keys changes); same layout and values as
+ * sparse_attn_compress for those rows.  n_tail_blocks >= 1. */
+sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, const void *k,
+                                    float *k_cmp, void *stream);
+
+/* Top-k block selection (SparDA summary, Method; LSA deep-read, §2.3; S3R
+ * review, sparse drafting: recent window + top-K by score).
+ *   q_sel  [total_q, h_q, d] of dtype: the selector queries (Q itself, or a
+ *          separate selector projection of the same shape)
+ *   k_cmp  pooled keys from sparse_attn_compress; ignored when block == 1 (the
+ *          raw keys `k` are scored) and may then be NULL
+ *   k      [total_k, h_kv, d]; read only when block == 1 (else may be NULL)
+ *   idx    [h_kv, rows, topk] int32 out: selected block indices of each row in
+ *          ascending order, padded with -1; rows = total_q, or batch when
+ *          shared_selection = 1
+ *   n_idx  [h_kv, rows] int32 out: number of selected blocks, min(k, |C|)
+ *   ws     workspace of at least select_bytes (sparse_attn_workspace_size).
+ * Scores are computed in fp32 from fp32 pooled keys and fp32-summed queries;
+ * equal scores keep the lower block index. */
+sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp,
+                             const void *k, int32_t *idx, int32_t *n_idx, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Sparse attention over A(p) for every query and query head (PulseCol, §3.1
+ * Eq. (2); S3R review, sparse drafting formula).
+ *   q      [total_q, h_q, d]; k, v [total_k, h_kv, d]; all of dtype
+ *   idx, n_idx  a selection table as written by sparse_attn_select
+ *   out    [total_q, h_q, d] of dtype
+ *   lse    [h_q, total_q] fp32 natural-log sum of exp of the scaled logits, or NULL
+ *   ws     workspace of at least fwd_bytes (sparse_attn_workspace_size).
+ * Logits, the running max and sum and the output accumulator are fp32. */
+sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v,
+                          const int32_t *idx, const int32_t *n_idx, void *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -103,13 +103,13 @@ def compress(w, k, cu_k=None) -> np.ndarray:
 
 
 def select(w, q_sel, k_cmp, k, rows=None, heads=None, q_pos0=None, cu_q=None, cu_k=None,
-           topk_per_seq="workload"):
+           topk_per_seq="workload", want_scores=False):
     """Selection for (row, KV head) requests; all rows x heads when ``rows`` is None.
 
     Returns dict(idx [n_req, kcap] int32 ascending and -1 padded, n [n_req],
     sk / sk1: the k-th and (k+1)-th scores in selection order (nan if absent),
     floor: the absolute near-tie floor, ncand: number of candidate blocks,
-    rows, heads).
+    rows, heads; scores [n_req, n_blocks] with nan for non-candidates if asked).
     """
     cu_q, cu_k, qp = _geom(w, cu_q, cu_k, q_pos0)
     n_rows = w.rows
@@ -129,15 +129,19 @@ def select(w, q_sel, k_cmp, k, rows=None, heads=None, q_pos0=None, cu_q=None, cu
     nb_max = -(-max(w.seqlens_k) // w.block)
     if k_cmp is not None:
         k_cmp = np.ascontiguousarray(k_cmp, dtype=np.float64)
+    n_blk = nb_max if w.block > 1 else max(w.seqlens_k)
+    scores = np.full((n, n_blk), np.nan) if want_scores else None
     rc = lib().or_select(
         w.batch, w.h_q, w.h_kv, w.head_dim, _ptr(cu_q, _i32p), _ptr(cu_k, _i32p),
         _ptr(qp, _i32p), w.block, int(w.topk), _ptr(tps, _i32p), w.n_init, w.window,
         int(w.shared_selection), w.dtype, _ptr(q_sel), _ptr(k_cmp, _f64p),
         ctypes.c_int64(nb_max), _ptr(k), ctypes.c_int64(n), _ptr(rows, _i64p),
         _ptr(heads, _i32p), kcap, _ptr(idx, _i32p), _ptr(nn, _i32p), _ptr(sk, _f64p),
-        _ptr(sk1, _f64p), _ptr(fl, _f64p), _ptr(ncand, _i32p))
+        _ptr(sk1, _f64p), _ptr(fl, _f64p), _ptr(ncand, _i32p), _ptr(scores, _f64p),
+        ctypes.c_int64(n_blk))
     assert rc == 0, "selection exceeded the row capacity"
-    return dict(idx=idx, n=nn, sk=sk, sk1=sk1, floor=fl, ncand=ncand, rows=rows, heads=heads)
+    return dict(idx=idx, n=nn, sk=sk, sk1=sk1, floor=fl, ncand=ncand, rows=rows, heads=heads,
+                scores=scores)
 
 
 def table(w, sel) -> tuple:

@@ -178,7 +178,8 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
               int window, int shared, int dtype, const void *q_sel, const double *k_cmp,
               int64_t nb_max, const void *k, int64_t n_req, const int64_t *req_row,
               const int32_t *req_kvh, int kcap, int32_t *out_idx, int32_t *out_n, double *out_sk,
-              double *out_sk1, double *out_floor, int32_t *out_ncand)
+              double *out_sk1, double *out_floor, int32_t *out_ncand, double *out_scores,
+              int64_t score_stride)
 {
     int G = h_q / h_kv;
     int bad = 0;
@@ -242,6 +243,8 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
                 kmax = sqrt(kn);
             cs[nc].s = dot / sqrt((double)d);
             cs[nc].j = (int32_t)j;
+            if (out_scores && j < score_stride)
+                out_scores[r * score_stride + j] = cs[nc].s;
             nc++;
         }
         qsort(cs, (size_t)nc, sizeof(cand), cand_order);

@@ -1,0 +1,139 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every
+symbol include/sparse_attn.h declares, and rejects bad arguments with the
+documented status before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import top_block_sparse_mean_amd as sa
+from top_block_sparse_mean_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = _lib.SA_ERR_INVALID_ARG, _lib.SA_ERR_UNSUPPORTED, _lib.SA_ERR_WORKSPACE
+FAKE = 1 << 20          # a 16-byte aligned stand-in device address: never dereferenced by host checks
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sparse_attn_[a-z_]+)\s*\(", text)))
+
+
+def params(**kw):
+    s = _lib.SaParams()
+    base = dict(batch=2, h_q=8, h_kv=2, head_dim=128, max_q=1, max_k=4096, total_q=2, total_k=8192,
+                cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, q_pos0=None, block=64, pool=0, topk=8,
+                topk_per_seq=None, n_init=64, window=128, shared_selection=0, softmax_scale=0.0, dtype=1)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(s, k, v)
+    return s
+
+
+def status(fn, *args):
+    return getattr(_lib.lib(), fn)(*args)
+
+
+def test_library_loads_and_version():
+    assert _lib.lib() is not None
+    assert sa.abi_version() == 1
+
+
+def test_every_declared_symbol_is_exported():
+    decl = declared_symbols()
+    assert set(decl) == set(_lib.EXPORTS), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sparse_attn_\w+)", out))
+    missing = [s for s in decl if s not in exported]
+    assert not missing, missing
+    for s in decl:
+        assert hasattr(_lib.lib(), s)
+
+
+def test_status_strings():
+    L = _lib.lib()
+    names = [L.sparse_attn_status_string(i).decode() for i in range(5)]
+    assert names[0] == "ok" and len(set(names)) == 5
+    assert L.sparse_attn_status_string(99)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, INVALID), ("h_q", 7, INVALID), ("h_kv", 0, INVALID), ("head_dim", 96, UNSUPPORTED),
+    ("max_q", 0, INVALID), ("max_k", 0, INVALID), ("total_k", 10, INVALID), ("cu_seqlens_q", None, INVALID),
+    ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID),
+    ("n_init", -2, INVALID), ("window", 0, INVALID), ("shared_selection", 2, INVALID), ("dtype", 5, INVALID),
+    ("softmax_scale", -1.0, INVALID), ("softmax_scale", float("inf"), INVALID),
+    ("h_q", 2 * 65, UNSUPPORTED)])
+def test_validate_rejects(field, value, code):
+    p = params(**{field: value})
+    if field == "h_q" and value == 130:
+        p.h_kv = 2
+    assert status("sparse_attn_validate", ctypes.byref(p)) == code
+    msg = _lib.lib().sparse_attn_last_error().decode()
+    assert msg
+
+
+def test_validate_accepts_and_clears_error():
+    assert status("sparse_attn_validate", None) == INVALID
+    assert status("sparse_attn_validate", ctypes.byref(params())) == 0
+    assert _lib.lib().sparse_attn_last_error().decode() == ""
+
+
+def _ws(p):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert status("sparse_attn_workspace_size", ctypes.byref(p), ctypes.byref(a), ctypes.byref(b)) == 0
+    return a.value, b.value
+
+
+def test_workspace_sizes():
+    # decode shape: fused selection needs no workspace; attention splits need partials
+    sel, fwd = _ws(params())
+    assert sel == 0 and fwd > 0 and fwd % (130 * 4) == 0
+    # prefill: scores of every (row, block) are kept: h_kv * rows * nb_max * 4
+    p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
+    sel, fwd = _ws(p)
+    assert sel == 2 * 4096 * 64 * 4
+    # token-level shared selection with long rows: scores in the workspace
+    p = params(block=1, shared_selection=1, max_q=6, total_q=12, max_k=20000, total_k=40000, topk=3000)
+    sel, _ = _ws(p)
+    assert sel == 2 * 2 * 20000 * 4
+    # k = 0: nothing to score
+    assert _ws(params(topk=0))[0] == 0
+
+
+def test_calls_reject_null_and_misaligned_pointers():
+    p = ctypes.byref(params())
+    vp = ctypes.c_void_p
+    assert status("sparse_attn_compress", p, None, vp(FAKE), None) == INVALID
+    assert status("sparse_attn_compress", p, vp(FAKE + 2), vp(FAKE), None) == INVALID
+    assert status("sparse_attn_compress_tail", p, 0, vp(FAKE), vp(FAKE), None) == INVALID
+    assert status("sparse_attn_select", p, None, vp(FAKE), None, vp(FAKE), vp(FAKE), None, 0, None) == INVALID
+    assert status("sparse_attn_select", p, vp(FAKE), None, None, vp(FAKE), vp(FAKE), None, 0, None) == INVALID
+    assert status("sparse_attn_fwd", p, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), None, None, 0,
+                  None) == INVALID
+    assert status("sparse_attn_fwd", p, vp(FAKE + 8), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
+                  None, 0, None) == INVALID
+
+
+def test_calls_reject_small_workspace():
+    p = params()
+    _, fwd = _ws(p)
+    vp = ctypes.c_void_p
+    r = status("sparse_attn_fwd", ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+               None, vp(FAKE), fwd - 1, None)
+    assert r == WORKSPACE
+    assert str(fwd) in _lib.lib().sparse_attn_last_error().decode()
+    p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
+    r = status("sparse_attn_select", ctypes.byref(p), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), None, 0, None)
+    assert r == WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.lib()

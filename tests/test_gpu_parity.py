@@ -1,0 +1,170 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Small workloads: every row and every (query, head) compared.  Full-size
+workloads: the launch configuration the benchmark times, compared on sampled
+rows and requests the oracle computes one by one.  Edge cases: k = 0, k >=
+|C| (dense), no sink, sequences with no candidates, ragged tails, head_dim
+64, GQA group 1, explicit query offsets.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import top_block_sparse_mean_amd as sa
+from workloads import DTYPE_BF16, DTYPE_F32, FULL, POOL_L2SUM, POOL_MEAN, Workload, generate, small
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    torch.cuda.set_device(0)
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_small_workload_parity(name):
+    w = small(name)
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
+def test_tiny_fp32_prefill_full():
+    w = FULL["tiny_fp32_prefill"]()
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
+EDGE = {
+    "k0": dict(topk=0),
+    "dense": dict(topk=4096),
+    "no_sink": dict(n_init=0),
+    "wide_window": dict(window=1000),
+    "odd_block": dict(block=7, topk=5, n_init=3, window=9),
+    "d64_bf16": dict(head_dim=64),
+    "group1": dict(h_q=8, h_kv=8),
+    "l2sum": dict(pool=POOL_L2SUM, block=4, topk=9),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(case):
+    base = Workload(name="edge", dtype=DTYPE_BF16, h_q=8, h_kv=2, head_dim=128,
+                    seqlens_k=[700, 129, 64, 1, 333], seqlens_q=[700, 5, 64, 1, 1], block=16,
+                    pool=POOL_MEAN, topk=6, n_init=16, window=32, seed=77)
+    w = base.scaled(**EDGE[case])
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
+def test_fp32_d64_decode_and_prefill_mix():
+    w = Workload(name="mix", dtype=DTYPE_F32, h_q=4, h_kv=1, head_dim=64, seqlens_k=[300, 1200, 95],
+                 seqlens_q=[300, 3, 95], block=32, pool=POOL_MEAN, topk=3, n_init=32, window=64, seed=5)
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
+def test_explicit_query_positions():
+    """q_pos0 given (queries not right-aligned): selection and causality follow it."""
+    w = Workload(name="qpos", dtype=DTYPE_BF16, h_q=4, h_kv=2, head_dim=128, seqlens_k=[900, 500],
+                 seqlens_q=[40, 7], block=16, pool=POOL_MEAN, topk=5, n_init=16, window=48, seed=9)
+    q_pos0 = [600, 100]
+    x, xg = parity.gen_pair(w)
+    p = sa.Params.from_lengths(w.seqlens_q, w.seqlens_k, device="cuda", h_q=4, h_kv=2, head_dim=128,
+                               block=16, topk=5, n_init=16, window=48, q_pos0=q_pos0, dtype=torch.bfloat16)
+    kc = sa.compress(p, xg["k"])
+    idx, n_idx = sa.select(p, xg["q"], kc, xg["k"])
+    out = sa.fwd(p, xg["q"], xg["k"], xg["v"], idx, n_idx)
+    kco = oracle.compress(w, x["k"])
+    sel = oracle.select(w, x["q"], kco, x["k"], q_pos0=q_pos0)
+    gi, gn = idx.cpu().numpy(), n_idx.cpu().numpy()
+    for r, (row, c) in enumerate(zip(sel["rows"], sel["heads"])):
+        assert gn[c, row] == sel["n"][r]
+        assert list(gi[c, row, :gn[c, row]]) == list(sel["idx"][r, :sel["n"][r]]) or parity.near_tie(sel, r)
+    att = oracle.attend(w, x["q"], x["k"], x["v"], gi, gn, q_pos0=q_pos0)
+    parity.check_output(w, out.float().cpu().reshape(-1, 128), att["out"])
+
+
+def test_shared_selection_drafts_share_one_set():
+    w = small("bf16_draft_decode")
+    x, xg = parity.gen_pair(w)
+    r = parity.full_check(w, x, xg)
+    assert r["gpu"]["idx"].shape[1] == w.batch      # one row per sequence
+
+
+def test_deterministic():
+    w = small("bf16_prefill_128k")
+    x, xg = parity.gen_pair(w)
+    a = parity.run_gpu(w, xg)
+    b = parity.run_gpu(w, xg)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["n_idx"], b["n_idx"])
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_compress_tail_matches_full():
+    w = small("bf16_decode_32k")
+    x, xg = parity.gen_pair(w)
+    p = parity.params_for(w)
+    full = sa.compress(p, xg["k"])
+    tail = torch.full_like(full, float("nan"))
+    sa.compress_tail(p, 2, xg["k"], tail)
+    for b, n in enumerate(w.seqlens_k):
+        nb = -(-n // w.block)
+        lo = max(0, nb - 2)
+        assert torch.equal(tail[:, b, lo:nb], full[:, b, lo:nb])
+        assert torch.isnan(tail[:, b, :lo]).all()
+
+
+# ---------------------------------------------------------------- full size, sampled
+
+def _sampled(w, n_rows, n_req, seed=0):
+    rng = np.random.default_rng(seed)
+    x, xg = parity.gen_pair(w, gen_on_device=True)
+    gp = parity.run_gpu(w, xg)
+    kc = oracle.compress(w, x["k"]) if w.block > 1 else None
+    if kc is not None:
+        bsel = rng.choice(w.batch, size=min(w.batch, 4), replace=False)
+        for b in bsel:
+            sub = w.scaled(seqlens_k=[w.seqlens_k[b]], seqlens_q=[w.seqlens_q[b]])
+            parity.check_compress(sub, gp["k_cmp"][:, b:b + 1], kc[:, b:b + 1])
+    rows = rng.choice(w.rows, size=min(w.rows, n_rows), replace=False)
+    rows = np.repeat(rows, w.h_kv)
+    heads = np.tile(np.arange(w.h_kv), len(rows) // w.h_kv)
+    sel, n_flag = parity.check_select(w, x, kc, gp["idx"], gp["n_idx"], rows=rows, heads=heads)
+    reqs = rng.choice(w.total_q, size=min(w.total_q, n_req), replace=False)
+    hs = rng.integers(0, w.h_q, size=len(reqs))
+    att = oracle.attend(w, x["q"], x["k"], x["v"], gp["idx"], gp["n_idx"], reqs=reqs, heads=hs)
+    gout = gp["out"].reshape(w.total_q, w.h_q, w.head_dim)[reqs, hs].double().numpy()
+    parity.check_output(w, gout, att["out"])
+    # GPU attention on a table whose sampled rows hold the oracle's selection
+    idx2, n2 = gp["idx"].copy(), gp["n_idx"].copy()
+    idx2[sel["heads"], sel["rows"]] = sel["idx"]
+    n2[sel["heads"], sel["rows"]] = sel["n"]
+    out2 = sa.fwd(gp["p"], xg["q"], xg["k"], xg["v"], torch.from_numpy(idx2).cuda(), torch.from_numpy(n2).cuda())
+    row_of = (lambda i: np.searchsorted(np.cumsum(w.seqlens_q), i, side="right")) if w.shared_selection \
+        else (lambda i: i)
+    mask = np.isin(np.array([row_of(i) for i in reqs]), sel["rows"])
+    if mask.any():
+        att2 = oracle.attend(w, x["q"], x["k"], x["v"], idx2, n2, reqs=reqs[mask], heads=hs[mask])
+        g2 = out2.float().cpu().reshape(w.total_q, w.h_q, w.head_dim)[reqs[mask], hs[mask]].double().numpy()
+        parity.check_output(w, g2, att2["out"], "output on oracle rows")
+    return n_flag
+
+
+def test_full_decode_32k_sampled():
+    parity_flags = _sampled(FULL["bf16_decode_32k"](), n_rows=32, n_req=512)
+    assert parity_flags <= 8
+
+
+def test_full_prefill_128k_sampled():
+    _sampled(FULL["bf16_prefill_128k"](), n_rows=96, n_req=384)
+
+
+def test_full_draft_decode_sampled():
+    _sampled(FULL["bf16_draft_decode"](), n_rows=64, n_req=768)
+
+
+def test_full_chunked_prefill_1m_sampled():
+    _sampled(FULL["bf16_chunked_prefill_1m"](), n_rows=24, n_req=256)

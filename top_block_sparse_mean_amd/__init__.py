@@ -1,0 +1,166 @@
+"""Selector-driven top-k block-sparse attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/sparse_attn.h.  It only marshals
+arguments: every step of the path (pooling, scoring, top-k, attention) runs in
+the HIP kernels of libsparse_attn.so.  PyTorch provides device memory and the
+current stream.  There is no CPU fallback: if the library is not built, every
+call raises.
+
+    p = Params.from_lengths(seqlens_q, seqlens_k, device="cuda", h_q=32, h_kv=8,
+                            head_dim=128, block=64, topk=32, n_init=64, window=128,
+                            dtype=torch.bfloat16)
+    k_cmp = compress(p, k)
+    idx, n_idx = select(p, q, k_cmp, k)
+    out = fwd(p, q, k, v, idx, n_idx)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
+                   SA_POOL_MEAN, SaParams, SparseAttnError, check, lib)
+
+__all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "select", "fwd",
+           "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "LIB_PATH", "EXPORTS"]
+
+_DT = {torch.float32: SA_DTYPE_F32, torch.bfloat16: SA_DTYPE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Params:
+    """One call configuration (sa_params); holds the device tensors it points at."""
+
+    def __init__(self, *, batch: int, h_q: int, h_kv: int, head_dim: int, cu_seqlens_q: torch.Tensor,
+                 cu_seqlens_k: torch.Tensor, max_q: int, max_k: int, total_q: int, total_k: int,
+                 block: int, topk: int, n_init: int, window: int, dtype=torch.bfloat16,
+                 pool: int = SA_POOL_MEAN, shared_selection: int = 0,
+                 topk_per_seq: Optional[torch.Tensor] = None, q_pos0: Optional[torch.Tensor] = None,
+                 softmax_scale: float = 0.0):
+        self._keep = (cu_seqlens_q, cu_seqlens_k, topk_per_seq, q_pos0)
+        self.dtype = dtype
+        s = SaParams()
+        s.batch, s.h_q, s.h_kv, s.head_dim = batch, h_q, h_kv, head_dim
+        s.max_q, s.max_k, s.total_q, s.total_k = max_q, max_k, total_q, total_k
+        s.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        s.cu_seqlens_k = cu_seqlens_k.data_ptr()
+        s.q_pos0 = None if q_pos0 is None else q_pos0.data_ptr()
+        s.block, s.pool, s.topk = block, pool, topk
+        s.topk_per_seq = None if topk_per_seq is None else topk_per_seq.data_ptr()
+        s.n_init, s.window, s.shared_selection = n_init, window, shared_selection
+        s.softmax_scale = softmax_scale
+        s.dtype = _DT[dtype]
+        self.s = s
+
+    @classmethod
+    def from_lengths(cls, seqlens_q: Sequence[int], seqlens_k: Sequence[int], device="cuda",
+                     topk_per_seq: Optional[Sequence[int]] = None, q_pos0: Optional[Sequence[int]] = None,
+                     **kw) -> "Params":
+        def cu(lens):
+            out = [0]
+            for x in lens:
+                out.append(out[-1] + int(x))
+            return torch.tensor(out, dtype=torch.int32, device=device)
+
+        tps = None if topk_per_seq is None else torch.tensor(list(topk_per_seq), dtype=torch.int32,
+                                                             device=device)
+        qp = None if q_pos0 is None else torch.tensor(list(q_pos0), dtype=torch.int32, device=device)
+        return cls(batch=len(seqlens_k), cu_seqlens_q=cu(seqlens_q), cu_seqlens_k=cu(seqlens_k),
+                   max_q=max(seqlens_q), max_k=max(seqlens_k), total_q=sum(seqlens_q),
+                   total_k=sum(seqlens_k), topk_per_seq=tps, q_pos0=qp, **kw)
+
+    @property
+    def rows(self) -> int:
+        return self.s.batch if self.s.shared_selection else self.s.total_q
+
+    @property
+    def nb_max(self) -> int:
+        return -(-self.s.max_k // self.s.block)
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def abi_version() -> int:
+    return lib().sparse_attn_abi_version()
+
+
+def validate(p: Params) -> None:
+    check("sparse_attn_validate", lib().sparse_attn_validate(p.ref()))
+
+
+def workspace_size(p: Params):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    check("sparse_attn_workspace_size", lib().sparse_attn_workspace_size(p.ref(), ctypes.byref(a),
+                                                                         ctypes.byref(b)))
+    return a.value, b.value
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def compress(p: Params, k: torch.Tensor, k_cmp: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if k_cmp is None:
+        k_cmp = torch.empty((p.s.h_kv, p.s.batch, p.nb_max, p.s.head_dim), dtype=torch.float32,
+                            device=k.device)
+    check("sparse_attn_compress", lib().sparse_attn_compress(p.ref(), _ptr(k), _ptr(k_cmp), _stream(stream)))
+    return k_cmp
+
+
+def compress_tail(p: Params, n_tail_blocks: int, k: torch.Tensor, k_cmp: torch.Tensor, stream=None) -> torch.Tensor:
+    check("sparse_attn_compress_tail", lib().sparse_attn_compress_tail(p.ref(), int(n_tail_blocks), _ptr(k),
+                                                                       _ptr(k_cmp), _stream(stream)))
+    return k_cmp
+
+
+def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Optional[torch.Tensor],
+           idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
+           ws: Optional[torch.Tensor] = None, stream=None):
+    dev = q_sel.device
+    if idx is None:
+        idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
+    if n_idx is None:
+        n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
+    ws, nbytes = _ws(workspace_size(p)[0], dev, ws)
+    check("sparse_attn_select", lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx),
+                                                         _ptr(n_idx), _ptr(ws), nbytes, _stream(stream)))
+    return idx, n_idx
+
+
+def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, n_idx: torch.Tensor,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+        ws: Optional[torch.Tensor] = None, stream=None, events=None):
+    """Sparse attention; ``events`` = (begin, end) torch.cuda.Event pair recorded around the
+    main attention kernel (both must have been recorded once, so their handles exist)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((p.s.h_q, p.s.total_q), dtype=torch.float32, device=q.device)
+    ws, nbytes = _ws(workspace_size(p)[1], q.device, ws)
+    if events is not None:
+        p.s.timing_events[0] = events[0].cuda_event
+        p.s.timing_events[1] = events[1].cuda_event
+    try:
+        st = lib().sparse_attn_fwd(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_idx), _ptr(out),
+                                   _ptr(lse), _ptr(ws), nbytes, _stream(stream))
+    finally:
+        p.s.timing_events[0] = None
+        p.s.timing_events[1] = None
+    check("sparse_attn_fwd", st)
+    return (out, lse) if want_lse else out

@@ -1,0 +1,231 @@
+// abi.cpp -- the C ABI declared in include/sparse_attn.h: host-side validation,
+// workspace sizing, status strings and dispatch to the kernel launchers.
+// No device memory is allocated here; nothing is launched before every host
+// check has passed.
+#include "sparse_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+sa_status fail(sa_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+sa_status ok()
+{
+    g_last_error.clear();
+    return SA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+sa_status check_params(const sa_params *p)
+{
+    if (!p)
+        return fail(SA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 1)
+        return fail(SA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
+    if (p->h_q < 1 || p->h_kv < 1 || p->h_q % p->h_kv != 0)
+        return fail(SA_ERR_INVALID_ARG, "h_q (%d) must be a positive multiple of h_kv (%d)", p->h_q, p->h_kv);
+    if (p->h_q / p->h_kv > 64)
+        return fail(SA_ERR_UNSUPPORTED, "group size h_q/h_kv = %d exceeds 64", p->h_q / p->h_kv);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+    if (p->max_q < 1 || p->max_k < 1)
+        return fail(SA_ERR_INVALID_ARG, "max_q (%d) and max_k (%d) must be >= 1", p->max_q, p->max_k);
+    if (p->total_q < p->max_q || p->total_k < p->max_k)
+        return fail(SA_ERR_INVALID_ARG, "total_q/total_k (%lld/%lld) below max_q/max_k (%d/%d)",
+                    (long long)p->total_q, (long long)p->total_k, p->max_q, p->max_k);
+    if (p->total_q > (1LL << 40) || p->total_k > (1LL << 40) || p->max_k > (1 << 30))
+        return fail(SA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if ((long long)p->batch * p->h_kv > 65535 || (p->max_q + 63) / 64 > 65535)
+        return fail(SA_ERR_UNSUPPORTED, "batch * h_kv must be <= 65535 and max_q <= 4194240");
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k)
+        return fail(SA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k are required");
+    if (p->block < 1)
+        return fail(SA_ERR_INVALID_ARG, "block must be >= 1 (got %d)", p->block);
+    if (p->pool != SA_POOL_MEAN && p->pool != SA_POOL_L2SUM)
+        return fail(SA_ERR_INVALID_ARG, "unknown pool mode %d", p->pool);
+    if (p->topk < 0)
+        return fail(SA_ERR_INVALID_ARG, "topk must be >= 0 (got %d)", p->topk);
+    if (p->n_init < 0)
+        return fail(SA_ERR_INVALID_ARG, "n_init must be >= 0 (got %d)", p->n_init);
+    if (p->window < 1)
+        return fail(SA_ERR_INVALID_ARG, "window must be >= 1 (got %d): the attended set would be empty",
+                    p->window);
+    if (p->shared_selection != 0 && p->shared_selection != 1)
+        return fail(SA_ERR_INVALID_ARG, "shared_selection must be 0 or 1");
+    if (p->dtype != SA_DTYPE_F32 && p->dtype != SA_DTYPE_BF16)
+        return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (!(p->softmax_scale >= 0.f) || std::isinf(p->softmax_scale))
+        return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    return SA_OK;
+}
+
+sa::KP make_kp(const sa_params *p)
+{
+    sa::KP k;
+    k.batch = p->batch;
+    k.h_q = p->h_q;
+    k.h_kv = p->h_kv;
+    k.d = p->head_dim;
+    k.G = p->h_q / p->h_kv;
+    k.max_q = p->max_q;
+    k.max_k = p->max_k;
+    k.total_q = p->total_q;
+    k.total_k = p->total_k;
+    k.cu_q = p->cu_seqlens_q;
+    k.cu_k = p->cu_seqlens_k;
+    k.q_pos0 = p->q_pos0;
+    k.g = p->block;
+    k.pool = p->pool;
+    k.topk = p->topk;
+    k.topk_per_seq = p->topk_per_seq;
+    k.n_init = p->n_init;
+    k.window = p->window;
+    k.shared = p->shared_selection;
+    k.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+    k.scale_log2 = k.scale * 1.4426950408889634f;
+    k.nb_max = (p->max_k + p->block - 1) / p->block;
+    k.rows = p->shared_selection ? p->batch : p->total_q;
+    return k;
+}
+
+sa_status device_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return ok();
+    return fail(SA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+} // namespace
+
+extern "C" {
+
+int sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
+
+const char *sparse_attn_status_string(sa_status s)
+{
+    switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_DEVICE: return "HIP device error";
+    }
+    return "unknown status";
+}
+
+const char *sparse_attn_last_error(void) { return g_last_error.c_str(); }
+
+sa_status sparse_attn_validate(const sa_params *p)
+{
+    sa_status s = check_params(p);
+    return s == SA_OK ? ok() : s;
+}
+
+sa_status sparse_attn_workspace_size(const sa_params *p, size_t *select_bytes, size_t *fwd_bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    sa::KP k = make_kp(p);
+    if (select_bytes)
+        *select_bytes = sa::select_workspace_bytes(k, sa::select_plan(k));
+    if (fwd_bytes)
+        *fwd_bytes = sa::fwd_workspace_bytes(k, sa::fwd_splits(k));
+    return ok();
+}
+
+static sa_status compress_common(const sa_params *p, int n_tail, const void *k, float *k_cmp, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!k || !k_cmp)
+        return fail(SA_ERR_INVALID_ARG, "k and k_cmp are required");
+    if (!aligned16(k) || !aligned16(k_cmp))
+        return fail(SA_ERR_INVALID_ARG, "k and k_cmp must be 16-byte aligned");
+    sa::KP kp = make_kp(p);
+    return device_status(sa::launch_compress(kp, p->dtype, k, k_cmp, n_tail, (hipStream_t)stream),
+                         "compress launch");
+}
+
+sa_status sparse_attn_compress(const sa_params *p, const void *k, float *k_cmp, void *stream)
+{
+    return compress_common(p, 0, k, k_cmp, stream);
+}
+
+sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, const void *k, float *k_cmp,
+                                    void *stream)
+{
+    if (n_tail_blocks < 1)
+        return fail(SA_ERR_INVALID_ARG, "n_tail_blocks must be >= 1 (got %d)", n_tail_blocks);
+    return compress_common(p, n_tail_blocks, k, k_cmp, stream);
+}
+
+sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,
+                             int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!q_sel || !n_idx || (!idx && p->topk > 0))
+        return fail(SA_ERR_INVALID_ARG, "q_sel, idx and n_idx are required");
+    if (p->block == 1 && !k)
+        return fail(SA_ERR_INVALID_ARG, "block == 1 scores the raw keys: k is required");
+    if (p->block > 1 && !k_cmp)
+        return fail(SA_ERR_INVALID_ARG, "block > 1 scores pooled keys: k_cmp is required");
+    if (!aligned16(q_sel) || (k && !aligned16(k)) || (k_cmp && !aligned16(k_cmp)))
+        return fail(SA_ERR_INVALID_ARG, "q_sel, k and k_cmp must be 16-byte aligned");
+    sa::KP kp = make_kp(p);
+    int plan = sa::select_plan(kp);
+    size_t need = sa::select_workspace_bytes(kp, plan);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SA_ERR_WORKSPACE, "select needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    return device_status(sa::launch_select(kp, p->dtype, q_sel, k_cmp, k, idx, n_idx, ws, (hipStream_t)stream),
+                         "select launch");
+}
+
+sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                          const int32_t *n_idx, void *out, float *lse, void *ws, size_t ws_bytes, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!q || !k || !v || !out || !n_idx || (!idx && p->topk > 0))
+        return fail(SA_ERR_INVALID_ARG, "q, k, v, out, idx and n_idx are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    sa::KP kp = make_kp(p);
+    int splits = sa::fwd_splits(kp);
+    size_t need = sa::fwd_workspace_bytes(kp, splits);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SA_ERR_WORKSPACE, "fwd needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    return device_status(sa::launch_fwd(kp, p->dtype, q, k, v, idx, n_idx, out, lse, ws, splits,
+                                        p->timing_events[0], p->timing_events[1], (hipStream_t)stream),
+                         "fwd launch");
+}
+
+} // extern "C"

@@ -1,0 +1,102 @@
+// compress.hip -- pooled keys, one streaming pass over K.
+//
+// K~_j = mean of the keys of block j (SparDA summary, Method: InfLLM-V2 pools
+// keys by a parameter-free mean), or the sum of the L2-normalised keys (LSA
+// deep-read, §2.2).  Blocks are g consecutive tokens of one KV head, stride g.
+//
+// Mapping: one thread owns 8 consecutive head-dim elements of one pooled
+// vector.  Threads are numbered chunk-fastest, then KV head, then block, then
+// sequence, so for a fixed token offset a wavefront reads d/8 x 16 B runs that
+// are contiguous across KV heads (rows of K are [Hkv, d] contiguous): the
+// pass is a coalesced stream of K and the kernel is HBM-bound.  L2SUM needs the
+// norm of each key: its d/8 owners are adjacent lanes of one wavefront and sum
+// their squares with xor shuffles; every lane runs the same g iterations so
+// the shuffles stay converged.
+#include "sa_common.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+template <typename T, int D, int POOL>
+__global__ __launch_bounds__(256) void compress_kernel(KP P, const T *__restrict__ k,
+                                                       float *__restrict__ k_cmp, int n_blk_iter,
+                                                       int tail)
+{
+    constexpr int L = D / 8;   // lanes per pooled vector
+    long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    int chunk = (int)(tid % L);
+    long long r = tid / L;
+    int c = (int)(r % P.h_kv);
+    r /= P.h_kv;
+    int jj = (int)(r % n_blk_iter);
+    int b = (int)(r / n_blk_iter);
+    bool live = b < P.batch;
+    int n_k = 0, j = 0;
+    long long k_off = 0;
+    if (live) {
+        k_off = P.cu_k[b];
+        n_k = P.cu_k[b + 1] - P.cu_k[b];
+        int nb = (n_k + P.g - 1) / P.g;
+        j = tail ? nb - n_blk_iter + jj : jj;
+        live = j >= 0 && j < nb && j < P.nb_max;
+    }
+    int t0 = j * P.g;
+    int t1 = min(t0 + P.g, n_k);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int it = 0; it < P.g; it++) {
+        int t = t0 + it;
+        bool ok = live && t < t1;
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (ok)
+            load8(k + ((k_off + t) * P.h_kv + c) * D + chunk * 8, x);
+        float s = 1.0f;
+        if (POOL == 1) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                ss += x[e] * x[e];
+            ss = group_sum<L>(ss);
+            s = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            acc[e] += x[e] * s;
+    }
+    if (!live)
+        return;
+    if (POOL == 0) {
+        float inv = 1.0f / (float)(t1 - t0);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            acc[e] *= inv;
+    }
+    store8(k_cmp + (((long long)c * P.batch + b) * P.nb_max + j) * D + chunk * 8, acc);
+}
+
+template <typename T, int D>
+static hipError_t launch_compress_t(const KP &P, const void *k, float *k_cmp, int n_blk_iter, int tail,
+                                    hipStream_t st)
+{
+    long long threads = (long long)P.batch * n_blk_iter * P.h_kv * (D / 8);
+    long long blocks = (threads + 255) / 256;
+    if (P.pool == 1)
+        compress_kernel<T, D, 1><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+            P, (const T *)k, k_cmp, n_blk_iter, tail);
+    else
+        compress_kernel<T, D, 0><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+            P, (const T *)k, k_cmp, n_blk_iter, tail);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, int n_tail, hipStream_t st)
+{
+    int n_blk_iter = n_tail > 0 ? (n_tail < P.nb_max ? n_tail : P.nb_max) : P.nb_max;
+    int tail = n_tail > 0 ? 1 : 0;
+    if (dtype == 1)
+        return P.d == 128 ? launch_compress_t<uint16_t, 128>(P, k, k_cmp, n_blk_iter, tail, st)
+                          : launch_compress_t<uint16_t, 64>(P, k, k_cmp, n_blk_iter, tail, st);
+    return P.d == 128 ? launch_compress_t<float, 128>(P, k, k_cmp, n_blk_iter, tail, st)
+                      : launch_compress_t<float, 64>(P, k, k_cmp, n_blk_iter, tail, st);
+}
+
+} // namespace sa

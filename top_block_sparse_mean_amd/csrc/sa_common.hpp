@@ -1,0 +1,244 @@
+// sa_common.hpp -- device-side helpers shared by the gfx950 kernels:
+// kernel parameter block, sequence / selection geometry, element loads,
+// wavefront reductions and the order-preserving score key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+// Everything a kernel needs about the call, passed by value.
+struct KP {
+    int batch, h_q, h_kv, d, G;
+    int max_q, max_k;
+    long long total_q, total_k;
+    const int32_t *cu_q, *cu_k, *q_pos0;
+    int g, pool, topk;
+    const int32_t *topk_per_seq;
+    int n_init, window, shared;
+    float scale_log2;   // softmax scale * log2(e): logits are kept in base 2
+    float scale;        // softmax scale
+    int nb_max;         // ceil(max_k / g)
+    long long rows;     // selection rows per KV head
+};
+
+struct Seq {
+    long long k_off, q_off;
+    int n_k, n_q, q0;
+};
+
+__device__ __forceinline__ Seq seq_info(const KP &P, int b)
+{
+    Seq s;
+    s.k_off = P.cu_k[b];
+    s.q_off = P.cu_q[b];
+    s.n_k = P.cu_k[b + 1] - P.cu_k[b];
+    s.n_q = P.cu_q[b + 1] - P.cu_q[b];
+    s.q0 = P.q_pos0 ? P.q_pos0[b] : s.n_k - s.n_q;
+    return s;
+}
+
+// Sequence holding packed query index i (binary search over cu_seqlens_q).
+__device__ __forceinline__ int seq_of_query(const KP &P, long long i)
+{
+    int lo = 0, hi = P.batch - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (P.cu_q[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Candidate blocks of a selection row are one contiguous range [j_lo, j_hi):
+// a block is a candidate iff it ends at or before p_sel and meets the non-fixed
+// region [n_init, p_sel - window + 1) (every other token up to p_sel is an init
+// or window token).
+__device__ __host__ __forceinline__ void cand_range(int g, int n_init, int window, int n_k, int p_sel,
+                                                    int &j_lo, int &j_hi)
+{
+    int hi = p_sel - window + 1;
+    j_lo = 0;
+    j_hi = 0;
+    if (p_sel < 0 || n_init >= hi)
+        return;
+    int nb = (n_k + g - 1) / g;
+    int nb_vis = (p_sel >= n_k - 1) ? nb : (p_sel + 1) / g;
+    int top = (hi + g - 1) / g;
+    j_lo = n_init / g;
+    j_hi = nb_vis < top ? nb_vis : top;
+    if (j_hi < j_lo)
+        j_hi = j_lo;
+}
+
+// The attended set of one query as three disjoint ranges of positions:
+//   [0, n1) -> init tokens; [n1, n1+n2) -> tokens of the selected blocks clipped
+//   to [n_init, p_sel-window+1); [n1+n2, total) -> [lo_w, p].
+struct ASet {
+    int n1, n2, n3, total;
+    int lo_w;
+    int nsel, g;
+    int start_f, len_f;   // first selected block, clipped
+    int p;                // query position (tokens are clamped to <= p)
+};
+
+__device__ __forceinline__ ASet aset_make(const KP &P, int n_k, int p, int p_sel, const int32_t *sel, int nsel)
+{
+    ASet a;
+    a.g = P.g;
+    a.p = p < n_k - 1 ? p : n_k - 1;
+    a.n1 = P.n_init < p + 1 ? P.n_init : p + 1;
+    if (a.n1 < 0)
+        a.n1 = 0;
+    int hi = p_sel - P.window + 1;
+    a.lo_w = P.n_init > hi ? P.n_init : hi;
+    a.n3 = p - a.lo_w + 1;
+    if (a.n3 < 0)
+        a.n3 = 0;
+    a.nsel = (nsel > 0 && P.n_init < hi) ? nsel : 0;
+    a.n2 = 0;
+    a.start_f = 0;
+    a.len_f = 0;
+    if (a.nsel > 0) {
+        int g = P.g;
+        int jf = sel[0];
+        int s0 = jf * g, e0 = min((jf + 1) * g, n_k);
+        a.start_f = max(s0, P.n_init);
+        a.len_f = max(0, min(e0, hi) - a.start_f);
+        if (a.nsel == 1) {
+            a.n2 = a.len_f;
+        } else {
+            int jl = sel[a.nsel - 1];
+            int len_l = max(0, min(min((jl + 1) * g, n_k), hi) - jl * g);
+            a.n2 = a.len_f + (a.nsel - 2) * g + len_l;
+        }
+    }
+    a.total = a.n1 + a.n2 + a.n3;
+    return a;
+}
+
+// Token at position pos (0 <= pos < total) of the attended set.
+__device__ __forceinline__ int aset_token(const ASet &a, const int32_t *sel, int pos)
+{
+    int t;
+    if (pos < a.n1) {
+        t = pos;
+    } else if (pos < a.n1 + a.n2) {
+        int r = pos - a.n1;
+        if (r < a.len_f) {
+            t = a.start_f + r;
+        } else {
+            r -= a.len_f;
+            int m = r / a.g;
+            if (m < a.nsel - 2)
+                t = sel[1 + m] * a.g + (r - m * a.g);
+            else
+                t = sel[a.nsel - 1] * a.g + (r - (a.nsel - 2) * a.g);
+        }
+    } else {
+        t = a.lo_w + (pos - a.n1 - a.n2);
+    }
+    return t < 0 ? 0 : (t > a.p ? a.p : t);   // never leave [0, p], whatever the table holds
+}
+
+// ---------------------------------------------------------------- elements
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u)             // inf / nan: keep, quiet the nan
+        return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);                   // round to nearest, ties to even
+    return (uint16_t)(u >> 16);
+}
+
+// Load 8 consecutive elements as fp32.
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8])
+{
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ void load8(const float *p, float (&x)[8])
+{
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(uint16_t *p, const float (&x)[8])
+{
+    uint4 v;
+    v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    v.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+    v.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+    *reinterpret_cast<uint4 *>(p) = v;
+}
+
+__device__ __forceinline__ void store8(float *p, const float (&x)[8])
+{
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// ---------------------------------------------------------------- reductions
+
+// Sum over aligned groups of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Monotone map of an fp32 score to uint32 (larger score -> larger key); -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(unsigned long long mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+} // namespace sa

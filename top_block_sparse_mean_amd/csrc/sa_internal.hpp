@@ -1,0 +1,23 @@
+// sa_internal.hpp -- host-side launchers shared between the C ABI and the kernels.
+#pragma once
+
+#include "sa_common.hpp"
+
+namespace sa {
+
+enum { kSelectEmpty = 0, kSelectFused = 1, kSelectSplit = 2, kSelectTile = 3 };
+
+hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, int n_tail, hipStream_t st);
+
+int select_plan(const KP &P);
+size_t select_workspace_bytes(const KP &P, int plan);
+hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
+                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st);
+
+int fwd_splits(const KP &P);
+size_t fwd_workspace_bytes(const KP &P, int splits);
+hipError_t launch_fwd(const KP &P, int dtype, const void *q, const void *k, const void *v, const int32_t *idx,
+                      const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev_begin,
+                      void *ev_end, hipStream_t st);
+
+} // namespace sa

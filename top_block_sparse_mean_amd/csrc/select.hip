@@ -1,0 +1,651 @@
+// select.hip -- top-k block selection on gfx950.
+//
+// Score of candidate block j for a selection row and KV head c: the row's
+// query heads of group c (and, for a shared row, all its queries) summed into
+// one fp32 selector query Qs, dotted with the fp32 pooled key K~_j (SparDA
+// summary, Method: one selector head per GQA group; LSA deep-read, §2.3-§2.4).
+// Ranking uses the raw dot: the positive 1/sqrt(d) factor cannot change the
+// order, and leaving it out avoids a rounding step that could merge two
+// neighbouring fp32 scores.  Equal scores keep the lower index.
+//
+// Kernels:
+//   select_rows   one workgroup per (row, KV head): streams the candidate
+//                 pooled keys (wavefront dot products), keeps the order keys in
+//                 LDS, wavefront top-k.  Decode rows with up to 4096 candidates.
+//   score_rows    split GEMV for rows with many candidates (token-level draft
+//                 selection): writes order keys to the workspace.
+//   score_tile    prefill: 64 rows x 64 blocks per workgroup, operands staged in
+//                 LDS, fp32 MFMA 16x16x4 (fp32-accurate products), writes keys.
+//   topk_wave     one wavefront per row, keys in registers (<= 2048 candidates).
+//   topk_block    one workgroup per row, 8-bit radix select over the workspace.
+//
+// Top-k rule on the keys: the k-th largest key tau is found by a binary search
+// on its bits (wavefront) or by 8-bit radix passes (workgroup); the output is
+// every key > tau plus the lowest-index keys == tau needed to reach k, written
+// in ascending index order by ballot compaction.
+#include "sa_common.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- row geometry
+
+struct RowGeo {
+    int b, n_k, p_sel;
+    long long q_first, q_last;   // packed query range summed into the selector
+    int j_lo, j_hi, n_cand, need;
+    long long k_off;
+};
+
+__device__ __forceinline__ RowGeo row_geo(const KP &P, long long row)
+{
+    RowGeo r;
+    if (P.shared) {
+        r.b = (int)row;
+        Seq s = seq_info(P, r.b);
+        r.q_first = s.q_off;
+        r.q_last = s.q_off + s.n_q;
+        r.p_sel = s.q0 - 1;
+        r.n_k = s.n_k;
+        r.k_off = s.k_off;
+    } else {
+        r.b = seq_of_query(P, row);
+        Seq s = seq_info(P, r.b);
+        r.q_first = row;
+        r.q_last = row + 1;
+        r.p_sel = s.q0 + (int)(row - s.q_off);
+        r.n_k = s.n_k;
+        r.k_off = s.k_off;
+    }
+    cand_range(P.g, P.n_init, P.window, r.n_k, r.p_sel, r.j_lo, r.j_hi);
+    const int cap = P.g == 1 ? P.max_k : P.nb_max;     // rows of the key table / workspace
+    r.j_hi = min(r.j_hi, cap);
+    r.j_lo = min(r.j_lo, r.j_hi);
+    r.n_cand = r.j_hi - r.j_lo;
+    int k = P.topk_per_seq ? P.topk_per_seq[r.b] : P.topk;
+    k = k < 0 ? 0 : (k > P.topk ? P.topk : k);
+    r.need = k < r.n_cand ? k : r.n_cand;
+    return r;
+}
+
+// Qs[e] for e in [e0, e0+n) : sum over the row's queries and group c's heads.
+template <typename T, int D>
+__device__ __forceinline__ float selector_elem(const KP &P, const T *q, const RowGeo &r, int c, int e)
+{
+    float s = 0.f;
+    for (long long i = r.q_first; i < r.q_last; i++) {
+        const T *qi = q + (i * P.h_q + (long long)c * P.G) * D + e;
+        for (int h = 0; h < P.G; h++) {
+            if constexpr (sizeof(T) == 2)
+                s += bf16_to_f32(qi[h * D]);
+            else
+                s += qi[h * D];
+        }
+    }
+    return s;
+}
+
+// Write idx = j_lo .. j_hi-1 (all candidates kept) and the -1 padding.
+__device__ __forceinline__ void write_all(const KP &P, int32_t *out, const RowGeo &r, int t, int nt)
+{
+    for (int s = t; s < P.topk; s += nt)
+        out[s] = s < r.n_cand ? r.j_lo + s : -1;
+}
+
+// ---------------------------------------------------------------- top-k cores
+
+// One wavefront: the `need` largest of n keys (key i at lane i % 64, slot i / 64),
+// indices j_base + i written ascending to out[0 .. need).
+template <int KPL>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int need, int j_base, int32_t *out)
+{
+    const int lane = lane_id();
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        uint32_t cand = tau | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; m++)
+            cnt += (m * kWave + lane < n && key[m] >= cand) ? 1 : 0;
+        cnt = wave_sum_int(cnt);
+        if (cnt >= need)
+            tau = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++)
+        gt += (m * kWave + lane < n && key[m] > tau) ? 1 : 0;
+    int need_eq = need - wave_sum_int(gt);
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        int i = m * kWave + lane;
+        bool valid = i < n;
+        bool is_gt = valid && key[m] > tau;
+        bool is_eq = valid && key[m] == tau;
+        unsigned long long meq = __ballot(is_eq);
+        int rank = eq_seen + lanes_below(meq);
+        eq_seen += __popcll(meq);
+        bool s = is_gt || (is_eq && rank < need_eq);
+        unsigned long long ms = __ballot(s);
+        if (s)
+            out[base + lanes_below(ms)] = j_base + i;
+        base += __popcll(ms);
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ int2 block_scan_flag(bool f, int *sh)
+{
+    unsigned long long m = __ballot(f);
+    int w = threadIdx.x / kWave;
+    if (lane_id() == 0)
+        sh[w] = __popcll(m);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) {
+        int c = sh[i];
+        off += i < w ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    return make_int2(off + lanes_below(m), tot);
+}
+
+// One workgroup: the `need` largest of keys[0 .. n) (global memory), 8-bit radix.
+template <int NT>
+__device__ void block_topk(const uint32_t *__restrict__ keys, int n, int need, int j_base, int32_t *out)
+{
+    __shared__ int hist[256];
+    __shared__ int sh_scan[NT / kWave];
+    __shared__ int sh_digit, sh_above;
+    const int tid = threadIdx.x, lane = lane_id();
+    uint32_t prefix = 0, pmask = 0;
+    int rem = need;
+    for (int pass = 0; pass < 4; pass++) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += NT)
+            hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+            uint32_t k = keys[i];
+            if ((k & pmask) == prefix)
+                atomicAdd(&hist[(k >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            int c[4], s = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                c[q] = hist[255 - 4 * lane - q];
+                s += c[q];
+            }
+            int incl = s;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                int t = __shfl_up(incl, o, kWave);
+                if (lane >= o)
+                    incl += t;
+            }
+            unsigned long long mk = __ballot(incl >= rem);
+            int first = __ffsll((long long)mk) - 1;
+            if (lane == first) {
+                int run = incl - s;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    if (run + c[q] >= rem) {
+                        sh_digit = 255 - 4 * lane - q;
+                        sh_above = run;
+                        break;
+                    }
+                    run += c[q];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= ((uint32_t)sh_digit) << shift;
+        pmask |= 255u << shift;
+        rem -= sh_above;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;
+    const int need_eq = rem;
+    int sel_base = 0, eq_seen = 0;
+    for (int base = 0; base < n; base += NT) {
+        int i = base + tid;
+        bool valid = i < n;
+        uint32_t k = valid ? keys[i] : 0u;
+        bool is_gt = valid && k > tau, is_eq = valid && k == tau;
+        int2 e = block_scan_flag<NT>(is_eq, sh_scan);
+        int rank = eq_seen + e.x;
+        eq_seen += e.y;
+        bool s = is_gt || (is_eq && rank < need_eq);
+        int2 p = block_scan_flag<NT>(s, sh_scan);
+        if (s)
+            out[sel_base + p.x] = j_base + i;
+        sel_base += p.y;
+    }
+}
+
+// ---------------------------------------------------------------- scoring helpers
+
+// Dot of Qs (this lane's VPL-element slice, in registers) with one key row.
+template <typename KT, int D>
+struct RowDot;
+
+template <int D>
+struct RowDot<float, D> {          // pooled fp32 keys: 4 floats (16 B) per lane
+    static constexpr int VPL = 4, L = D / 4;
+    static __device__ __forceinline__ float dot(const float *row, int sub, const float (&qs)[4])
+    {
+        float4 k = reinterpret_cast<const float4 *>(row)[sub];
+        return qs[0] * k.x + qs[1] * k.y + qs[2] * k.z + qs[3] * k.w;
+    }
+};
+
+template <int D>
+struct RowDot<uint16_t, D> {       // raw bf16 keys (g = 1): 8 elements (16 B) per lane
+    static constexpr int VPL = 8, L = D / 8;
+    static __device__ __forceinline__ float dot(const uint16_t *row, int sub, const float (&qs)[8])
+    {
+        float x[8];
+        load8(row + sub * 8, x);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            s += qs[e] * x[e];
+        return s;
+    }
+};
+
+// Pointer to key row j of (sequence, KV head c) for scoring: pooled fp32 or raw.
+template <typename KT, int D>
+__device__ __forceinline__ const KT *key_row(const KP &P, const KT *base, const RowGeo &r, int c, int j)
+{
+    if (P.g == 1)
+        return base + ((r.k_off + j) * P.h_kv + c) * D;
+    return base + (((long long)c * P.batch + r.b) * P.nb_max + j) * D;
+}
+
+// ---------------------------------------------------------------- select_rows
+
+// grid: (rows, h_kv); NT threads; keys of up to MAXC candidates kept in LDS.
+template <typename T, typename KT, int D, int NT, int MAXC, int U>
+__global__ __launch_bounds__(NT) void select_rows_kernel(KP P, const T *__restrict__ q,
+                                                         const KT *__restrict__ kbase,
+                                                         int32_t *__restrict__ idx,
+                                                         int32_t *__restrict__ n_idx)
+{
+    using RD = RowDot<KT, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L;                 // key rows per wavefront pass
+    constexpr int NG = (NT / kWave) * GPW;         // key rows per workgroup pass
+    __shared__ float qs_sh[D];
+    __shared__ uint32_t keys[MAXC];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y;
+    const int tid = threadIdx.x;
+    RowGeo r = row_geo(P, row);
+    if (r.n_cand > MAXC) {                             // only if the lengths break the call's max_k
+        r.n_cand = MAXC;
+        r.j_hi = r.j_lo + MAXC;
+        r.need = min(r.need, MAXC);
+    }
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (tid == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, tid, NT);
+        return;
+    }
+    for (int e = tid; e < D; e += NT)
+        qs_sh[e] = selector_elem<T, D>(P, q, r, c, e);
+    __syncthreads();
+    const int lane = lane_id();
+    const int sub = lane % L;
+    const int grp = (tid / kWave) * GPW + lane / L;
+    float qv[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; e++)
+        qv[e] = qs_sh[sub * VPL + e];
+    for (int base = 0; base < r.n_cand; base += NG * U) {
+        float part[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            int jj = base + u * NG + grp;
+            part[u] = 0.f;
+            if (jj < r.n_cand)
+                part[u] = RD::dot(key_row<KT, D>(P, kbase, r, c, r.j_lo + jj), sub, qv);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float s = group_sum<L>(part[u]);
+            int jj = base + u * NG + grp;
+            if (sub == 0 && jj < r.n_cand)
+                keys[jj] = order_key(s);
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        constexpr int KPL = MAXC / kWave;
+        uint32_t kr[KPL];
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            int i = m * kWave + lane;
+            kr[m] = i < r.n_cand ? keys[i] : 0u;
+        }
+        wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
+        for (int s = r.need + lane; s < P.topk; s += kWave)
+            out[s] = -1;
+    }
+}
+
+// ---------------------------------------------------------------- score_rows (split)
+
+// grid: (rows * n_chunk, h_kv), CH candidates per chunk; writes order keys to
+// ws[(c*rows+row)*stride + j].
+template <typename T, typename KT, int D, int CH>
+__global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restrict__ q,
+                                                         const KT *__restrict__ kbase,
+                                                         uint32_t *__restrict__ ws, long long stride, int n_chunk)
+{
+    using RD = RowDot<KT, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L, NG = 4 * GPW, U = 4;
+    __shared__ float qs_sh[D];
+    const long long row = blockIdx.x / n_chunk;
+    const int chunk = (int)(blockIdx.x % n_chunk);
+    const int c = blockIdx.y;
+    RowGeo r = row_geo(P, row);
+    if (r.need == r.n_cand)
+        return;
+    int j0 = r.j_lo + chunk * CH;
+    int j1 = min(j0 + CH, r.j_hi);
+    if (j0 >= j1)
+        return;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < D; e += 256)
+        qs_sh[e] = selector_elem<T, D>(P, q, r, c, e);
+    __syncthreads();
+    const int lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    float qv[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; e++)
+        qv[e] = qs_sh[sub * VPL + e];
+    uint32_t *dst = ws + ((long long)c * P.rows + row) * stride;
+    for (int base = j0; base < j1; base += NG * U) {
+        float part[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            int j = base + u * NG + grp;
+            part[u] = j < j1 ? RD::dot(key_row<KT, D>(P, kbase, r, c, j), sub, qv) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float s = group_sum<L>(part[u]);
+            int j = base + u * NG + grp;
+            if (sub == 0 && j < j1)
+                dst[j] = order_key(s);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- score_tile (MFMA fp32)
+
+// Prefill rows (one per query).  grid: (block chunks of 64, row tiles of 64, h_kv * batch).
+// 4 wavefronts in a 2 x 2 arrangement, each a 32 x 32 tile of 2 x 2 MFMA 16x16x4 f32.
+// MFMA 16x16x4 f32 operands: lane l gives A[l%16][l/16] and B[l/16][l%16];
+// the result lane l holds D[4*(l/16)+i][l%16], i = 0..3.
+template <typename T, typename KT, int D>
+__global__ __launch_bounds__(256) void score_tile_kernel(KP P, const T *__restrict__ q,
+                                                         const KT *__restrict__ kbase,
+                                                         uint32_t *__restrict__ ws, long long stride)
+{
+    constexpr int TR = 64, TJ = 64, LD = D + 4;
+    __shared__ float qs_sh[TR * LD];
+    __shared__ float kt_sh[TJ * LD];
+    const int b = blockIdx.z % P.batch, c = blockIdx.z / P.batch;
+    Seq s = seq_info(P, b);
+    const int r0 = blockIdx.y * TR;
+    if (r0 >= s.n_q)
+        return;
+    const int r_end = min(r0 + TR, s.n_q);
+    // candidate range of the tile's last row bounds every row of the tile
+    int jlo_last, jhi_last;
+    cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
+    jhi_last = min(jhi_last, (int)stride);
+    const int j0 = jlo_last + blockIdx.x * TJ;
+    if (j0 >= jhi_last)
+        return;
+    const int tid = threadIdx.x;
+    // stage Qs: 64 rows x D, 8 elements per item
+    for (int it = tid; it < TR * (D / 8); it += 256) {
+        int rr = it / (D / 8), e0 = (it % (D / 8)) * 8;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r0 + rr < r_end) {
+            long long i = s.q_off + r0 + rr;
+            for (int h = 0; h < P.G; h++) {
+                float x[8];
+                load8(q + (i * P.h_q + (long long)c * P.G + h) * D + e0, x);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    acc[e] += x[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            qs_sh[rr * LD + e0 + e] = acc[e];
+    }
+    // stage keys: 64 candidate rows x D
+    for (int it = tid; it < TJ * (D / 8); it += 256) {
+        int jj = it / (D / 8), e0 = (it % (D / 8)) * 8;
+        int j = j0 + jj;
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (j < jhi_last) {
+            if (P.g == 1)
+                load8(kbase + ((s.k_off + j) * P.h_kv + c) * D + e0, x);
+            else
+                load8(kbase + (((long long)c * P.batch + b) * P.nb_max + j) * D + e0, x);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            kt_sh[jj * LD + e0 + e] = x[e];
+    }
+    __syncthreads();
+    const int lane = lane_id(), w = tid / kWave;
+    const int wr = (w >> 1) * 32, wj = (w & 1) * 32;
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++)
+            acc[a][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int li = lane % 16, lk = lane / 16;
+#pragma unroll 8
+    for (int e = 0; e < D; e += 4) {
+        float av[2], bv[2];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+            av[a] = qs_sh[(wr + a * 16 + li) * LD + e + lk];
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++)
+            bv[bb] = kt_sh[(wj + bb * 16 + li) * LD + e + lk];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++)
+                acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[bb], acc[a][bb], 0, 0, 0);
+    }
+    // epilogue: row = r0 + wr + a*16 + 4*lk + i, block = j0 + wj + bb*16 + li
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int rl = r0 + wr + a * 16 + 4 * lk + i;
+            if (rl >= r_end)
+                continue;
+            int jl, jh;
+            cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + rl, jl, jh);
+            jh = min(jh, (int)stride);
+            uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride;
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++) {
+                int j = j0 + wj + bb * 16 + li;
+                if (j >= jl && j < jh)
+                    dst[j] = order_key(acc[a][bb][i]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- top-k over the workspace
+
+// 4 wavefronts per workgroup, one row each (<= 2048 candidates).  grid: (ceil(rows/4), h_kv).
+__global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__restrict__ ws,
+                                                        long long stride, int32_t *__restrict__ idx,
+                                                        int32_t *__restrict__ n_idx)
+{
+    const long long row = (long long)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int c = blockIdx.y, lane = lane_id();
+    if (row >= P.rows)
+        return;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (lane == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, lane, kWave);
+        return;
+    }
+    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride + r.j_lo;
+    constexpr int KPL = 32;
+    uint32_t kr[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        int i = m * kWave + lane;
+        kr[m] = i < r.n_cand ? src[i] : 0u;
+    }
+    wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
+    for (int s = r.need + lane; s < P.topk; s += kWave)
+        out[s] = -1;
+}
+
+// One workgroup per row.  grid: (rows, h_kv).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_block_kernel(KP P, const uint32_t *__restrict__ ws,
+                                                        long long stride, int32_t *__restrict__ idx,
+                                                        int32_t *__restrict__ n_idx)
+{
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (threadIdx.x == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, threadIdx.x, NT);
+        return;
+    }
+    block_topk<NT>(ws + ((long long)c * P.rows + row) * stride + r.j_lo, r.n_cand, r.need, r.j_lo, out);
+    for (int s = r.need + (int)threadIdx.x; s < P.topk; s += NT)
+        out[s] = -1;
+}
+
+// Every row: n_idx = 0 and no index (k = 0 everywhere).
+__global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
+{
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < P.rows * P.h_kv)
+        n_idx[i] = 0;
+}
+
+// ---------------------------------------------------------------- dispatch
+
+static constexpr int kFusedMaxCand = 4096;
+static constexpr int kWaveTopkMax = 2048;
+static constexpr int kSplitChunk = 2048;
+
+size_t select_workspace_bytes(const KP &P, int plan)
+{
+    if (plan == kSelectFused || plan == kSelectEmpty)
+        return 0;
+    long long stride = P.g == 1 ? P.max_k : P.nb_max;
+    return (size_t)P.h_kv * (size_t)P.rows * (size_t)stride * sizeof(uint32_t);
+}
+
+int select_plan(const KP &P)
+{
+    if (P.topk == 0)
+        return kSelectEmpty;
+    long long max_cand = P.g == 1 ? P.max_k : P.nb_max;
+    bool few_rows = P.shared || P.max_q <= 8;
+    if (few_rows)
+        return max_cand <= kFusedMaxCand ? kSelectFused : kSelectSplit;
+    return kSelectTile;
+}
+
+template <typename T, int D>
+static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k_cmp, const void *k,
+                                  int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st)
+{
+    const T *q = (const T *)q_sel;
+    int plan = select_plan(P);
+    long long stride = P.g == 1 ? P.max_k : P.nb_max;
+    uint32_t *wsk = (uint32_t *)ws;
+    if (plan == kSelectEmpty) {
+        long long n = P.rows * P.h_kv;
+        select_empty_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(P, n_idx);
+        return hipGetLastError();
+    }
+    if (plan == kSelectFused) {
+        dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
+        if (P.g == 1)
+            select_rows_kernel<T, T, D, 1024, kFusedMaxCand, 8><<<grid, dim3(1024), 0, st>>>(
+                P, q, (const T *)k, idx, n_idx);
+        else
+            select_rows_kernel<T, float, D, 1024, kFusedMaxCand, 8><<<grid, dim3(1024), 0, st>>>(
+                P, q, k_cmp, idx, n_idx);
+        return hipGetLastError();
+    }
+    if (plan == kSelectSplit) {
+        int n_chunk = (int)((stride + kSplitChunk - 1) / kSplitChunk);
+        dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
+        if (P.g == 1)
+            score_rows_kernel<T, T, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,
+                                                                              n_chunk);
+        else
+            score_rows_kernel<T, float, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride,
+                                                                                  n_chunk);
+    } else {
+        dim3 grid((unsigned)((stride + 63) / 64), (unsigned)((P.max_q + 63) / 64), (unsigned)(P.h_kv * P.batch));
+        if (P.g == 1)
+            score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride);
+        else
+            score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (stride <= kWaveTopkMax)
+        topk_wave_kernel<<<dim3((unsigned)((P.rows + 3) / 4), (unsigned)P.h_kv), dim3(256), 0, st>>>(
+            P, wsk, stride, idx, n_idx);
+    else
+        topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
+            P, wsk, stride, idx, n_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
+                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st)
+{
+    if (dtype == 1)
+        return P.d == 128 ? launch_select_t<uint16_t, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, st)
+                          : launch_select_t<uint16_t, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, st);
+    return P.d == 128 ? launch_select_t<float, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, st)
+                      : launch_select_t<float, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, st);
+}
+
+} // namespace sa

@@ -94,6 +94,16 @@ def test_shared_selection_drafts_share_one_set():
     assert r["gpu"]["idx"].shape[1] == w.batch      # one row per sequence
 
 
+def test_split_selection_path():
+    """Shared token-level rows with more candidates than the fused kernel holds in LDS:
+    split scoring into the workspace + workgroup radix top-k."""
+    from workloads import draft_decode
+    w = draft_decode(batch=3, median=5000, lo=4500, hi=9000, seed=4321)
+    assert w.max_k > 4096
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
 def test_deterministic():
     w = small("bf16_prefill_128k")
     x, xg = parity.gen_pair(w)

@@ -107,6 +107,7 @@ sa::KP make_kp(const sa_params *p)
     k.scale_log2 = k.scale * 1.4426950408889634f;
     k.nb_max = (p->max_k + p->block - 1) / p->block;
     k.rows = p->shared_selection ? p->batch : p->total_q;
+    k.dtype = p->dtype;
     return k;
 }
 

@@ -164,6 +164,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(KP P, const T *__restric
 }
 
 // Merge the splits of one (query, head): one wavefront each, 4 per workgroup.
+// Lane s reads split s's (max, sum); the weights are broadcast from their lanes.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(KP P, const float *__restrict__ part, int n_split,
                                                            T *__restrict__ out, float *__restrict__ lse)
@@ -173,25 +174,28 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(KP P, const float *__
         return;
     const int lane = lane_id();
     const float *src = part + ih * n_split * (D + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; sp++)
-        M = fmaxf(M, src[sp * (D + 2) + D]);
-    float Ls = 0.f;
+    float ms = lane < n_split ? src[lane * (D + 2) + D] : -INFINITY;
+    float ls = lane < n_split ? src[lane * (D + 2) + D + 1] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        M = fmaxf(M, __shfl_xor(M, o, kWave));
+    float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    float Ls = ls * wgt;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        Ls += __shfl_xor(Ls, o, kWave);
     constexpr int EPL = D / kWave;
     float O[EPL];
 #pragma unroll
     for (int x = 0; x < EPL; x++)
         O[x] = 0.f;
     for (int sp = 0; sp < n_split; sp++) {
+        float f = __shfl(wgt, sp, kWave);
         const float *pp = src + sp * (D + 2);
-        float ms = pp[D];
-        if (ms == -INFINITY)
-            continue;
-        float w = exp2f(ms - M);
-        Ls += pp[D + 1] * w;
 #pragma unroll
         for (int x = 0; x < EPL; x++)
-            O[x] += pp[lane + x * kWave] * w;
+            O[x] += pp[lane + x * kWave] * f;
     }
     const long long i = ih / P.h_q;
     const int h = (int)(ih % P.h_q);
@@ -212,6 +216,8 @@ static int head_chunk(const KP &P) { return P.G < 4 ? P.G : 4; }
 
 int fwd_splits(const KP &P)
 {
+    if (mfma_fwd_ok(P, P.dtype))
+        return mfma_fwd_splits(P);
     long long a_max = (long long)P.n_init + (long long)P.topk * P.g + P.window + (P.shared ? P.max_q : 0);
     if (a_max > P.max_k)
         a_max = P.max_k;
@@ -223,6 +229,15 @@ int fwd_splits(const KP &P)
     if (sp > 32)
         sp = 32;
     return sp < 1 ? 1 : (int)sp;
+}
+
+template <typename T, int D>
+static hipError_t launch_combine(const KP &P, const void *ws, int splits, void *out, float *lse, hipStream_t st)
+{
+    long long n = P.total_q * P.h_q;
+    attn_combine_kernel<T, D><<<dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st>>>(P, (const float *)ws, splits,
+                                                                                   (T *)out, lse);
+    return hipGetLastError();
 }
 
 size_t fwd_workspace_bytes(const KP &P, int splits)
@@ -248,10 +263,7 @@ static hipError_t launch_fwd_t(const KP &P, const void *q, const void *k, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
-    long long n = P.total_q * P.h_q;
-    attn_combine_kernel<T, D><<<dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st>>>(P, (const float *)ws, splits,
-                                                                                   (T *)out, lse);
-    return hipGetLastError();
+    return launch_combine<T, D>(P, ws, splits, out, lse, st);
 }
 
 template <typename T, int D>
@@ -271,6 +283,13 @@ hipError_t launch_fwd(const KP &P, int dtype, const void *q, const void *k, cons
                       const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev0, void *ev1,
                       hipStream_t st)
 {
+    if (mfma_fwd_ok(P, dtype)) {
+        hipError_t e = launch_fwd_mfma(P, q, k, v, idx, n_idx, out, lse, ws, splits, ev0, ev1, st);
+        if (e != hipSuccess || splits == 1)
+            return e;
+        return P.d == 128 ? launch_combine<uint16_t, 128>(P, ws, splits, out, lse, st)
+                          : launch_combine<uint16_t, 64>(P, ws, splits, out, lse, st);
+    }
     if (dtype == 1)
         return P.d == 128 ? launch_fwd_d<uint16_t, 128>(P, q, k, v, idx, n_idx, out, lse, ws, splits, ev0, ev1, st)
                           : launch_fwd_d<uint16_t, 64>(P, q, k, v, idx, n_idx, out, lse, ws, splits, ev0, ev1, st);

@@ -73,11 +73,74 @@ __global__ __launch_bounds__(256) void compress_kernel(KP P, const T *__restrict
     store8(k_cmp + (((long long)c * P.batch + b) * P.nb_max + j) * D + chunk * 8, acc);
 }
 
+// Few pooled vectors (a decode step re-pools the newest block of each
+// sequence): one workgroup per (sequence, KV head, block); the block's tokens
+// are spread over 256/(d/8) token groups and summed through LDS.
+template <typename T, int D, int POOL>
+__global__ __launch_bounds__(256) void compress_few_kernel(KP P, const T *__restrict__ k, float *__restrict__ k_cmp,
+                                                           int n_blk_iter, int tail)
+{
+    constexpr int L = D / 8, TG = 256 / L;
+    __shared__ float sh[TG][D];
+    const int jj = blockIdx.x % n_blk_iter;
+    const int c = (blockIdx.x / n_blk_iter) % P.h_kv;
+    const int b = blockIdx.x / (n_blk_iter * P.h_kv);
+    const int tid = threadIdx.x, chunk = tid % L, tg = tid / L;
+    const long long k_off = P.cu_k[b];
+    const int n_k = P.cu_k[b + 1] - P.cu_k[b];
+    const int nb = (n_k + P.g - 1) / P.g;
+    const int j = tail ? nb - n_blk_iter + jj : jj;
+    if (j < 0 || j >= nb || j >= P.nb_max)
+        return;
+    const int t0 = j * P.g, t1 = min(t0 + P.g, n_k);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int it = 0; it < P.g; it += TG) {
+        int t = t0 + it + tg;
+        bool ok = t < t1;
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (ok)
+            load8(k + ((k_off + t) * P.h_kv + c) * D + chunk * 8, x);
+        float sc = 1.0f;
+        if (POOL == 1) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                ss += x[e] * x[e];
+            ss = group_sum<L>(ss);
+            sc = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            acc[e] += x[e] * sc;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        sh[tg][chunk * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+        for (int g2 = 0; g2 < TG; g2++)
+            sum += sh[g2][tid];
+        if (POOL == 0)
+            sum *= 1.0f / (float)(t1 - t0);
+        k_cmp[(((long long)c * P.batch + b) * P.nb_max + j) * D + tid] = sum;
+    }
+}
+
 template <typename T, int D>
 static hipError_t launch_compress_t(const KP &P, const void *k, float *k_cmp, int n_blk_iter, int tail,
                                     hipStream_t st)
 {
-    long long threads = (long long)P.batch * n_blk_iter * P.h_kv * (D / 8);
+    long long vectors = (long long)P.batch * n_blk_iter * P.h_kv;
+    if (vectors <= 4096 && P.g >= 16) {          // too few vectors to fill the chip one thread-slice each
+        dim3 grid((unsigned)vectors);
+        if (P.pool == 1)
+            compress_few_kernel<T, D, 1><<<grid, dim3(256), 0, st>>>(P, (const T *)k, k_cmp, n_blk_iter, tail);
+        else
+            compress_few_kernel<T, D, 0><<<grid, dim3(256), 0, st>>>(P, (const T *)k, k_cmp, n_blk_iter, tail);
+        return hipGetLastError();
+    }
+    long long threads = vectors * (D / 8);
     long long blocks = (threads + 255) / 256;
     if (P.pool == 1)
         compress_kernel<T, D, 1><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(

@@ -23,6 +23,7 @@ struct KP {
     float scale;        // softmax scale
     int nb_max;         // ceil(max_k / g)
     long long rows;     // selection rows per KV head
+    int dtype;          // 0 fp32, 1 bf16
 };
 
 struct Seq {
@@ -41,18 +42,18 @@ __device__ __forceinline__ Seq seq_info(const KP &P, int b)
     return s;
 }
 
-// Sequence holding packed query index i (binary search over cu_seqlens_q).
+// Sequence holding packed query index i: the number of b in [1, batch) with
+// cu_seqlens_q[b] <= i, counted with one load per lane and a ballot (no chain
+// of dependent loads).  Every lane of the wavefront must call it with the same i.
 __device__ __forceinline__ int seq_of_query(const KP &P, long long i)
 {
-    int lo = 0, hi = P.batch - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (P.cu_q[mid] <= i)
-            lo = mid;
-        else
-            hi = mid - 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    int cnt = 0;
+    for (int base = 1; base < P.batch; base += kWave) {
+        int b = base + lane;
+        cnt += __popcll(__ballot(b < P.batch && P.cu_q[b] <= i));
     }
-    return lo;
+    return cnt;
 }
 
 // Candidate blocks of a selection row are one contiguous range [j_lo, j_hi):

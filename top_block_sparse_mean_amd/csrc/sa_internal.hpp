@@ -5,7 +5,7 @@
 
 namespace sa {
 
-enum { kSelectEmpty = 0, kSelectFused = 1, kSelectSplit = 2, kSelectTile = 3 };
+enum { kSelectEmpty = 0, kSelectRow = 1, kSelectSplit = 2, kSelectTile = 3 };
 
 hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, int n_tail, hipStream_t st);
 
@@ -13,6 +13,12 @@ int select_plan(const KP &P);
 size_t select_workspace_bytes(const KP &P, int plan);
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
                          int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st);
+
+bool mfma_fwd_ok(const KP &P, int dtype);
+int mfma_fwd_splits(const KP &P);
+hipError_t launch_fwd_mfma(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
+                           const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev0, void *ev1,
+                           hipStream_t st);
 
 int fwd_splits(const KP &P);
 size_t fwd_workspace_bytes(const KP &P, int splits);

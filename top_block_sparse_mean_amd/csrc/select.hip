@@ -9,11 +9,9 @@
 // neighbouring fp32 scores.  Equal scores keep the lower index.
 //
 // Kernels:
-//   select_rows   one workgroup per (row, KV head): streams the candidate
-//                 pooled keys (wavefront dot products), keeps the order keys in
-//                 LDS, wavefront top-k.  Decode rows with up to 4096 candidates.
-//   score_rows    split GEMV for rows with many candidates (token-level draft
-//                 selection): writes order keys to the workspace.
+//   score_rows    decode / shared rows: 64 candidates per workgroup, one round of
+//                 16 B loads per lane (wavefront dot products, xor-shuffle sums),
+//                 order keys to the workspace.
 //   score_tile    prefill: 64 rows x 64 blocks per workgroup, operands staged in
 //                 LDS, fp32 MFMA 16x16x4 (fp32-accurate products), writes keys.
 //   topk_wave     one wavefront per row, keys in registers (<= 2048 candidates).
@@ -23,6 +21,8 @@
 // on its bits (wavefront) or by 8-bit radix passes (workgroup); the output is
 // every key > tau plus the lowest-index keys == tau needed to reach k, written
 // in ascending index order by ballot compaction.
+#include <stdlib.h>
+
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
@@ -70,23 +70,6 @@ __device__ __forceinline__ RowGeo row_geo(const KP &P, long long row)
     return r;
 }
 
-// Qs[e] for e in [e0, e0+n) : sum over the row's queries and group c's heads.
-template <typename T, int D>
-__device__ __forceinline__ float selector_elem(const KP &P, const T *q, const RowGeo &r, int c, int e)
-{
-    float s = 0.f;
-    for (long long i = r.q_first; i < r.q_last; i++) {
-        const T *qi = q + (i * P.h_q + (long long)c * P.G) * D + e;
-        for (int h = 0; h < P.G; h++) {
-            if constexpr (sizeof(T) == 2)
-                s += bf16_to_f32(qi[h * D]);
-            else
-                s += qi[h * D];
-        }
-    }
-    return s;
-}
-
 // Write idx = j_lo .. j_hi-1 (all candidates kept) and the -1 padding.
 __device__ __forceinline__ void write_all(const KP &P, int32_t *out, const RowGeo &r, int t, int nt)
 {
@@ -102,22 +85,22 @@ template <int KPL>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int need, int j_base, int32_t *out)
 {
     const int lane = lane_id();
+    // counts come from ballots (one scalar popcount per slot): no cross-lane data moves
     uint32_t tau = 0;
     for (int bit = 31; bit >= 0; --bit) {
         uint32_t cand = tau | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int m = 0; m < KPL; m++)
-            cnt += (m * kWave + lane < n && key[m] >= cand) ? 1 : 0;
-        cnt = wave_sum_int(cnt);
+            cnt += __popcll(__ballot(m * kWave + lane < n && key[m] >= cand));
         if (cnt >= need)
             tau = cand;
     }
     int gt = 0;
 #pragma unroll
     for (int m = 0; m < KPL; m++)
-        gt += (m * kWave + lane < n && key[m] > tau) ? 1 : 0;
-    int need_eq = need - wave_sum_int(gt);
+        gt += __popcll(__ballot(m * kWave + lane < n && key[m] > tau));
+    int need_eq = need - gt;
     int base = 0, eq_seen = 0;
 #pragma unroll
     for (int m = 0; m < KPL; m++) {
@@ -232,33 +215,11 @@ __device__ void block_topk(const uint32_t *__restrict__ keys, int n, int need, i
 
 // ---------------------------------------------------------------- scoring helpers
 
-// Dot of Qs (this lane's VPL-element slice, in registers) with one key row.
+// Lanes per key row and elements per lane for 16 B loads: pooled fp32 keys
+// (4 floats per lane) or raw keys at g = 1 (8 bf16, or 4 fp32, per lane).
 template <typename KT, int D>
-struct RowDot;
-
-template <int D>
-struct RowDot<float, D> {          // pooled fp32 keys: 4 floats (16 B) per lane
-    static constexpr int VPL = 4, L = D / 4;
-    static __device__ __forceinline__ float dot(const float *row, int sub, const float (&qs)[4])
-    {
-        float4 k = reinterpret_cast<const float4 *>(row)[sub];
-        return qs[0] * k.x + qs[1] * k.y + qs[2] * k.z + qs[3] * k.w;
-    }
-};
-
-template <int D>
-struct RowDot<uint16_t, D> {       // raw bf16 keys (g = 1): 8 elements (16 B) per lane
-    static constexpr int VPL = 8, L = D / 8;
-    static __device__ __forceinline__ float dot(const uint16_t *row, int sub, const float (&qs)[8])
-    {
-        float x[8];
-        load8(row + sub * 8, x);
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            s += qs[e] * x[e];
-        return s;
-    }
+struct RowDot {
+    static constexpr int VPL = 16 / sizeof(KT) < 8 ? 16 / sizeof(KT) : 8, L = D / VPL;
 };
 
 // Pointer to key row j of (sequence, KV head c) for scoring: pooled fp32 or raw.
@@ -270,83 +231,33 @@ __device__ __forceinline__ const KT *key_row(const KP &P, const KT *base, const 
     return base + (((long long)c * P.batch + r.b) * P.nb_max + j) * D;
 }
 
-// ---------------------------------------------------------------- select_rows
+// ---------------------------------------------------------------- score_rows (split)
 
-// grid: (rows, h_kv); NT threads; keys of up to MAXC candidates kept in LDS.
-template <typename T, typename KT, int D, int NT, int MAXC, int U>
-__global__ __launch_bounds__(NT) void select_rows_kernel(KP P, const T *__restrict__ q,
-                                                         const KT *__restrict__ kbase,
-                                                         int32_t *__restrict__ idx,
-                                                         int32_t *__restrict__ n_idx)
+// Selector slice of this lane: Qs[sub*VPL .. +VPL] summed over the row's queries and group c's heads.
+template <typename T, int D, int VPL>
+__device__ __forceinline__ void selector_slice(const KP &P, const T *q, const RowGeo &r, int c, int sub,
+                                               float (&qs)[VPL])
 {
-    using RD = RowDot<KT, D>;
-    constexpr int L = RD::L, VPL = RD::VPL;
-    constexpr int GPW = kWave / L;                 // key rows per wavefront pass
-    constexpr int NG = (NT / kWave) * GPW;         // key rows per workgroup pass
-    __shared__ float qs_sh[D];
-    __shared__ uint32_t keys[MAXC];
-    const long long row = blockIdx.x;
-    const int c = blockIdx.y;
-    const int tid = threadIdx.x;
-    RowGeo r = row_geo(P, row);
-    if (r.n_cand > MAXC) {                             // only if the lengths break the call's max_k
-        r.n_cand = MAXC;
-        r.j_hi = r.j_lo + MAXC;
-        r.need = min(r.need, MAXC);
-    }
-    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
-    if (tid == 0)
-        n_idx[(long long)c * P.rows + row] = r.need;
-    if (r.need == r.n_cand) {
-        write_all(P, out, r, tid, NT);
-        return;
-    }
-    for (int e = tid; e < D; e += NT)
-        qs_sh[e] = selector_elem<T, D>(P, q, r, c, e);
-    __syncthreads();
-    const int lane = lane_id();
-    const int sub = lane % L;
-    const int grp = (tid / kWave) * GPW + lane / L;
-    float qv[VPL];
 #pragma unroll
     for (int e = 0; e < VPL; e++)
-        qv[e] = qs_sh[sub * VPL + e];
-    for (int base = 0; base < r.n_cand; base += NG * U) {
-        float part[U];
+        qs[e] = 0.f;
+    for (long long i = r.q_first; i < r.q_last; i++) {
+        const T *qi = q + (i * P.h_q + (long long)c * P.G) * D + sub * VPL;
+        for (int h = 0; h < P.G; h++) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            int jj = base + u * NG + grp;
-            part[u] = 0.f;
-            if (jj < r.n_cand)
-                part[u] = RD::dot(key_row<KT, D>(P, kbase, r, c, r.j_lo + jj), sub, qv);
+            for (int e = 0; e < VPL; e++) {
+                if constexpr (sizeof(T) == 2)
+                    qs[e] += bf16_to_f32(qi[h * D + e]);
+                else
+                    qs[e] += qi[h * D + e];
+            }
         }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            float s = group_sum<L>(part[u]);
-            int jj = base + u * NG + grp;
-            if (sub == 0 && jj < r.n_cand)
-                keys[jj] = order_key(s);
-        }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-        constexpr int KPL = MAXC / kWave;
-        uint32_t kr[KPL];
-#pragma unroll
-        for (int m = 0; m < KPL; m++) {
-            int i = m * kWave + lane;
-            kr[m] = i < r.n_cand ? keys[i] : 0u;
-        }
-        wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
-        for (int s = r.need + lane; s < P.topk; s += kWave)
-            out[s] = -1;
     }
 }
 
-// ---------------------------------------------------------------- score_rows (split)
-
 // grid: (rows * n_chunk, h_kv), CH candidates per chunk; writes order keys to
-// ws[(c*rows+row)*stride + j].
+// ws[(c*rows+row)*stride + j].  Each lane first issues the loads of all its key
+// rows, then builds its slice of the selector query, then reduces.
 template <typename T, typename KT, int D, int CH>
 __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restrict__ q,
                                                          const KT *__restrict__ kbase,
@@ -354,42 +265,110 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
 {
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
-    constexpr int GPW = kWave / L, NG = 4 * GPW, U = 4;
-    __shared__ float qs_sh[D];
+    constexpr int GPW = kWave / L, NG = 4 * GPW;
+    constexpr int U = (CH + NG - 1) / NG;
     const long long row = blockIdx.x / n_chunk;
     const int chunk = (int)(blockIdx.x % n_chunk);
     const int c = blockIdx.y;
     RowGeo r = row_geo(P, row);
     if (r.need == r.n_cand)
         return;
-    int j0 = r.j_lo + chunk * CH;
-    int j1 = min(j0 + CH, r.j_hi);
+    const int j0 = r.j_lo + chunk * CH;
+    const int j1 = min(j0 + CH, r.j_hi);
     if (j0 >= j1)
         return;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < D; e += 256)
-        qs_sh[e] = selector_elem<T, D>(P, q, r, c, e);
-    __syncthreads();
-    const int lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        int j = min(j0 + u * NG + grp, j1 - 1);
+        raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, j))[sub];
+    }
     float qv[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; e++)
-        qv[e] = qs_sh[sub * VPL + e];
+    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
     uint32_t *dst = ws + ((long long)c * P.rows + row) * stride;
-    for (int base = j0; base < j1; base += NG * U) {
-        float part[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            int j = base + u * NG + grp;
-            part[u] = j < j1 ? RD::dot(key_row<KT, D>(P, kbase, r, c, j), sub, qv) : 0.f;
-        }
+    for (int u = 0; u < U; u++) {
+        float part = 0.f;
+        if constexpr (VPL == 4) {
+            part = qv[0] * __uint_as_float(raw[u].x) + qv[1] * __uint_as_float(raw[u].y) +
+                   qv[2] * __uint_as_float(raw[u].z) + qv[3] * __uint_as_float(raw[u].w);
+        } else {
+            uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            float s = group_sum<L>(part[u]);
-            int j = base + u * NG + grp;
-            if (sub == 0 && j < j1)
-                dst[j] = order_key(s);
+            for (int e = 0; e < 4; e++)
+                part += qv[2 * e] * __uint_as_float(wd[e] << 16) + qv[2 * e + 1] * __uint_as_float(wd[e] & 0xffff0000u);
         }
+        float sc = group_sum<L>(part);
+        int j = j0 + u * NG + grp;
+        if (sub == 0 && j < j1)
+            dst[j] = order_key(sc);
+    }
+}
+
+// ---------------------------------------------------------------- select_row (fused)
+
+// One 1024-thread workgroup per (row, KV head) for rows with at most 64*KPL
+// candidates: every lane issues the loads of all its key rows at once, the
+// order keys go to LDS, wavefront 0 selects.  No workspace, one launch.
+template <typename T, typename KT, int D, int KPL>
+__global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
+                                                          const KT *__restrict__ kbase,
+                                                          int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+{
+    using RD = RowDot<KT, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L, NG = 16 * GPW, MAXC = 64 * KPL;
+    constexpr int U = (MAXC + NG - 1) / NG;
+    __shared__ uint32_t keys[MAXC];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y;
+    const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (tid == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, tid, 1024);
+        return;
+    }
+    const int n = min(r.n_cand, MAXC);
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        int jj = min(u * NG + grp, n - 1);
+        raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, r.j_lo + jj))[sub];
+    }
+    float qv[VPL];
+    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        float part = 0.f;
+        if constexpr (VPL == 4) {
+            part = qv[0] * __uint_as_float(raw[u].x) + qv[1] * __uint_as_float(raw[u].y) +
+                   qv[2] * __uint_as_float(raw[u].z) + qv[3] * __uint_as_float(raw[u].w);
+        } else {
+            uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                part += qv[2 * e] * __uint_as_float(wd[e] << 16) + qv[2 * e + 1] * __uint_as_float(wd[e] & 0xffff0000u);
+        }
+        float sc = group_sum<L>(part);
+        int jj = u * NG + grp;
+        if (sub == 0 && jj < n)
+            keys[jj] = order_key(sc);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        uint32_t kr[KPL];
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            int i = m * kWave + lane;
+            kr[m] = i < n ? keys[i] : 0u;
+        }
+        wave_topk<KPL>(kr, n, min(r.need, n), r.j_lo, out);
+        for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
+            out[s2] = -1;
     }
 }
 
@@ -503,7 +482,8 @@ __global__ __launch_bounds__(256) void score_tile_kernel(KP P, const T *__restri
 
 // ---------------------------------------------------------------- top-k over the workspace
 
-// 4 wavefronts per workgroup, one row each (<= 2048 candidates).  grid: (ceil(rows/4), h_kv).
+// 4 wavefronts per workgroup, one row each (<= 64 * KPL candidates).  grid: (ceil(rows/4), h_kv).
+template <int KPL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__restrict__ ws,
                                                         long long stride, int32_t *__restrict__ idx,
                                                         int32_t *__restrict__ n_idx)
@@ -512,6 +492,16 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     const int c = blockIdx.y, lane = lane_id();
     if (row >= P.rows)
         return;
+    // the candidate range of any row with candidates starts at n_init / g: load first, then
+    // resolve the row's geometry while the loads are in flight
+    const int j_first = P.n_init / P.g;
+    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
+    uint32_t kr[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        long long j = j_first + m * kWave + lane;
+        kr[m] = j < stride ? src[j] : 0u;
+    }
     RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     if (lane == 0)
@@ -519,14 +509,6 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     if (r.need == r.n_cand) {
         write_all(P, out, r, lane, kWave);
         return;
-    }
-    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride + r.j_lo;
-    constexpr int KPL = 32;
-    uint32_t kr[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; m++) {
-        int i = m * kWave + lane;
-        kr[m] = i < r.n_cand ? src[i] : 0u;
     }
     wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
     for (int s = r.need + lane; s < P.topk; s += kWave)
@@ -564,13 +546,13 @@ __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 
 // ---------------------------------------------------------------- dispatch
 
-static constexpr int kFusedMaxCand = 4096;
 static constexpr int kWaveTopkMax = 2048;
-static constexpr int kSplitChunk = 2048;
+static constexpr int kRowMaxCand = 1024;
+static constexpr int kSplitChunk = 64;   // candidates per scoring workgroup: one round of loads
 
 size_t select_workspace_bytes(const KP &P, int plan)
 {
-    if (plan == kSelectFused || plan == kSelectEmpty)
+    if (plan == kSelectEmpty || plan == kSelectRow)
         return 0;
     long long stride = P.g == 1 ? P.max_k : P.nb_max;
     return (size_t)P.h_kv * (size_t)P.rows * (size_t)stride * sizeof(uint32_t);
@@ -580,11 +562,15 @@ int select_plan(const KP &P)
 {
     if (P.topk == 0)
         return kSelectEmpty;
-    long long max_cand = P.g == 1 ? P.max_k : P.nb_max;
     bool few_rows = P.shared || P.max_q <= 8;
-    if (few_rows)
-        return max_cand <= kFusedMaxCand ? kSelectFused : kSelectSplit;
-    return kSelectTile;
+    long long max_cand = P.g == 1 ? P.max_k : P.nb_max;
+    int plan = !few_rows ? kSelectTile : (max_cand <= kRowMaxCand ? kSelectRow : kSelectSplit);
+    if (const char *e = getenv("SPARSE_ATTN_SELECT_PLAN")) {       // tuning override
+        int v = atoi(e);
+        if (few_rows && (v == kSelectSplit || (v == kSelectRow && max_cand <= kRowMaxCand)))
+            plan = v;
+    }
+    return plan;
 }
 
 template <typename T, int D>
@@ -600,14 +586,19 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         select_empty_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(P, n_idx);
         return hipGetLastError();
     }
-    if (plan == kSelectFused) {
+    if (plan == kSelectRow) {
         dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
-        if (P.g == 1)
-            select_rows_kernel<T, T, D, 1024, kFusedMaxCand, 8><<<grid, dim3(1024), 0, st>>>(
-                P, q, (const T *)k, idx, n_idx);
-        else
-            select_rows_kernel<T, float, D, 1024, kFusedMaxCand, 8><<<grid, dim3(1024), 0, st>>>(
-                P, q, k_cmp, idx, n_idx);
+        if (P.g == 1) {
+            if (stride <= 512)
+                select_row_kernel<T, T, D, 8><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
+            else
+                select_row_kernel<T, T, D, 16><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
+        } else {
+            if (stride <= 512)
+                select_row_kernel<T, float, D, 8><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
+            else
+                select_row_kernel<T, float, D, 16><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
+        }
         return hipGetLastError();
     }
     if (plan == kSelectSplit) {
@@ -629,9 +620,15 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (stride <= kWaveTopkMax)
-        topk_wave_kernel<<<dim3((unsigned)((P.rows + 3) / 4), (unsigned)P.h_kv), dim3(256), 0, st>>>(
-            P, wsk, stride, idx, n_idx);
+    dim3 tgrid((unsigned)((P.rows + 3) / 4), (unsigned)P.h_kv);
+    if (stride <= 256)
+        topk_wave_kernel<4><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
+    else if (stride <= 512)
+        topk_wave_kernel<8><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
+    else if (stride <= 1024)
+        topk_wave_kernel<16><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
+    else if (stride <= kWaveTopkMax)
+        topk_wave_kernel<32><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
     else
         topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
             P, wsk, stride, idx, n_idx);

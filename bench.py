@@ -98,6 +98,26 @@ def attended_total_exact(w, idx_host, n_idx_host):
     return tot
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    record (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain
+    1 GiB device copy), or None when the record is for another workload or the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", "attn_mfma_decode_32k_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("workload") != workload:
+        return None
+    src = open(os.path.join(HERE, rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    kib = (rec["fetch_kib_per_dispatch"] * rec["fetch_calibration"]["factor"]
+           + rec["write_kib_per_dispatch"] * rec["write_calibration"]["factor"])
+    return int(kib * 1024)
+
+
 def cpu_baseline(w, x, seconds=10.0):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -218,7 +238,7 @@ def main():
         roof["frac"] = round(roof["achieved"] / BF16_PEAK_TFLOPS, 4)
         value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
         attn_bytes = None
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
 
     extra = {}
     if w.name == "bf16_decode_32k":

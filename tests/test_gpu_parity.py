@@ -46,6 +46,10 @@ EDGE = {
     "d64_bf16": dict(head_dim=64),
     "group1": dict(h_q=8, h_kv=8),
     "l2sum": dict(pool=POOL_L2SUM, block=4, topk=9),
+    # multi-query union tiles (per-query selection, block a multiple of 32)
+    "tile_d64": dict(head_dim=64, block=32, topk=7),
+    "tile_g8": dict(h_q=16, h_kv=2, block=64, topk=4, n_init=64, window=100),
+    "tile_g16": dict(h_q=16, h_kv=1, block=32, topk=5, n_init=0, window=33),
 }
 
 

@@ -273,6 +273,244 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
     }
 }
 
+// ---------------------------------------------------------------- union tiles (prefill)
+
+// Load one 32-token key tile starting at token t0 (contiguous), with the lane's
+// 8-bit live mask taken from the 32-bit token mask of its row.
+template <int D>
+__device__ __forceinline__ void load_tile(ChunkRegs<D> &r, int t0, int n_k, uint32_t m32, const uint16_t *kb,
+                                          const uint16_t *vb, long long tstride, int rr, int g4)
+{
+    constexpr int KS = D / 32;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        int t = min(t0 + 16 * s + rr, n_k - 1);
+        long long off = (long long)t * tstride + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            r.k[s][ks] = ld16(kb + off + 32 * ks);
+    }
+    r.live = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int off = i < 4 ? 4 * g4 + i : 16 + 4 * g4 + (i - 4);
+        int t = min(t0 + off, n_k - 1);
+        r.live |= ((m32 >> off) & 1u) << i;
+        if (D == 128 || rr < D / 8)
+            r.v[i] = ld16(vb + (long long)t * tstride + 8 * rr);
+        else
+            r.v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Tokens [t0, t0+32) of a query at p with window start lo_w and the tile's
+// selected bit: causal & (init | window | selected block).
+__device__ __forceinline__ uint32_t tile_mask(int t0, int p, int n_init, int lo_w, bool sel)
+{
+    auto below = [](int n) -> uint32_t {      // bits [0, n) for n clamped to [0, 32]
+        return n <= 0 ? 0u : (n >= 32 ? 0xffffffffu : ((1u << n) - 1u));
+    };
+    uint32_t causal = below(p - t0 + 1);
+    uint32_t init = below(n_init - t0);
+    uint32_t win = ~below(lo_w - t0);
+    return causal & (init | win | (sel ? 0xffffffffu : 0u));
+}
+
+constexpr int kTileWaves = 4;
+constexpr int kTileMax = 4096;             // 32-token tiles per sequence (max_k <= 131072)
+constexpr int kTileWords = kTileMax / 32;
+
+// grid: 1-D, n_qtile * batch * h_kv workgroups, remapped so that each XCD
+// (blockIdx % 8) works through a contiguous range of (sequence, KV head, query
+// tile) items.  Wavefront w owns 16/G consecutive queries = 16 rows.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v,
+                                                           const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ n_idx,
+                                                           uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                           int n_qtile)
+{
+    constexpr int KS = D / 32;
+    __shared__ uint32_t sh_sel[kTileWaves][4][kTileWords];   // per-query selected-tile bits (G >= 4)
+    __shared__ uint32_t sh_uni[kTileWaves][kTileWords];
+    __shared__ int sh_list[kTileWaves][kTileMax];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rr = lane & 15, g4 = lane >> 4;
+    // XCD-contiguous work mapping
+    const long long n_items = (long long)n_qtile * P.batch * P.h_kv;
+    const long long per_xcd = (n_items + 7) / 8;
+    const long long item = (long long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= n_items)
+        return;
+    const int qt = (int)(item % n_qtile);
+    const int c = (int)((item / n_qtile) % P.h_kv);
+    const int b = (int)(item / ((long long)n_qtile * P.h_kv));
+    const Seq s = seq_info(P, b);
+    const int QPW = 16 / P.G;                       // queries per wavefront (<= 4)
+    const int qw0 = qt * kTileWaves * QPW + w * QPW;    // first local query of this wave
+    const int nqw = max(0, min(QPW, s.n_q - qw0));
+    const int ntile = (s.n_k + 31) / 32;
+    const int nword = (ntile + 31) / 32;
+    for (int x = lane; x < 4 * kTileWords; x += kWave)
+        (&sh_sel[w][0][0])[x] = 0u;
+    for (int x = lane; x < kTileWords; x += kWave)
+        sh_uni[w][x] = 0u;
+    __syncthreads();
+    // selected tiles of each query of the wave
+    const int tpb = P.g / 32;                       // tiles per pooled block
+    for (int qq = 0; qq < nqw; qq++) {
+        const long long qi = s.q_off + qw0 + qq;
+        const int32_t *sel = idx + ((long long)c * P.rows + qi) * P.topk;
+        int ns = n_idx[(long long)c * P.rows + qi];
+        ns = ns < 0 ? 0 : (ns > P.topk ? P.topk : ns);
+        for (int e = lane; e < ns * tpb; e += kWave) {
+            int tile = sel[e / tpb] * tpb + e % tpb;
+            if (tile >= 0 && tile < ntile) {
+                atomicOr(&sh_sel[w][qq][tile >> 5], 1u << (tile & 31));
+                atomicOr(&sh_uni[w][tile >> 5], 1u << (tile & 31));
+            }
+        }
+    }
+    // init and window tiles of the wave's queries
+    int p_first = s.q0 + qw0, p_last = s.q0 + qw0 + nqw - 1;
+    if (nqw > 0) {
+        int lo_first = max(P.n_init, p_first - P.window + 1);
+        int i_hi = (min(P.n_init, p_last + 1) + 31) / 32;          // init tiles [0, i_hi)
+        for (int tile = lane; tile < i_hi; tile += kWave)
+            atomicOr(&sh_uni[w][tile >> 5], 1u << (tile & 31));
+        for (int tile = lo_first / 32 + lane; tile <= p_last / 32; tile += kWave)
+            atomicOr(&sh_uni[w][tile >> 5], 1u << (tile & 31));
+    }
+    __syncthreads();
+    // compact the union into an ascending tile list
+    int n_list = 0;
+    for (int base = 0; base < nword; base += kWave) {
+        int wd = base + lane;
+        uint32_t bits = wd < nword ? sh_uni[w][wd] : 0u;
+        int cnt = __popc(bits);
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            int t = __shfl_up(incl, o, kWave);
+            if (lane >= o)
+                incl += t;
+        }
+        int pos = n_list + incl - cnt;
+        while (bits) {
+            int bit = __ffs(bits) - 1;
+            bits &= bits - 1;
+            sh_list[w][pos++] = wd * 32 + bit;
+        }
+        n_list += __shfl(incl, kWave - 1, kWave);
+    }
+    __syncthreads();
+
+    // this lane's row: query qq = rr / G, head c*G + rr % G
+    const int qq = rr / P.G;
+    const bool row_ok = qq < nqw;
+    const long long qi = s.q_off + qw0 + (row_ok ? qq : 0);
+    const int p_row = row_ok ? s.q0 + qw0 + qq : -1;
+    const int lo_w = max(P.n_init, p_row - P.window + 1);
+    bf16x8 qop[KS];
+    if (row_ok) {
+        const uint16_t *qp = q + (qi * P.h_q + c * P.G + rr % P.G) * D + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    const uint32_t *selw = sh_sel[w][row_ok ? qq : 0];
+    auto row_mask = [&](int tile) -> uint32_t {
+        if (!row_ok)
+            return 0u;
+        bool sb = (selw[tile >> 5] >> (tile & 31)) & 1u;
+        return tile_mask(tile * 32, p_row, P.n_init, lo_w, sb);
+    };
+    const long long tstride = (long long)P.h_kv * D;
+    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
+    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int p = 0; p < 8; p++)
+        acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ChunkRegs<D> ra, rb;
+    if (n_list > 0) {
+        int t = sh_list[w][0];
+        load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+    }
+    for (int it = 0; it < n_list; it += 2) {
+        if (it + 1 < n_list) {
+            int t = sh_list[w][it + 1];
+            load_tile<D>(rb, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+        }
+        compute_chunk<D>(ra, qop, P.scale_log2, g4, m_run, l_part, acc);
+        if (it + 1 >= n_list)
+            break;
+        if (it + 2 < n_list) {
+            int t = sh_list[w][it + 2];
+            load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+        }
+        compute_chunk<D>(rb, qop, P.scale_log2, g4, m_run, l_part, acc);
+    }
+    float l_row = l_part + __shfl_xor(l_part, 16, kWave);
+    l_row += __shfl_xor(l_row, 32, kWave);
+    // output: lane (g4 group) holds rows 4*g4 + r4, head-dim 8*rr + p; the row's
+    // (max, sum) live in lanes with lane%16 == row
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+        const int row = 4 * g4 + r4;
+        const float lrow = __shfl(l_row, row, kWave);
+        const float mrow = __shfl(m_run, row, kWave);
+        const int rq = row / P.G;
+        if (rq < nqw && (D == 128 || rr < D / 8)) {
+            const long long oq = s.q_off + qw0 + rq;
+            const int h = c * P.G + row % P.G;
+            const float inv = 1.0f / lrow;
+            float o8[8];
+#pragma unroll
+            for (int p = 0; p < 8; p++)
+                o8[p] = acc[p][r4] * inv;
+            store8(out + (oq * P.h_q + h) * D + 8 * rr, o8);
+            if (lse && rr == 0)
+                lse[(long long)h * P.total_q + oq] = (mrow + log2f(lrow)) * 0.69314718055994531f;
+        }
+    }
+}
+
+bool tile_fwd_ok(const KP &P, int dtype)
+{
+    return dtype == 1 && !P.shared && P.G >= 4 && P.G <= 16 && 16 % P.G == 0 && P.g % 32 == 0 &&
+           P.max_k <= kTileMax * 32 && P.max_q > 64;
+}
+
+hipError_t launch_fwd_tile(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
+                           const int32_t *n_idx, void *out, float *lse, void *ev0, void *ev1, hipStream_t st)
+{
+    const int qpw = 16 / P.G;
+    const int n_qtile = (P.max_q + kTileWaves * qpw - 1) / (kTileWaves * qpw);
+    const long long n_items = (long long)n_qtile * P.batch * P.h_kv;
+    const long long grid = ((n_items + 7) / 8) * 8;
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev0, st);
+    if (P.d == 128)
+        attn_tile_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, st>>>(
+            P, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
+            n_qtile);
+    else
+        attn_tile_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, st>>>(
+            P, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
+            n_qtile);
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev1, st);
+    return hipGetLastError();
+}
+
 bool mfma_fwd_ok(const KP &P, int dtype)
 {
     if (dtype != 1)

@@ -255,9 +255,27 @@ __device__ __forceinline__ void selector_slice(const KP &P, const T *q, const Ro
     }
 }
 
-// grid: (rows * n_chunk, h_kv), CH candidates per chunk; writes order keys to
-// ws[(c*rows+row)*stride + j].  Each lane first issues the loads of all its key
-// rows, then builds its slice of the selector query, then reduces.
+// Partial dot of one 16 B key slice with this lane's selector slice.
+template <int VPL>
+__device__ __forceinline__ float slice_dot(const uint4 &raw, const float (&qv)[VPL])
+{
+    if constexpr (VPL == 4) {
+        return qv[0] * __uint_as_float(raw.x) + qv[1] * __uint_as_float(raw.y) + qv[2] * __uint_as_float(raw.z) +
+               qv[3] * __uint_as_float(raw.w);
+    } else {
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            part += qv[2 * e] * __uint_as_float(wd[e] << 16) + qv[2 * e + 1] * __uint_as_float(wd[e] & 0xffff0000u);
+        return part;
+    }
+}
+
+// grid: (rows * n_chunk, h_kv), CH candidates per workgroup in rounds of U x NG rows;
+// writes order keys to ws[(c*rows+row)*stride + j].  The loads of round r+1 are
+// issued before round r is reduced; the selector slice is built while the first
+// round is in flight.
 template <typename T, typename KT, int D, int CH>
 __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restrict__ q,
                                                          const KT *__restrict__ kbase,
@@ -266,7 +284,8 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
     constexpr int GPW = kWave / L, NG = 4 * GPW;
-    constexpr int U = (CH + NG - 1) / NG;
+    constexpr int U = 64 / NG < 1 ? 1 : 64 / NG;      // 64 rows per round
+    constexpr int RW = U * NG;
     const long long row = blockIdx.x / n_chunk;
     const int chunk = (int)(blockIdx.x % n_chunk);
     const int c = blockIdx.y;
@@ -278,31 +297,37 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     if (j0 >= j1)
         return;
     const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
-    uint4 raw[U];
+    const int rounds = (j1 - j0 + RW - 1) / RW;
+    uint4 ra[U], rb[U];
+    auto load = [&](uint4 (&raw)[U], int rd) {
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        int j = min(j0 + u * NG + grp, j1 - 1);
-        raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, j))[sub];
-    }
-    float qv[VPL];
-    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
-    uint32_t *dst = ws + ((long long)c * P.rows + row) * stride;
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        float part = 0.f;
-        if constexpr (VPL == 4) {
-            part = qv[0] * __uint_as_float(raw[u].x) + qv[1] * __uint_as_float(raw[u].y) +
-                   qv[2] * __uint_as_float(raw[u].z) + qv[3] * __uint_as_float(raw[u].w);
-        } else {
-            uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                part += qv[2 * e] * __uint_as_float(wd[e] << 16) + qv[2 * e + 1] * __uint_as_float(wd[e] & 0xffff0000u);
+        for (int u = 0; u < U; u++) {
+            int j = min(j0 + rd * RW + u * NG + grp, j1 - 1);
+            raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, j))[sub];
         }
-        float sc = group_sum<L>(part);
-        int j = j0 + u * NG + grp;
-        if (sub == 0 && j < j1)
-            dst[j] = order_key(sc);
+    };
+    uint32_t *dst = ws + ((long long)c * P.rows + row) * stride;
+    float qv[VPL];
+    auto reduce = [&](const uint4 (&raw)[U], int rd) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
+            int j = j0 + rd * RW + u * NG + grp;
+            if (sub == 0 && j < j1)
+                dst[j] = order_key(sc);
+        }
+    };
+    load(ra, 0);
+    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
+    for (int rd = 0; rd < rounds; rd += 2) {
+        if (rd + 1 < rounds)
+            load(rb, rd + 1);
+        reduce(ra, rd);
+        if (rd + 1 >= rounds)
+            break;
+        if (rd + 2 < rounds)
+            load(ra, rd + 2);
+        reduce(rb, rd + 1);
     }
 }
 
@@ -343,17 +368,7 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        float part = 0.f;
-        if constexpr (VPL == 4) {
-            part = qv[0] * __uint_as_float(raw[u].x) + qv[1] * __uint_as_float(raw[u].y) +
-                   qv[2] * __uint_as_float(raw[u].z) + qv[3] * __uint_as_float(raw[u].w);
-        } else {
-            uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                part += qv[2 * e] * __uint_as_float(wd[e] << 16) + qv[2 * e + 1] * __uint_as_float(wd[e] & 0xffff0000u);
-        }
-        float sc = group_sum<L>(part);
+        float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
         int jj = u * NG + grp;
         if (sub == 0 && jj < n)
             keys[jj] = order_key(sc);
@@ -515,6 +530,115 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
         out[s] = -1;
 }
 
+// One 1024-thread workgroup per row with up to 1024 * KPT candidates held in
+// registers (key i in thread i % 1024, slot i / 1024).  tau is found by a
+// binary search on its bits; counts are wave ballots summed through LDS (one
+// barrier per bit).  The output is written in index order from per-(slot, wave)
+// counts, so it needs only three more barriers.  grid: (rows, h_kv).
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_regs_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
+                                                         int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+{
+    constexpr int NT = 1024, NW = NT / kWave;
+    __shared__ int sh_cnt[2][NW];
+    __shared__ int sh_gt[KPT][NW], sh_eq[KPT][NW];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int j_first = P.n_init / P.g;
+    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (tid == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, tid, NT);
+        return;
+    }
+    const int n = min(r.n_cand, NT * KPT);
+    const int need = min(r.need, n);
+    const int slots = (n + NT - 1) / NT;            // slots holding candidates (uniform)
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int m = 0; m < KPT; m++) {
+        long long j = j_first + (long long)m * NT + tid;
+        kr[m] = (m < slots && j < stride) ? src[j] : 0u;
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < KPT; m++)
+            if (m < slots)
+                cnt += __popcll(__ballot(m * NT + tid < n && kr[m] >= cand));
+        if (lane == 0)
+            sh_cnt[bit & 1][w] = cnt;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int x = 0; x < NW; x++)
+            tot += sh_cnt[bit & 1][x];
+        if (tot >= need)
+            tau = cand;
+    }
+    // per (slot, wave) counts of keys above tau and equal to tau
+    int g_tot = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; m++) {
+        if (m >= slots)
+            break;
+        bool valid = m * NT + tid < n;
+        int g = __popcll(__ballot(valid && kr[m] > tau));
+        int e = __popcll(__ballot(valid && kr[m] == tau));
+        g_tot += g;
+        if (lane == 0) {
+            sh_gt[m][w] = g;
+            sh_eq[m][w] = e;
+        }
+    }
+    __syncthreads();                                   // every wave has read sh_cnt too
+    if (lane == 0)
+        sh_cnt[0][w] = g_tot;
+    __syncthreads();
+    int n_gt = 0;
+#pragma unroll
+    for (int x = 0; x < NW; x++)
+        n_gt += sh_cnt[0][x];
+    const int need_eq = need - n_gt;
+    // output position of a selected key = selected keys before it in index order
+    // (index = slot * 1024 + wave * 64 + lane)
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; m++) {
+        if (m >= slots)
+            break;
+        int eq_m_before_w = 0, gt_m_before_w = 0, eq_m = 0, gt_m = 0;
+#pragma unroll
+        for (int x = 0; x < NW; x++) {
+            int e = sh_eq[m][x], g = sh_gt[m][x];
+            eq_m_before_w += x < w ? e : 0;
+            gt_m_before_w += x < w ? g : 0;
+            eq_m += e;
+            gt_m += g;
+        }
+        const bool valid = m * NT + tid < n;
+        const bool is_gt = valid && kr[m] > tau, is_eq = valid && kr[m] == tau;
+        const unsigned long long meq = __ballot(is_eq);
+        const int eq_rank = eq_before + eq_m_before_w + lanes_below(meq);
+        const bool s_eq = is_eq && eq_rank < need_eq;
+        const unsigned long long msel = __ballot(is_gt || s_eq);
+        // selected before this lane = gt before + eq selected before
+        const int eq_sel_before_wave = min(max(need_eq - eq_before, 0), eq_m_before_w);
+        const int pos = sel_before + gt_m_before_w + eq_sel_before_wave + lanes_below(msel);
+        if (is_gt || s_eq)
+            out[pos] = r.j_lo + m * NT + tid;
+        sel_before += gt_m + min(max(need_eq - eq_before, 0), eq_m);
+        eq_before += eq_m;
+    }
+    for (int s2 = need + tid; s2 < P.topk; s2 += NT)
+        out[s2] = -1;
+}
+
 // One workgroup per row.  grid: (rows, h_kv).
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_block_kernel(KP P, const uint32_t *__restrict__ ws,
@@ -548,7 +672,7 @@ __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 
 static constexpr int kWaveTopkMax = 2048;
 static constexpr int kRowMaxCand = 1024;
-static constexpr int kSplitChunk = 64;   // candidates per scoring workgroup: one round of loads
+static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (8 rounds of 64)
 
 size_t select_workspace_bytes(const KP &P, int plan)
 {
@@ -629,6 +753,12 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         topk_wave_kernel<16><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
     else if (stride <= kWaveTopkMax)
         topk_wave_kernel<32><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
+    else if (stride <= 8192)
+        topk_regs_kernel<8><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
+                                                                                           n_idx);
+    else if (stride <= 32768)
+        topk_regs_kernel<32><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
+                                                                                            n_idx);
     else
         topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
             P, wsk, stride, idx, n_idx);

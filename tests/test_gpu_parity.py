@@ -48,8 +48,11 @@ EDGE = {
     "l2sum": dict(pool=POOL_L2SUM, block=4, topk=9),
     # multi-query union tiles (per-query selection, block a multiple of 32)
     "tile_d64": dict(head_dim=64, block=32, topk=7),
-    "tile_g8": dict(h_q=16, h_kv=2, block=64, topk=4, n_init=64, window=100),
     "tile_g16": dict(h_q=16, h_kv=1, block=32, topk=5, n_init=0, window=33),
+    # LDS-shared 64-token tiles (block 64, a sequence of >= 256 queries)
+    "wg_g4": dict(block=64, topk=5),
+    "wg_g8": dict(h_q=16, h_kv=2, block=64, topk=4, n_init=64, window=100),
+    "wg_g16_window1": dict(h_q=16, h_kv=1, block=64, topk=3, n_init=0, window=1),
 }
 
 
@@ -108,6 +111,39 @@ def test_split_selection_path():
     parity.full_check(w, x, xg)
 
 
+def _integer_inputs(w, lo=-2, hi=2, seed=0):
+    """Small-integer Q and K: every score is exact in fp32 and fp64, so ties are exact
+    and the GPU must resolve them exactly like the oracle (lower index first)."""
+    g = torch.Generator().manual_seed(seed)
+    x = generate(w)
+    x["q"] = torch.randint(lo, hi + 1, x["q"].shape, generator=g).to(x["q"].dtype)
+    x["k"] = torch.randint(lo, hi + 1, x["k"].shape, generator=g).to(x["k"].dtype)
+    return x
+
+
+@pytest.mark.parametrize("case", ["wave", "compact", "tile"])
+def test_topk_exact_ties(case):
+    from workloads import draft_decode
+    if case == "compact":      # token-level shared rows with > 2048 candidates
+        w = draft_decode(batch=3, median=5000, lo=4500, hi=9000, seed=11)
+    elif case == "wave":       # decode rows, <= 2048 candidates
+        w = small("bf16_decode_32k")
+    else:                      # prefill rows (MFMA fp32 scores) with 4097 candidates, mean pooling
+        w = small("bf16_chunked_prefill_1m").scaled(pool=POOL_MEAN)
+    x = _integer_inputs(w)
+    parity.full_check(w, x, parity.to_device(x))
+
+
+def test_topk_all_scores_equal():
+    """Every candidate scores the same: the k lowest indices (all-equal keys overflow the
+    compaction buffer of the large-row top-k)."""
+    from workloads import draft_decode
+    w = draft_decode(batch=2, median=9000, lo=8000, hi=12000, seed=12)
+    x = generate(w)
+    x["k"] = torch.ones_like(x["k"])
+    parity.full_check(w, x, parity.to_device(x))
+
+
 def test_deterministic():
     w = small("bf16_prefill_128k")
     x, xg = parity.gen_pair(w)
@@ -152,6 +188,8 @@ def _sampled(w, n_rows, n_req, seed=0):
     att = oracle.attend(w, x["q"], x["k"], x["v"], gp["idx"], gp["n_idx"], reqs=reqs, heads=hs)
     gout = gp["out"].reshape(w.total_q, w.h_q, w.head_dim)[reqs, hs].double().numpy()
     parity.check_output(w, gout, att["out"])
+    lse_g = gp["lse"][torch.from_numpy(hs), torch.from_numpy(reqs)].double().numpy()
+    assert np.abs(lse_g - att["lse"]).max() < 1e-4
     # GPU attention on a table whose sampled rows hold the oracle's selection
     idx2, n2 = gp["idx"].copy(), gp["n_idx"].copy()
     idx2[sel["heads"], sel["rows"]] = sel["idx"]

@@ -216,7 +216,7 @@ static int head_chunk(const KP &P) { return P.G < 4 ? P.G : 4; }
 
 int fwd_splits(const KP &P)
 {
-    if (tile_fwd_ok(P, P.dtype))
+    if (wg_fwd_ok(P, P.dtype) || tile_fwd_ok(P, P.dtype))
         return 1;
     if (mfma_fwd_ok(P, P.dtype))
         return mfma_fwd_splits(P);
@@ -285,6 +285,8 @@ hipError_t launch_fwd(const KP &P, int dtype, const void *q, const void *k, cons
                       const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev0, void *ev1,
                       hipStream_t st)
 {
+    if (wg_fwd_ok(P, dtype))
+        return launch_fwd_wg(P, q, k, v, idx, n_idx, out, lse, ev0, ev1, st);
     if (tile_fwd_ok(P, dtype))
         return launch_fwd_tile(P, q, k, v, idx, n_idx, out, lse, ev0, ev1, st);
     if (mfma_fwd_ok(P, dtype)) {

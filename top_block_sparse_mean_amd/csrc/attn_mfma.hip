@@ -65,8 +65,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D> &r, const int *tok, int 
 }
 
 template <int D>
-__device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, const bf16x8 (&qop)[D / 32], float scale_log2,
-                                              int g4, float &m_run, float &l_part, f32x4 (&acc)[8])
+__device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, uint32_t live, const bf16x8 (&qop)[D / 32],
+                                              float scale_log2, int g4, float &m_run, float &l_part, f32x4 (&acc)[8])
 {
     constexpr int KS = D / 32;
     f32x4 st[2];
@@ -83,7 +83,7 @@ __device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, const bf16x
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         float x = st[i >> 2][i & 3] * scale_log2;
-        sv[i] = (r.live >> i) & 1u ? x : -INFINITY;
+        sv[i] = (live >> i) & 1u ? x : -INFINITY;
         mc = fmaxf(mc, sv[i]);
     }
     mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
@@ -120,6 +120,31 @@ __device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, const bf16x
 }
 
 constexpr int kTokCap = 8192;
+
+// Exclusive scan of one int per thread over a 512-thread workgroup; (exclusive, total).
+__device__ __forceinline__ int2 block_scan_int_512(int v, int *sh)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int t = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += t;
+    }
+    if (lane == kWave - 1)
+        sh[w] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int c = sh[i];
+        off += i < w ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    return make_int2(off + incl - v, tot);
+}
 constexpr int kSelCap = 4096;
 
 // grid: (units * h_kv, splits); 256 threads.  unit = query (per-query selection) or sequence (shared).
@@ -218,13 +243,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
         const int c1 = ch + 4;
         if (32 * c1 < n)
             load_chunk<D>(rb, sh_tok, 32 * c1, n, kb, vb, tstride, rr, g4, p_row);
-        compute_chunk<D>(ra, qop, P.scale_log2, g4, m_run, l_part, acc);
+        compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
         if (32 * c1 >= n)
             break;
         const int c2 = c1 + 4;
         if (32 * c2 < n)
             load_chunk<D>(ra, sh_tok, 32 * c2, n, kb, vb, tstride, rr, g4, p_row);
-        compute_chunk<D>(rb, qop, P.scale_log2, g4, m_run, l_part, acc);
+        compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
     }
     float l_row = l_part + __shfl_xor(l_part, 16, kWave);
     l_row += __shfl_xor(l_row, 32, kWave);
@@ -449,14 +474,14 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
             int t = sh_list[w][it + 1];
             load_tile<D>(rb, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
         }
-        compute_chunk<D>(ra, qop, P.scale_log2, g4, m_run, l_part, acc);
+        compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
         if (it + 1 >= n_list)
             break;
         if (it + 2 < n_list) {
             int t = sh_list[w][it + 2];
             load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
         }
-        compute_chunk<D>(rb, qop, P.scale_log2, g4, m_run, l_part, acc);
+        compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
     }
     float l_row = l_part + __shfl_xor(l_part, 16, kWave);
     l_row += __shfl_xor(l_row, 32, kWave);
@@ -481,6 +506,356 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
                 lse[(long long)h * P.total_q + oq] = (mrow + log2f(lrow)) * 0.69314718055994531f;
         }
     }
+}
+
+// ---------------------------------------------------------------- shared union tiles (prefill)
+
+// 8 wavefronts share each 64-token K/V tile through LDS.  A workgroup owns 8 x
+// 32/G consecutive queries (64 for G = 4); wavefront w owns 32 rows (two 16-row
+// MFMA tiles) = 32/G queries x G heads.  The workgroup's tile list is the union
+// of its queries' init tiles, windows and selected blocks (block = tile, g = 64);
+// for each listed tile a 64-bit mask says which of its queries selected it.  The
+// list is walked in lockstep: while tile e is computed from LDS, the loads of
+// tile e + kWgStage are in flight in registers and tile e + 1 is written to the
+// other LDS buffer at the end of the iteration (one barrier per tile).  A
+// wavefront skips the MFMA work of tiles none of its rows attends.
+constexpr int kWgWaves = 8;
+constexpr int kWgQueries = 64;                 // 8 waves x 8 queries (G = 4)
+constexpr int kWgMaxTiles = 2048;              // 64-token tiles per sequence (max_k <= 131072)
+constexpr int kWgStage = 2;                    // tiles in flight in registers
+constexpr int kWgPitch = 272;                  // LDS bytes per staged 256-byte row (bank spread)
+
+struct WgStage {
+    u32x4 c[4];                                // this thread's 4 x 16 B of a 32 KB K/V tile
+};
+
+__device__ __forceinline__ void wg_issue(WgStage &st, const uint16_t *kb, const uint16_t *vb, long long tstride,
+                                         int t0, int n_k, int tid)
+{
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int chunk = tid + 512 * u;       // 2048 chunks: 128 rows (64 K, 64 V) x 16
+        const int row = chunk >> 4, col = chunk & 15;
+        const int t = min(t0 + (row & 63), n_k - 1);
+        const uint16_t *base = row < 64 ? kb : vb;
+        st.c[u] = ld16(base + (long long)t * tstride + 8 * col);
+    }
+}
+
+__device__ __forceinline__ void wg_write(const WgStage &st, unsigned char *buf, int tid)
+{
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int chunk = tid + 512 * u;
+        const int row = chunk >> 4, col = chunk & 15;
+        *reinterpret_cast<u32x4 *>(buf + row * kWgPitch + 16 * col) = st.c[u];
+    }
+}
+
+// Softmax bookkeeping of one 16-row tile for a 32-token chunk.  The running max is
+// kept on the raw logits (the scale is positive), so each logit costs one max, one
+// FMA and one exp2; the output accumulators are rescaled only when some row's max
+// moved (a wavefront-uniform branch).  Returns the bf16 P operand (A layout of
+// the P V product).
+__device__ __forceinline__ bf16x8 chunk_softmax(const f32x4 (&st)[2], uint32_t live, float scale_log2, int g4,
+                                                float &m_run, float &l_part, f32x4 (&acc)[8])
+{
+    float sv[8];
+    float mc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        sv[i] = (live >> i) & 1u ? st[i >> 2][i & 3] : -INFINITY;
+        mc = fmaxf(mc, sv[i]);
+    }
+    mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
+    mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
+    const float m_new = fmaxf(m_run, mc);
+    const float neg_mc = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
+    const float alpha = m_run == m_new ? 1.f : exp2f(fmaf(m_run, scale_log2, neg_mc));
+    float sum = 0.f;
+    bf16x8 aop;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float pe = exp2f(fmaf(sv[i], scale_log2, neg_mc));
+        sum += pe;
+        aop[i] = (__bf16)pe;
+    }
+    l_part = fmaf(l_part, alpha, sum);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+            float a = __shfl(alpha, 4 * g4 + qq, kWave);
+#pragma unroll
+            for (int p = 0; p < 8; p++)
+                acc[p][qq] *= a;
+        }
+    }
+    return aop;
+}
+
+// One 32-token half of a staged tile for the wavefront's two row tiles: K operands
+// from LDS feed both QK products, then V operands are read and each transposed
+// B operand serves both row tiles.
+__device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr, int g4, const bf16x8 (&qop)[2][4],
+                                        const uint32_t (&live)[2], const bool (&act)[2], float scale_log2,
+                                        float (&m_run)[2], float (&l_part)[2], f32x4 (&acc)[2][8])
+{
+    f32x4 st[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            st[a][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        const unsigned char *kr = buf + (32 * h + 16 * s + rr) * kWgPitch + 16 * g4;
+        u32x4 kk[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            kk[ks] = *reinterpret_cast<const u32x4 *>(kr + 64 * ks);
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+            if (act[a])
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++)
+                    st[a][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[ks]),
+                                                                       qop[a][ks], st[a][s], 0, 0, 0);
+    }
+    bf16x8 aop[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+        if (act[a])
+            aop[a] = chunk_softmax(st[a], live[a], scale_log2, g4, m_run[a], l_part[a], acc[a]);
+    u32x4 vv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int off = i < 4 ? 4 * g4 + i : 16 + 4 * g4 + (i - 4);
+        vv[i] = *reinterpret_cast<const u32x4 *>(buf + (64 + 32 * h + off) * kWgPitch + 16 * rr);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; p++) {
+        const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 bw;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; w4++)
+            bw[w4] = __builtin_amdgcn_perm(vv[2 * w4 + 1][p >> 1], vv[2 * w4][p >> 1], sel);
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+            if (act[a])
+                acc[a][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], bop, acc[a][p], 0, 0, 0);
+    }
+}
+
+// The 8 logits of lane group g4 are tokens 4*g4 .. +3 and 16 + 4*g4 .. +3 of the chunk.
+__device__ __forceinline__ uint32_t live8(uint32_t m32, int g4)
+{
+    return ((m32 >> (4 * g4)) & 0xfu) | (((m32 >> (16 + 4 * g4)) & 0xfu) << 4);
+}
+
+__global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *__restrict__ q,
+                                                         const uint16_t *__restrict__ k,
+                                                         const uint16_t *__restrict__ v,
+                                                         const int32_t *__restrict__ idx,
+                                                         const int32_t *__restrict__ n_idx,
+                                                         uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                         int n_qtile)
+{
+    constexpr int D = 128, KS = D / 32;
+    __shared__ unsigned long long sh_qm[kWgMaxTiles];      // per tile: queries that selected it
+    __shared__ int sh_list[kWgMaxTiles];
+    __shared__ unsigned long long sh_lqm[kWgMaxTiles];
+    __shared__ __attribute__((aligned(16))) unsigned char sh_kv[2][128 * kWgPitch];
+    __shared__ int sh_scan[kWgWaves];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rr = lane & 15, g4 = lane >> 4;
+    const long long n_items = (long long)n_qtile * P.batch * P.h_kv;
+    const long long per_xcd = (n_items + 7) / 8;
+    const long long item = (long long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= n_items)
+        return;
+    const int qt = (int)(item % n_qtile);
+    const int c = (int)((item / n_qtile) % P.h_kv);
+    const int b = (int)(item / ((long long)n_qtile * P.h_kv));
+    const Seq s = seq_info(P, b);
+    const int QPW = 32 / P.G;                             // queries per wavefront
+    const int qwg = kWgWaves * QPW;                       // queries per workgroup (<= 64)
+    const int q_lo = qt * qwg;
+    const int nq = max(0, min(qwg, s.n_q - q_lo));
+    const int ntile = (s.n_k + 63) / 64;
+
+    for (int x = tid; x < ntile; x += 512)
+        sh_qm[x] = 0ull;
+    __syncthreads();
+    for (int x = tid; x < nq * P.topk; x += 512) {
+        const int qq = x / P.topk, e = x % P.topk;
+        const long long qi = s.q_off + q_lo + qq;
+        int ns = n_idx[(long long)c * P.rows + qi];
+        ns = ns < 0 ? 0 : (ns > P.topk ? P.topk : ns);
+        if (e < ns) {
+            const int j = idx[((long long)c * P.rows + qi) * P.topk + e];
+            if (j >= 0 && j < ntile)
+                atomicOr(&sh_qm[j], 1ull << qq);
+        }
+    }
+    __syncthreads();
+    // union list: selected blocks, init tiles, window tiles of the workgroup's queries
+    const int p_first = s.q0 + q_lo, p_last = s.q0 + q_lo + nq - 1;
+    const int init_hi = (min(P.n_init, p_last + 1) + 63) / 64;
+    const int win_lo = max(P.n_init, p_first - P.window + 1) / 64, win_hi = p_last / 64;
+    const int per = (ntile + 511) / 512;
+    int cnt = 0;
+    for (int u = 0; u < per; u++) {
+        const int j = tid * per + u;
+        cnt += (j < ntile && (sh_qm[j] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) ? 1 : 0;
+    }
+    int2 sc = block_scan_int_512(cnt, sh_scan);
+    int pos = sc.x;
+    for (int u = 0; u < per; u++) {
+        const int j = tid * per + u;
+        if (j < ntile && (sh_qm[j] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) {
+            sh_list[pos] = j;
+            sh_lqm[pos] = sh_qm[j];
+            pos++;
+        }
+    }
+    const int n_list = sc.y;
+
+    // this wavefront's rows: a = 0, 1 -> rows 16a + rr of its 32
+    const long long tstride = (long long)P.h_kv * D;
+    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
+    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
+    bf16x8 qop[2][KS];
+    int p_row[2], lo_w[2], qbit[2];
+    bool row_ok[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+        const int rq = (16 * a + rr) / P.G;                  // query within the wavefront
+        const int ql = w * QPW + rq;                          // query within the workgroup
+        row_ok[a] = ql < nq;
+        qbit[a] = ql;
+        p_row[a] = row_ok[a] ? s.q0 + q_lo + ql : -1;
+        lo_w[a] = max(P.n_init, p_row[a] - P.window + 1);
+        if (row_ok[a]) {
+            const long long qi = s.q_off + q_lo + ql;
+            const uint16_t *qp = q + (qi * P.h_q + c * P.G + (16 * a + rr) % P.G) * D + 8 * g4;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                qop[a][ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                qop[a][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    // the wavefront's query bits in the 64-bit masks, and its query span for init/window tests
+    const int wq_lo = w * QPW, wq_n = max(0, min(QPW, nq - wq_lo));
+    const unsigned long long wmask = wq_n > 0 ? (((wq_n == 64) ? ~0ull : ((1ull << wq_n) - 1ull)) << wq_lo) : 0ull;
+    const int wp_first = s.q0 + q_lo + wq_lo, wp_last = wp_first + wq_n - 1;
+    const int w_init_hi = wq_n > 0 ? (min(P.n_init, wp_last + 1) + 63) / 64 : 0;
+    const int w_win_lo = max(P.n_init, wp_first - P.window + 1) / 64, w_win_hi = wq_n > 0 ? wp_last / 64 : -1;
+
+    float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int p = 0; p < 8; p++)
+            acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Tile t lives in register slot t % kWgStage.  Every iteration: barrier (LDS
+    // buffer e&1 holds tile e), compute tile e, write tile e+1 from its slot into
+    // the other buffer, then reuse that slot for tile e+1+kWgStage.  Issues and
+    // writes are unconditional (clamped to the last tile) so the load counters the
+    // compiler tracks are the same on every path.
+    WgStage stage[kWgStage];
+    const int last = max(n_list - 1, 0);
+#pragma unroll
+    for (int x = 0; x < kWgStage; x++)
+        wg_issue(stage[x], kb, vb, tstride, sh_list[min(x, last)] * 64, s.n_k, tid);
+    wg_write(stage[0], sh_kv[0], tid);
+    wg_issue(stage[0], kb, vb, tstride, sh_list[min(kWgStage, last)] * 64, s.n_k, tid);
+    const int n_iter = ((n_list + kWgStage - 1) / kWgStage) * kWgStage;
+    for (int e0 = 0; e0 < n_iter; e0 += kWgStage) {
+#pragma unroll
+        for (int x = 0; x < kWgStage; x++) {
+            const int e = e0 + x;
+            __syncthreads();                               // LDS buffer e&1 holds tile e
+            const int tile = sh_list[min(e, last)];
+            const unsigned long long qm = sh_lqm[min(e, last)];
+            const bool need = e < n_list &&
+                              ((qm & wmask) != 0ull || tile < w_init_hi || (tile >= w_win_lo && tile <= w_win_hi));
+            if (need) {
+                const unsigned char *buf = sh_kv[e & 1];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int t0 = tile * 64 + 32 * h;
+                    uint32_t live[2];
+                    bool act[2];
+#pragma unroll
+                    for (int a = 0; a < 2; a++) {
+                        const bool sb = (qm >> qbit[a]) & 1ull;
+                        live[a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
+                        act[a] = __ballot(live[a] != 0u) != 0ull;
+                    }
+                    if (!act[0] && !act[1])
+                        continue;
+                    wg_half(buf, h, rr, g4, qop, live, act, P.scale_log2, m_run, l_part, acc);
+                }
+            }
+            const int xn = (x + 1) % kWgStage;
+            wg_write(stage[xn], sh_kv[(e + 1) & 1], tid);
+            wg_issue(stage[xn], kb, vb, tstride, sh_list[min(e + 1 + kWgStage, last)] * 64, s.n_k, tid);
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+        float l_row = l_part[a] + __shfl_xor(l_part[a], 16, kWave);
+        l_row += __shfl_xor(l_row, 32, kWave);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+            const int row = 4 * g4 + r4;                      // row within the 16-row tile a
+            const float lrow = __shfl(l_row, row, kWave);
+            const float mrow = __shfl(m_run[a], row, kWave);
+            const int ql = w * QPW + (16 * a + row) / P.G;
+            if (ql < nq) {
+                const long long oq = s.q_off + q_lo + ql;
+                const int h = c * P.G + (16 * a + row) % P.G;
+                const float inv = 1.0f / lrow;
+                float o8[8];
+#pragma unroll
+                for (int p = 0; p < 8; p++)
+                    o8[p] = acc[a][p][r4] * inv;
+                store8(out + (oq * P.h_q + h) * D + 8 * rr, o8);
+                if (lse && rr == 0)
+                    lse[(long long)h * P.total_q + oq] = (mrow * P.scale_log2 + log2f(lrow)) * 0.69314718055994531f;
+            }
+        }
+    }
+}
+
+bool wg_fwd_ok(const KP &P, int dtype)
+{
+    return dtype == 1 && !P.shared && P.d == 128 && P.g == 64 && (P.G == 4 || P.G == 8 || P.G == 16) &&
+           P.max_k <= kWgMaxTiles * 64 && P.max_q >= 256 && !getenv("SPARSE_ATTN_NO_WG");
+}
+
+hipError_t launch_fwd_wg(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
+                         const int32_t *n_idx, void *out, float *lse, void *ev0, void *ev1, hipStream_t st)
+{
+    const int qwg = kWgWaves * (32 / P.G);
+    const int n_qtile = (P.max_q + qwg - 1) / qwg;
+    const long long n_items = (long long)n_qtile * P.batch * P.h_kv;
+    const long long grid = ((n_items + 7) / 8) * 8;
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev0, st);
+    attn_wg_kernel<<<dim3((unsigned)grid), dim3(512), 0, st>>>(P, (const uint16_t *)q, (const uint16_t *)k,
+                                                               (const uint16_t *)v, idx, n_idx, (uint16_t *)out,
+                                                               lse, n_qtile);
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev1, st);
+    return hipGetLastError();
 }
 
 bool tile_fwd_ok(const KP &P, int dtype)

@@ -14,6 +14,9 @@ size_t select_workspace_bytes(const KP &P, int plan);
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
                          int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st);
 
+bool wg_fwd_ok(const KP &P, int dtype);
+hipError_t launch_fwd_wg(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
+                         const int32_t *n_idx, void *out, float *lse, void *ev0, void *ev1, hipStream_t st);
 bool tile_fwd_ok(const KP &P, int dtype);
 hipError_t launch_fwd_tile(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
                            const int32_t *n_idx, void *out, float *lse, void *ev0, void *ev1, hipStream_t st);

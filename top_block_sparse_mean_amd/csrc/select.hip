@@ -389,109 +389,149 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
 
 // ---------------------------------------------------------------- score_tile (MFMA fp32)
 
-// Prefill rows (one per query).  grid: (block chunks of 64, row tiles of 64, h_kv * batch).
-// 4 wavefronts in a 2 x 2 arrangement, each a 32 x 32 tile of 2 x 2 MFMA 16x16x4 f32.
-// MFMA 16x16x4 f32 operands: lane l gives A[l%16][l/16] and B[l/16][l%16];
-// the result lane l holds D[4*(l/16)+i][l%16], i = 0..3.
-template <typename T, typename KT, int D>
-__global__ __launch_bounds__(256) void score_tile_kernel(KP P, const T *__restrict__ q,
-                                                         const KT *__restrict__ kbase,
-                                                         uint32_t *__restrict__ ws, long long stride)
+// 4 consecutive candidate-key elements as fp32 (pooled fp32 keys, or raw bf16 / fp32 keys).
+__device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 ld4f(const uint16_t *p)
 {
-    constexpr int TR = 64, TJ = 64, LD = D + 4;
-    __shared__ float qs_sh[TR * LD];
-    __shared__ float kt_sh[TJ * LD];
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Prefill rows (one per query).  grid: (column chunks of kColTiles x 64 candidates,
+// row tiles of 64, h_kv * batch).  4 wavefronts in 2 x 2, each a 32 x 32 block of
+// 2 x 2 MFMA 16x16x4 f32 tiles.  The selector-query operands (the group's heads
+// summed in fp32) are built once per workgroup and stay in registers; each
+// column tile's key operands are loaded straight from memory as float4 per lane
+// (lane l: key row l%16, head-dim elements 16k + 4(l/16) .. +4, which is the
+// MFMA k index l/16 of the four steps s = 0..3) while the previous tile computes.
+// The head dimension is contracted in the order (k, s, l/16); fp32 products and sums.
+constexpr int kColTiles = 16;
+
+template <typename T, typename KT, int D>
+__global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__restrict__ q,
+                                                            const KT *__restrict__ kbase,
+                                                            uint32_t *__restrict__ ws, long long stride)
+{
+    constexpr int KG = D / 16;
     const int b = blockIdx.z % P.batch, c = blockIdx.z / P.batch;
-    Seq s = seq_info(P, b);
-    const int r0 = blockIdx.y * TR;
+    const Seq s = seq_info(P, b);
+    const int r0 = blockIdx.y * 64;
     if (r0 >= s.n_q)
         return;
-    const int r_end = min(r0 + TR, s.n_q);
-    // candidate range of the tile's last row bounds every row of the tile
+    const int r_end = min(r0 + 64, s.n_q);
     int jlo_last, jhi_last;
     cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
     jhi_last = min(jhi_last, (int)stride);
-    const int j0 = jlo_last + blockIdx.x * TJ;
-    if (j0 >= jhi_last)
+    const int jc0 = jlo_last + blockIdx.x * kColTiles * 64;
+    if (jc0 >= jhi_last)
         return;
-    const int tid = threadIdx.x;
-    // stage Qs: 64 rows x D, 8 elements per item
-    for (int it = tid; it < TR * (D / 8); it += 256) {
-        int rr = it / (D / 8), e0 = (it % (D / 8)) * 8;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r0 + rr < r_end) {
-            long long i = s.q_off + r0 + rr;
-            for (int h = 0; h < P.G; h++) {
-                float x[8];
-                load8(q + (i * P.h_q + (long long)c * P.G + h) * D + e0, x);
+    const int jc1 = min(jc0 + kColTiles * 64, jhi_last);
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int li = lane % 16, lk = lane / 16;
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+
+    // selector operands: rows r0 + wr + 16a + li, elements 16k + 4lk .. +4
+    float4 qa[2][KG];
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    acc[e] += x[e];
+    for (int a = 0; a < 2; a++) {
+        const int rl = r0 + wr + 16 * a + li;
+#pragma unroll
+        for (int k = 0; k < KG; k++)
+            qa[a][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rl < r_end) {
+            const long long i = s.q_off + rl;
+            for (int h = 0; h < P.G; h++) {
+                const T *qp = q + (i * P.h_q + (long long)c * P.G + h) * D + 4 * lk;
+#pragma unroll
+                for (int k = 0; k < KG; k++) {
+                    float4 x = ld4f(qp + 16 * k);
+                    qa[a][k].x += x.x;
+                    qa[a][k].y += x.y;
+                    qa[a][k].z += x.z;
+                    qa[a][k].w += x.w;
+                }
             }
         }
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            qs_sh[rr * LD + e0 + e] = acc[e];
     }
-    // stage keys: 64 candidate rows x D
-    for (int it = tid; it < TJ * (D / 8); it += 256) {
-        int jj = it / (D / 8), e0 = (it % (D / 8)) * 8;
-        int j = j0 + jj;
-        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (j < jhi_last) {
-            if (P.g == 1)
-                load8(kbase + ((s.k_off + j) * P.h_kv + c) * D + e0, x);
-            else
-                load8(kbase + (((long long)c * P.batch + b) * P.nb_max + j) * D + e0, x);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            kt_sh[jj * LD + e0 + e] = x[e];
-    }
-    __syncthreads();
-    const int lane = lane_id(), w = tid / kWave;
-    const int wr = (w >> 1) * 32, wj = (w & 1) * 32;
-    floatx4 acc[2][2];
+    auto key_ptr = [&](int j) -> const KT * {
+        j = min(j, jhi_last - 1);
+        if (P.g == 1)
+            return kbase + ((s.k_off + j) * P.h_kv + c) * D;
+        return kbase + (((long long)c * P.batch + b) * P.nb_max + j) * D;
+    };
+    // candidate upper bound of each output row this lane writes (rows are fixed per workgroup);
+    // the lower bound n_init / g is the same for every row that has candidates
+    int jh_row[2][4];
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int bb = 0; bb < 2; bb++)
-            acc[a][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int li = lane % 16, lk = lane / 16;
-#pragma unroll 8
-    for (int e = 0; e < D; e += 4) {
-        float av[2], bv[2];
+        for (int i = 0; i < 4; i++) {
+            const int rl = r0 + wr + 16 * a + 4 * lk + i;
+            int jl = 0, jh = 0;
+            if (rl < r_end)
+                cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + rl, jl, jh);
+            jh_row[a][i] = jh > jl ? min(jh, (int)stride) : 0;
+        }
+    const int j_first = P.n_init / P.g;
+    float4 ka[2][KG], kb[2][KG];
+    auto load_keys = [&](float4 (&kk)[2][KG], int jt) {
 #pragma unroll
-        for (int a = 0; a < 2; a++)
-            av[a] = qs_sh[(wr + a * 16 + li) * LD + e + lk];
+        for (int bb = 0; bb < 2; bb++) {
+            const KT *kp = key_ptr(jt + wc + 16 * bb + li) + 4 * lk;
 #pragma unroll
-        for (int bb = 0; bb < 2; bb++)
-            bv[bb] = kt_sh[(wj + bb * 16 + li) * LD + e + lk];
+            for (int k = 0; k < KG; k++)
+                kk[bb][k] = ld4f(kp + 16 * k);
+        }
+    };
+    auto tile = [&](const float4 (&kk)[2][KG], int jt) {
+        floatx4 acc[2][2];
 #pragma unroll
         for (int a = 0; a < 2; a++)
 #pragma unroll
             for (int bb = 0; bb < 2; bb++)
-                acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[bb], acc[a][bb], 0, 0, 0);
-    }
-    // epilogue: row = r0 + wr + a*16 + 4*lk + i, block = j0 + wj + bb*16 + li
+                acc[a][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a < 2; a++) {
+        for (int k = 0; k < KG; k++) {
+            const float av[2][4] = {{qa[0][k].x, qa[0][k].y, qa[0][k].z, qa[0][k].w},
+                                    {qa[1][k].x, qa[1][k].y, qa[1][k].z, qa[1][k].w}};
+            const float bv[2][4] = {{kk[0][k].x, kk[0][k].y, kk[0][k].z, kk[0][k].w},
+                                    {kk[1][k].x, kk[1][k].y, kk[1][k].z, kk[1][k].w}};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int rl = r0 + wr + a * 16 + 4 * lk + i;
-            if (rl >= r_end)
-                continue;
-            int jl, jh;
-            cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + rl, jl, jh);
-            jh = min(jh, (int)stride);
-            uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride;
+            for (int st = 0; st < 4; st++)
 #pragma unroll
-            for (int bb = 0; bb < 2; bb++) {
-                int j = j0 + wj + bb * 16 + li;
-                if (j >= jl && j < jh)
-                    dst[j] = order_key(acc[a][bb][i]);
+                for (int a = 0; a < 2; a++)
+#pragma unroll
+                    for (int bb = 0; bb < 2; bb++)
+                        acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a][st], bv[bb][st], acc[a][bb], 0, 0, 0);
+        }
+        // row = r0 + wr + 16a + 4lk + i, candidate = jt + wc + 16bb + li
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int rl = r0 + wr + 16 * a + 4 * lk + i;
+                uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride;
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) {
+                    const int j = jt + wc + 16 * bb + li;
+                    if (j >= j_first && j < jh_row[a][i])
+                        dst[j] = order_key(acc[a][bb][i]);
+                }
             }
         }
+    };
+    load_keys(ka, jc0);
+    for (int jt = jc0; jt < jc1; jt += 128) {
+        const int jn = jt + 64;
+        if (jn < jc1)
+            load_keys(kb, jn);
+        tile(ka, jt);
+        if (jn >= jc1)
+            break;
+        if (jn + 64 < jc1)
+            load_keys(ka, jn + 64);
+        tile(kb, jn);
     }
 }
 
@@ -530,22 +570,57 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
         out[s] = -1;
 }
 
-// One 1024-thread workgroup per row with up to 1024 * KPT candidates held in
-// registers (key i in thread i % 1024, slot i / 1024).  tau is found by a
-// binary search on its bits; counts are wave ballots summed through LDS (one
-// barrier per bit).  The output is written in index order from per-(slot, wave)
-// counts, so it needs only three more barriers.  grid: (rows, h_kv).
-template <int KPT>
-__global__ __launch_bounds__(1024) void topk_regs_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
-                                                         int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+// Exclusive block-wide scan of one int per thread (NT threads); returns (exclusive, total).
+template <int NT>
+__device__ __forceinline__ int2 block_scan_int(int v, int *sh)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int t = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += t;
+    }
+    if (lane == kWave - 1)
+        sh[w] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) {
+        int c = sh[i];
+        off += i < w ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    return make_int2(off + incl - v, tot);
+}
+
+constexpr int kCompactMaxN = 262144;     // candidates per row (bitmap of 8192 words in LDS)
+constexpr int kCompactCap = 4096;        // keys kept for the exact last step
+
+// One 1024-thread workgroup per row, 2048 < candidates <= 262144.
+//  1. histograms of 12, 12 and 8 key bits (most significant first), each restricted to
+//     the prefix chosen so far, until the bin holding the k-th largest key has at most
+//     kCompactCap keys (usually after the first histogram: the selected tail is thin);
+//  2. one pass marks every key above that bin in an LDS bitmap and copies the bin's
+//     keys and indices to LDS;
+//  3. the remaining picks are made exactly inside LDS (binary search on the key, then
+//     on the index for equal keys: ties go to the lower index);
+//  4. the bitmap is compacted into ascending indices.
+// The keys are read from the workspace two to four times in all.
+__global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
+                                                            int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
 {
     constexpr int NT = 1024, NW = NT / kWave;
-    __shared__ int sh_cnt[2][NW];
-    __shared__ int sh_gt[KPT][NW], sh_eq[KPT][NW];
+    __shared__ int hist[4096];
+    __shared__ uint32_t bitmap[kCompactMaxN / 32];
+    __shared__ uint32_t cand_key[kCompactCap];
+    __shared__ int cand_idx[kCompactCap];
+    __shared__ int sh_scan[NW];
+    __shared__ int sh_digit, sh_above, sh_ncand;
     const long long row = blockIdx.x;
-    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-    const int j_first = P.n_init / P.g;
-    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
+    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id();
     RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     if (tid == 0)
@@ -554,89 +629,155 @@ __global__ __launch_bounds__(1024) void topk_regs_kernel(KP P, const uint32_t *_
         write_all(P, out, r, tid, NT);
         return;
     }
-    const int n = min(r.n_cand, NT * KPT);
+    const int n = min(r.n_cand, kCompactMaxN);
     const int need = min(r.need, n);
-    const int slots = (n + NT - 1) / NT;            // slots holding candidates (uniform)
-    uint32_t kr[KPT];
-#pragma unroll
-    for (int m = 0; m < KPT; m++) {
-        long long j = j_first + (long long)m * NT + tid;
-        kr[m] = (m < slots && j < stride) ? src[j] : 0u;
+    if (need == 0) {
+        for (int s2 = tid; s2 < P.topk; s2 += NT)
+            out[s2] = -1;
+        return;
     }
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int m = 0; m < KPT; m++)
-            if (m < slots)
-                cnt += __popcll(__ballot(m * NT + tid < n && kr[m] >= cand));
-        if (lane == 0)
-            sh_cnt[bit & 1][w] = cnt;
+    const uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + r.j_lo;
+    const int nword = (n + 31) / 32;
+    for (int x = tid; x < nword; x += NT)
+        bitmap[x] = 0u;
+    uint32_t prefix = 0, pmask = 0;
+    int rem = need, cnt_bin = 0;
+    const int shifts[3] = {20, 8, 0};
+    const int widths[3] = {12, 12, 8};
+    for (int level = 0; level < 3; level++) {
+        const int shift = shifts[level], nb = 1 << widths[level];
+        for (int x = tid; x < nb; x += NT)
+            hist[x] = 0;
         __syncthreads();
-        int tot = 0;
-#pragma unroll
-        for (int x = 0; x < NW; x++)
-            tot += sh_cnt[bit & 1][x];
-        if (tot >= need)
-            tau = cand;
-    }
-    // per (slot, wave) counts of keys above tau and equal to tau
-    int g_tot = 0;
-#pragma unroll
-    for (int m = 0; m < KPT; m++) {
-        if (m >= slots)
-            break;
-        bool valid = m * NT + tid < n;
-        int g = __popcll(__ballot(valid && kr[m] > tau));
-        int e = __popcll(__ballot(valid && kr[m] == tau));
-        g_tot += g;
-        if (lane == 0) {
-            sh_gt[m][w] = g;
-            sh_eq[m][w] = e;
+        for (int i = tid; i < n; i += NT) {
+            uint32_t k = keys[i];
+            if ((k & pmask) == prefix)
+                atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
         }
+        __syncthreads();
+        // digit holding the rem-th largest key: scan the bins from the top
+        const int per = nb / NT > 0 ? nb / NT : 1;           // bins per thread (4 or 1)
+        int loc = 0;
+        const int b0 = nb - 1 - tid * per;                   // this thread's bins: b0, b0-1, ...
+        for (int q = 0; q < per; q++)
+            if (tid * per + q < nb)
+                loc += hist[b0 - q];
+        int2 sc = block_scan_int<NT>(tid * per < nb ? loc : 0, sh_scan);
+        if (tid * per < nb && sc.x < rem && sc.x + loc >= rem) {
+            int run = sc.x;
+            for (int q = 0; q < per; q++) {
+                int h = hist[b0 - q];
+                if (run + h >= rem) {
+                    sh_digit = b0 - q;
+                    sh_above = run;
+                    break;
+                }
+                run += h;
+            }
+        }
+        __syncthreads();
+        const int d = sh_digit;
+        prefix |= ((uint32_t)d) << shift;
+        pmask |= ((uint32_t)(nb - 1)) << shift;
+        rem -= sh_above;
+        cnt_bin = hist[d];
+        __syncthreads();
+        if (cnt_bin <= kCompactCap)
+            break;
     }
-    __syncthreads();                                   // every wave has read sh_cnt too
-    if (lane == 0)
-        sh_cnt[0][w] = g_tot;
+    // mark keys above the bin, gather the bin
+    if (tid == 0)
+        sh_ncand = 0;
     __syncthreads();
-    int n_gt = 0;
-#pragma unroll
-    for (int x = 0; x < NW; x++)
-        n_gt += sh_cnt[0][x];
-    const int need_eq = need - n_gt;
-    // output position of a selected key = selected keys before it in index order
-    // (index = slot * 1024 + wave * 64 + lane)
-    int eq_before = 0, sel_before = 0;
-#pragma unroll
-    for (int m = 0; m < KPT; m++) {
-        if (m >= slots)
-            break;
-        int eq_m_before_w = 0, gt_m_before_w = 0, eq_m = 0, gt_m = 0;
-#pragma unroll
-        for (int x = 0; x < NW; x++) {
-            int e = sh_eq[m][x], g = sh_gt[m][x];
-            eq_m_before_w += x < w ? e : 0;
-            gt_m_before_w += x < w ? g : 0;
-            eq_m += e;
-            gt_m += g;
+    const uint32_t top_of_bin = prefix | ~pmask;
+    const bool gather = cnt_bin <= kCompactCap;
+    for (int i = tid; i < n; i += NT) {
+        uint32_t k = keys[i];
+        if (k > top_of_bin) {
+            atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+        } else if (gather && (k & pmask) == prefix) {
+            int slot = atomicAdd(&sh_ncand, 1);
+            cand_key[slot] = k;
+            cand_idx[slot] = i;
         }
-        const bool valid = m * NT + tid < n;
-        const bool is_gt = valid && kr[m] > tau, is_eq = valid && kr[m] == tau;
-        const unsigned long long meq = __ballot(is_eq);
-        const int eq_rank = eq_before + eq_m_before_w + lanes_below(meq);
-        const bool s_eq = is_eq && eq_rank < need_eq;
-        const unsigned long long msel = __ballot(is_gt || s_eq);
-        // selected before this lane = gt before + eq selected before
-        const int eq_sel_before_wave = min(max(need_eq - eq_before, 0), eq_m_before_w);
-        const int pos = sel_before + gt_m_before_w + eq_sel_before_wave + lanes_below(msel);
-        if (is_gt || s_eq)
-            out[pos] = r.j_lo + m * NT + tid;
-        sel_before += gt_m + min(max(need_eq - eq_before, 0), eq_m);
-        eq_before += eq_m;
+    }
+    __syncthreads();
+    if (gather) {
+        // exact pick of rem among the gathered keys: tau = rem-th largest key
+        const int nc = sh_ncand;
+        uint32_t tau = prefix;
+        for (int bit = 31; bit >= 0; --bit) {
+            if (pmask & (1u << bit))
+                continue;                                    // fixed by the prefix
+            const uint32_t cand = tau | (1u << bit);
+            int cnt = 0;
+            for (int x = tid; x < nc; x += NT)
+                cnt += cand_key[x] >= cand ? 1 : 0;
+            cnt = block_scan_int<NT>(cnt, sh_scan).y;
+            if (cnt >= rem)
+                tau = cand;
+        }
+        int gt = 0;
+        for (int x = tid; x < nc; x += NT)
+            gt += cand_key[x] > tau ? 1 : 0;
+        const int n_gt = block_scan_int<NT>(gt, sh_scan).y;
+        const int need_eq = rem - n_gt;
+        // among keys == tau: the need_eq lowest indices (binary search on the index)
+        int ilim = 0;                                        // select eq keys with index < ilim... found below
+        {
+            int lo = 0;                                      // largest bound with count(idx < bound) <= need_eq
+            for (int bit = 18; bit >= 0; --bit) {
+                const int candb = lo | (1 << bit);
+                int cnt = 0;
+                for (int x = tid; x < nc; x += NT)
+                    cnt += (cand_key[x] == tau && cand_idx[x] < candb) ? 1 : 0;
+                cnt = block_scan_int<NT>(cnt, sh_scan).y;
+                if (cnt <= need_eq)
+                    lo = candb;
+            }
+            ilim = lo;
+        }
+        for (int x = tid; x < nc; x += NT) {
+            const uint32_t k = cand_key[x];
+            const int i = cand_idx[x];
+            if (k > tau || (k == tau && i < ilim))
+                atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+        }
+    } else {
+        // more than kCompactCap keys share the full 32-bit key: the lowest indices win
+        int seen = 0;
+        for (int base = 0; base < n; base += NT) {
+            const int i = base + tid;
+            const bool eq = i < n && keys[i] == prefix;
+            int2 e = block_scan_int<NT>(eq ? 1 : 0, sh_scan);
+            if (eq && seen + e.x < rem)
+                atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+            seen += e.y;
+        }
+    }
+    __syncthreads();
+    // ascending output from the bitmap
+    const int wpt = (nword + NT - 1) / NT;                    // words per thread
+    int cnt = 0;
+    for (int q = 0; q < wpt; q++) {
+        int wd = tid * wpt + q;
+        cnt += wd < nword ? __popc(bitmap[wd]) : 0;
+    }
+    int pos = block_scan_int<NT>(cnt, sh_scan).x;
+    for (int q = 0; q < wpt; q++) {
+        int wd = tid * wpt + q;
+        uint32_t bits = wd < nword ? bitmap[wd] : 0u;
+        while (bits) {
+            int bpos = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (pos < P.topk)
+                out[pos] = r.j_lo + wd * 32 + bpos;
+            pos++;
+        }
     }
     for (int s2 = need + tid; s2 < P.topk; s2 += NT)
         out[s2] = -1;
+    (void)lane;
 }
 
 // One workgroup per row.  grid: (rows, h_kv).
@@ -651,8 +792,9 @@ __global__ __launch_bounds__(NT) void topk_block_kernel(KP P, const uint32_t *__
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     if (threadIdx.x == 0)
         n_idx[(long long)c * P.rows + row] = r.need;
-    if (r.need == r.n_cand) {
-        write_all(P, out, r, threadIdx.x, NT);
+    if (r.need == r.n_cand || r.need == 0) {
+        write_all(P, out, r.need == 0 ? RowGeo{r.b, r.n_k, r.p_sel, r.q_first, r.q_last, r.j_lo, r.j_lo, 0, 0, r.k_off}
+                                      : r, threadIdx.x, NT);
         return;
     }
     block_topk<NT>(ws + ((long long)c * P.rows + row) * stride + r.j_lo, r.n_cand, r.need, r.j_lo, out);
@@ -735,7 +877,8 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             score_rows_kernel<T, float, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride,
                                                                                   n_chunk);
     } else {
-        dim3 grid((unsigned)((stride + 63) / 64), (unsigned)((P.max_q + 63) / 64), (unsigned)(P.h_kv * P.batch));
+        dim3 grid((unsigned)((stride + kColTiles * 64 - 1) / (kColTiles * 64)), (unsigned)((P.max_q + 63) / 64),
+                  (unsigned)(P.h_kv * P.batch));
         if (P.g == 1)
             score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride);
         else
@@ -753,12 +896,9 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         topk_wave_kernel<16><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
     else if (stride <= kWaveTopkMax)
         topk_wave_kernel<32><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
-    else if (stride <= 8192)
-        topk_regs_kernel<8><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
+    else if (stride <= kCompactMaxN && !getenv("SPARSE_ATTN_TOPK_RADIX"))
+        topk_compact_kernel<<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
                                                                                            n_idx);
-    else if (stride <= 32768)
-        topk_regs_kernel<32><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
-                                                                                            n_idx);
     else
         topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
             P, wsk, stride, idx, n_idx);

@@ -28,6 +28,14 @@ from workloads import DTYPE_BF16, generate
 REL_GAP = 1e-4
 F32_ABS = 1e-5
 BF16_REL = 1e-2
+# Log-sum-exp: fp32 arithmetic keeps it within 1e-4.  The bf16 path rounds each
+# softmax weight to bf16 (relative error <= 2^-8) before the P V product and may
+# normalise by the sum of the rounded weights, so |d lse| <= log(1 + 2^-8) < 4e-3.
+LSE_ABS = {"f32": 1e-4, "bf16": 4e-3}
+
+
+def lse_tol(w):
+    return LSE_ABS["bf16" if w.dtype == DTYPE_BF16 else "f32"]
 
 
 def params_for(w, device="cuda"):
@@ -139,7 +147,7 @@ def full_check(w, x_host, xg=None):
     att = oracle.attend(w, x_host["q"], x_host["k"], x_host["v"], gp["idx"], gp["n_idx"])
     check_output(w, gp["out"].reshape(-1, w.head_dim), att["out"])
     lse_g = gp["lse"].t().reshape(-1).double().numpy()          # [h_q, total_q] -> (i, h) order
-    assert np.abs(lse_g - att["lse"]).max() < 1e-4
+    assert np.abs(lse_g - att["lse"]).max() < lse_tol(w)
     # GPU attention on the oracle's own table
     sel = oracle.select(w, x_host["q"], kc, x_host["k"])
     idx_o, n_o = oracle.table(w, sel)

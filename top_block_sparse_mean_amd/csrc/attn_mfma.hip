@@ -28,6 +28,8 @@ namespace sa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D>
 struct ChunkRegs {
@@ -552,54 +554,66 @@ __device__ __forceinline__ void wg_write(const WgStage &st, unsigned char *buf, 
     }
 }
 
-// Softmax bookkeeping of one 16-row tile for a 32-token chunk.  The running max is
-// kept on the raw logits (the scale is positive), so each logit costs one max, one
-// FMA and one exp2; the output accumulators are rescaled only when some row's max
-// moved (a wavefront-uniform branch).  Returns the bf16 P operand (A layout of
-// the P V product).
-__device__ __forceinline__ bf16x8 chunk_softmax(const f32x4 (&st)[2], uint32_t live, float scale_log2, int g4,
-                                                float &m_run, float &l_part, f32x4 (&acc)[8])
+// Softmax bookkeeping of one 16-row tile for a 32-token chunk (this lane: row rr,
+// 8 logits).  The reference max m_run is kept on raw logits (the scale is
+// positive) and moves lazily: only when a chunk's max exceeds it by more than
+// `lazy` (2^8 after scaling), so unnormalised weights stay below 256 and the
+// output accumulators are rescaled rarely (a wavefront-uniform branch).  Any
+// reference gives the same normalised result.  A lane whose 8 logits are all
+// masked gets scale 0 and offset -inf, so its weights are exp2(-inf) = 0 without
+// a select per logit; per-logit masks (a -1e30 sentinel, which underflows to 0)
+// are applied only when some lane of the wavefront has a partly live chunk
+// (causal edge, window or sink boundary).
+// exp2 is the hardware instruction (results below 2^-126 flush to zero, which
+// the sum cannot see next to the reference term).  Row sums come from the P V
+// product itself (a ones column tile), so the accumulators carry them and their
+// rescaling.  Returns the bf16 P operand (A layout of the P V product).
+__device__ __forceinline__ bf16x8 chunk_softmax(f32x4 (&st)[2], uint32_t live, bool partial, float scale_log2,
+                                                float lazy, int g4, float &m_run, f32x4 (&acc)[9])
 {
-    float sv[8];
-    float mc = -INFINITY;
+    if (partial) {                       // finite sentinel: a dead lane multiplies it by scale 0
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        sv[i] = (live >> i) & 1u ? st[i >> 2][i & 3] : -INFINITY;
-        mc = fmaxf(mc, sv[i]);
+        for (int i = 0; i < 8; i++)
+            st[i >> 2][i & 3] = (live >> i) & 1u ? st[i >> 2][i & 3] : -1e30f;
     }
+    float mc = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                     fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+    const bool row_live = live != 0u;
+    mc = row_live ? mc : -INFINITY;
     mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
     mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
-    const float m_new = fmaxf(m_run, mc);
-    const float neg_mc = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
-    const float alpha = m_run == m_new ? 1.f : exp2f(fmaf(m_run, scale_log2, neg_mc));
-    float sum = 0.f;
+    const bool bump = mc > m_run + lazy;
+    const float m_new = bump ? mc : m_run;
+    const float neg = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
+    const float s_eff = row_live ? scale_log2 : 0.f;
+    const float n_eff = row_live ? neg : -INFINITY;
     bf16x8 aop;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float pe = exp2f(fmaf(sv[i], scale_log2, neg_mc));
-        sum += pe;
-        aop[i] = (__bf16)pe;
-    }
-    l_part = fmaf(l_part, alpha, sum);
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
+    for (int i = 0; i < 8; i++)
+        aop[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[i >> 2][i & 3], s_eff, n_eff));
+    if (__ballot(bump)) {
+        const float alpha = bump ? __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, neg)) : 1.f;
 #pragma unroll
         for (int qq = 0; qq < 4; qq++) {
             float a = __shfl(alpha, 4 * g4 + qq, kWave);
 #pragma unroll
-            for (int p = 0; p < 8; p++)
+            for (int p = 0; p < 9; p++)
                 acc[p][qq] *= a;
         }
     }
+    m_run = m_new;
     return aop;
 }
 
-// One 32-token half of a staged tile for the wavefront's two row tiles: K operands
-// from LDS feed both QK products, then V operands are read and each transposed
-// B operand serves both row tiles.
+// One 32-token half of a staged tile for the wavefront's row tiles selected by
+// ACT (bit a: row tile a has a live logit): K operands from LDS feed the QK
+// products, then V operands are read and each transposed B operand serves the
+// active row tiles.  ACT is a template argument so every MFMA sequence is
+// straight-line code.
+template <int ACT>
 __device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr, int g4, const bf16x8 (&qop)[2][4],
-                                        const uint32_t (&live)[2], const bool (&act)[2], float scale_log2,
-                                        float (&m_run)[2], float (&l_part)[2], f32x4 (&acc)[2][8])
+                                        const uint32_t (&live)[2], bool partial, float scale_log2, float lazy,
+                                        float (&m_run)[2], f32x4 (&acc)[2][9])
 {
     f32x4 st[2][2];
 #pragma unroll
@@ -616,7 +630,7 @@ __device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr,
             kk[ks] = *reinterpret_cast<const u32x4 *>(kr + 64 * ks);
 #pragma unroll
         for (int a = 0; a < 2; a++)
-            if (act[a])
+            if (ACT >> a & 1)
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++)
                     st[a][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[ks]),
@@ -625,28 +639,31 @@ __device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr,
     bf16x8 aop[2];
 #pragma unroll
     for (int a = 0; a < 2; a++)
-        if (act[a])
-            aop[a] = chunk_softmax(st[a], live[a], scale_log2, g4, m_run[a], l_part[a], acc[a]);
-    u32x4 vv[8];
+        if (ACT >> a & 1)
+            aop[a] = chunk_softmax(st[a], live[a], partial, scale_log2, lazy, g4, m_run[a], acc[a]);
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int off = i < 4 ? 4 * g4 + i : 16 + 4 * g4 + (i - 4);
-        vv[i] = *reinterpret_cast<const u32x4 *>(buf + (64 + 32 * h + off) * kWgPitch + 16 * rr);
-    }
+    for (int a = 0; a < 2; a++)
+        if (ACT >> a & 1)
+            acc[a][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], ones, acc[a][8], 0, 0, 0);
+    // V operand of column tile p (d = 16 p + n) by transposing LDS reads: within a
+    // 16-lane group, lane j receives element j % 4 of the 8-byte chunks addressed by
+    // lanes 4 e + j / 4 (e = 0..3).  Lane (rr, g4) therefore addresses token
+    // 4 g4 + rr / 4 (first read) or 16 + 4 g4 + rr / 4 (second read) at d = 16 p +
+    // 4 (rr % 4), which yields the lane's 8 tokens in the order of its logits.
+    const unsigned char *vr = buf + (64 + 32 * h + 4 * g4 + (rr >> 2)) * kWgPitch + 8 * (rr & 3);
 #pragma unroll
     for (int p = 0; p < 8; p++) {
-        const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 bw;
-#pragma unroll
-        for (int w4 = 0; w4 < 4; w4++)
-            bw[w4] = __builtin_amdgcn_perm(vv[2 * w4 + 1][p >> 1], vv[2 * w4][p >> 1], sel);
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vr + 32 * p));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vr + 16 * kWgPitch + 32 * p));
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int a = 0; a < 2; a++)
-            if (act[a])
+            if (ACT >> a & 1)
                 acc[a][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], bop, acc[a][p], 0, 0, 0);
     }
 }
+
 
 // The 8 logits of lane group g4 are tokens 4*g4 .. +3 and 16 + 4*g4 .. +3 of the chunk.
 __device__ __forceinline__ uint32_t live8(uint32_t m32, int g4)
@@ -756,12 +773,13 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     const int w_init_hi = wq_n > 0 ? (min(P.n_init, wp_last + 1) + 63) / 64 : 0;
     const int w_win_lo = max(P.n_init, wp_first - P.window + 1) / 64, w_win_hi = wq_n > 0 ? wp_last / 64 : -1;
 
-    float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
-    f32x4 acc[2][8];
+    float m_run[2] = {-INFINITY, -INFINITY};
+    const float lazy = 8.f / P.scale_log2;
+    f32x4 acc[2][9];                                      // [8]: row sums (ones column tile)
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int p = 0; p < 8; p++)
+        for (int p = 0; p < 9; p++)
             acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Tile t lives in register slot t % kWgStage.  Every iteration: barrier (LDS
@@ -792,16 +810,18 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
                 for (int h = 0; h < 2; h++) {
                     const int t0 = tile * 64 + 32 * h;
                     uint32_t live[2];
-                    bool act[2];
+                    int act = 0;
+                    bool part = false;
 #pragma unroll
                     for (int a = 0; a < 2; a++) {
                         const bool sb = (qm >> qbit[a]) & 1ull;
                         live[a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
-                        act[a] = __ballot(live[a] != 0u) != 0ull;
+                        act |= __ballot(live[a] != 0u) != 0ull ? 1 << a : 0;
+                        part = part || (live[a] != 0u && live[a] != 0xffu);
                     }
-                    if (!act[0] && !act[1])
-                        continue;
-                    wg_half(buf, h, rr, g4, qop, live, act, P.scale_log2, m_run, l_part, acc);
+                    const bool partial = __ballot(part) != 0ull;
+                    if (act != 0)
+                        wg_half<3>(buf, h, rr, g4, qop, live, partial, P.scale_log2, lazy, m_run, acc);
                 }
             }
             const int xn = (x + 1) % kWgStage;
@@ -809,28 +829,43 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
             wg_issue(stage[xn], kb, vb, tstride, sh_list[min(e + 1 + kWgStage, last)] * 64, s.n_k, tid);
         }
     }
+    // Epilogue: lane (rr, g4) holds d = 16 p + rr of rows 4 g4 + r4; normalised bf16
+    // rows are transposed through this wavefront's 32 x 272-byte slice of the (now
+    // idle) staging buffers and stored as 16-byte row pieces.
+    __syncthreads();
+    unsigned char *ob = &sh_kv[0][0] + w * 32 * kWgPitch;
 #pragma unroll
     for (int a = 0; a < 2; a++) {
-        float l_row = l_part[a] + __shfl_xor(l_part[a], 16, kWave);
-        l_row += __shfl_xor(l_row, 32, kWave);
 #pragma unroll
         for (int r4 = 0; r4 < 4; r4++) {
             const int row = 4 * g4 + r4;                      // row within the 16-row tile a
-            const float lrow = __shfl(l_row, row, kWave);
+            const float lrow = acc[a][8][r4];                 // sum of the bf16 weights of the row
+            const float inv = 1.0f / lrow;
+            uint16_t *orow = reinterpret_cast<uint16_t *>(ob + (16 * a + row) * kWgPitch);
+#pragma unroll
+            for (int p = 0; p < 8; p++)
+                orow[16 * p + rr] = f32_to_bf16(acc[a][p][r4] * inv);
             const float mrow = __shfl(m_run[a], row, kWave);
             const int ql = w * QPW + (16 * a + row) / P.G;
-            if (ql < nq) {
+            if (lse && rr == 0 && ql < nq) {
                 const long long oq = s.q_off + q_lo + ql;
                 const int h = c * P.G + (16 * a + row) % P.G;
-                const float inv = 1.0f / lrow;
-                float o8[8];
-#pragma unroll
-                for (int p = 0; p < 8; p++)
-                    o8[p] = acc[a][p][r4] * inv;
-                store8(out + (oq * P.h_q + h) * D + 8 * rr, o8);
-                if (lse && rr == 0)
-                    lse[(long long)h * P.total_q + oq] = (mrow * P.scale_log2 + log2f(lrow)) * 0.69314718055994531f;
+                lse[(long long)h * P.total_q + oq] = (mrow * P.scale_log2 + log2f(lrow)) * 0.69314718055994531f;
             }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): this wavefront's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        const int u = lane + 64 * t;                       // 512 pieces: 32 rows x 16
+        const int row = u >> 4, piece = u & 15;
+        const int ql = w * QPW + row / P.G;
+        if (ql < nq) {
+            const long long oq = s.q_off + q_lo + ql;
+            const int h = c * P.G + row % P.G;
+            *reinterpret_cast<u32x4 *>(out + (oq * P.h_q + h) * D + 8 * piece) =
+                *reinterpret_cast<const u32x4 *>(ob + row * kWgPitch + 16 * piece);
         }
     }
 }

@@ -554,68 +554,11 @@ __device__ __forceinline__ void wg_write(const WgStage &st, unsigned char *buf, 
     }
 }
 
-// Softmax bookkeeping of one 16-row tile for a 32-token chunk (this lane: row rr,
-// 8 logits).  The reference max m_run is kept on raw logits (the scale is
-// positive) and moves lazily: only when a chunk's max exceeds it by more than
-// `lazy` (2^8 after scaling), so unnormalised weights stay below 256 and the
-// output accumulators are rescaled rarely (a wavefront-uniform branch).  Any
-// reference gives the same normalised result.  A lane whose 8 logits are all
-// masked gets scale 0 and offset -inf, so its weights are exp2(-inf) = 0 without
-// a select per logit; per-logit masks (a -1e30 sentinel, which underflows to 0)
-// are applied only when some lane of the wavefront has a partly live chunk
-// (causal edge, window or sink boundary).
-// exp2 is the hardware instruction (results below 2^-126 flush to zero, which
-// the sum cannot see next to the reference term).  Row sums come from the P V
-// product itself (a ones column tile), so the accumulators carry them and their
-// rescaling.  Returns the bf16 P operand (A layout of the P V product).
-__device__ __forceinline__ bf16x8 chunk_softmax(f32x4 (&st)[2], uint32_t live, bool partial, float scale_log2,
-                                                float lazy, int g4, float &m_run, f32x4 (&acc)[9])
+// S^T = K Q^T of one 32-token half of a staged tile for the wavefront's two row
+// tiles (K operands read from LDS once, used by both).
+__device__ __forceinline__ void wg_qk(const unsigned char *buf, int h, int rr, int g4, const bf16x8 (&qop)[2][4],
+                                      f32x4 (&st)[2][2])
 {
-    if (partial) {                       // finite sentinel: a dead lane multiplies it by scale 0
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            st[i >> 2][i & 3] = (live >> i) & 1u ? st[i >> 2][i & 3] : -1e30f;
-    }
-    float mc = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
-                     fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
-    const bool row_live = live != 0u;
-    mc = row_live ? mc : -INFINITY;
-    mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
-    mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
-    const bool bump = mc > m_run + lazy;
-    const float m_new = bump ? mc : m_run;
-    const float neg = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
-    const float s_eff = row_live ? scale_log2 : 0.f;
-    const float n_eff = row_live ? neg : -INFINITY;
-    bf16x8 aop;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        aop[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[i >> 2][i & 3], s_eff, n_eff));
-    if (__ballot(bump)) {
-        const float alpha = bump ? __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, neg)) : 1.f;
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-            float a = __shfl(alpha, 4 * g4 + qq, kWave);
-#pragma unroll
-            for (int p = 0; p < 9; p++)
-                acc[p][qq] *= a;
-        }
-    }
-    m_run = m_new;
-    return aop;
-}
-
-// One 32-token half of a staged tile for the wavefront's row tiles selected by
-// ACT (bit a: row tile a has a live logit): K operands from LDS feed the QK
-// products, then V operands are read and each transposed B operand serves the
-// active row tiles.  ACT is a template argument so every MFMA sequence is
-// straight-line code.
-template <int ACT>
-__device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr, int g4, const bf16x8 (&qop)[2][4],
-                                        const uint32_t (&live)[2], bool partial, float scale_log2, float lazy,
-                                        float (&m_run)[2], f32x4 (&acc)[2][9])
-{
-    f32x4 st[2][2];
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
@@ -630,27 +573,26 @@ __device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr,
             kk[ks] = *reinterpret_cast<const u32x4 *>(kr + 64 * ks);
 #pragma unroll
         for (int a = 0; a < 2; a++)
-            if (ACT >> a & 1)
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++)
-                    st[a][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[ks]),
-                                                                       qop[a][ks], st[a][s], 0, 0, 0);
+            for (int ks = 0; ks < 4; ks++)
+                st[a][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[ks]), qop[a][ks],
+                                                                   st[a][s], 0, 0, 0);
     }
-    bf16x8 aop[2];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-        if (ACT >> a & 1)
-            aop[a] = chunk_softmax(st[a], live[a], partial, scale_log2, lazy, g4, m_run[a], acc[a]);
+}
+
+// O += P V for one 32-token half: the row sums come from a ones column tile; V
+// operands of column tile p (d = 16 p + n) come from transposing LDS reads.
+// Within a 16-lane group, lane j receives element j % 4 of the 8-byte chunks
+// addressed by lanes 4 e + j / 4 (e = 0..3), so lane (rr, g4) addresses token
+// 4 g4 + rr / 4 (first read) or 16 + 4 g4 + rr / 4 (second read) at d = 16 p +
+// 4 (rr % 4), which yields the lane's 8 tokens in the order of its logits.
+__device__ __forceinline__ void wg_pv(const unsigned char *buf, int h, int rr, int g4, const bf16x8 (&aop)[2],
+                                      f32x4 (&acc)[2][9])
+{
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
     for (int a = 0; a < 2; a++)
-        if (ACT >> a & 1)
-            acc[a][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], ones, acc[a][8], 0, 0, 0);
-    // V operand of column tile p (d = 16 p + n) by transposing LDS reads: within a
-    // 16-lane group, lane j receives element j % 4 of the 8-byte chunks addressed by
-    // lanes 4 e + j / 4 (e = 0..3).  Lane (rr, g4) therefore addresses token
-    // 4 g4 + rr / 4 (first read) or 16 + 4 g4 + rr / 4 (second read) at d = 16 p +
-    // 4 (rr % 4), which yields the lane's 8 tokens in the order of its logits.
+        acc[a][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], ones, acc[a][8], 0, 0, 0);
     const unsigned char *vr = buf + (64 + 32 * h + 4 * g4 + (rr >> 2)) * kWgPitch + 8 * (rr & 3);
 #pragma unroll
     for (int p = 0; p < 8; p++) {
@@ -659,11 +601,87 @@ __device__ __forceinline__ void wg_half(const unsigned char *buf, int h, int rr,
         const bf16x8 bop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int a = 0; a < 2; a++)
-            if (ACT >> a & 1)
-                acc[a][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], bop, acc[a][p], 0, 0, 0);
+            acc[a][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[a], bop, acc[a][p], 0, 0, 0);
     }
 }
 
+// One staged 64-token tile for the wavefront's two 16-row tiles (this lane: row
+// rr of each, 8 logits per 32-token half).  Both QK products come first; the
+// reference max m_run is kept on raw logits (the scale is positive) and moves
+// lazily, at most once per tile: only when the tile's max exceeds it by more than
+// `lazy` (2^8 after scaling), so unnormalised weights stay below 256 and the
+// output accumulators are rescaled rarely (a wavefront-uniform branch).  Any
+// reference gives the same normalised result.  A lane whose 8 logits of a half
+// are all masked gets scale 0 and offset -inf there, so its weights are
+// exp2(-inf) = 0 without a select per logit; per-logit masks (a -1e30 sentinel,
+// which underflows to 0) are applied only when some lane has a partly live half
+// (causal edge, window or sink boundary).  exp2 is the hardware instruction
+// (results below 2^-126 flush to zero, which the sum cannot see next to the
+// reference term).  Row sums come from the P V product itself (a ones column
+// tile), so the accumulators carry them and their rescaling.
+__device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4, const bf16x8 (&qop)[2][4],
+                                        const uint32_t (&live)[2][2], bool partial, float scale_log2, float lazy,
+                                        float (&m_run)[2], f32x4 (&acc)[2][9])
+{
+    f32x4 st[2][2][2];                                    // [half][row tile][16-token subtile]
+    wg_qk(buf, 0, rr, g4, qop, st[0]);
+    wg_qk(buf, 1, rr, g4, qop, st[1]);
+    if (partial) {                       // finite sentinel: a dead lane multiplies it by scale 0
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    st[h][a][i >> 2][i & 3] = (live[h][a] >> i) & 1u ? st[h][a][i >> 2][i & 3] : -1e30f;
+    }
+    float neg[2], m_old[2];
+    bool bump[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+        float mc = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const f32x4 *x = st[h][a];
+            const float mh = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            mc = live[h][a] != 0u ? fmaxf(mc, mh) : mc;
+        }
+        mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
+        mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
+        bump[a] = mc > m_run[a] + lazy;
+        m_old[a] = m_run[a];
+        m_run[a] = bump[a] ? mc : m_run[a];
+        neg[a] = m_run[a] == -INFINITY ? 0.f : -m_run[a] * scale_log2;
+    }
+    if (__ballot(bump[0] || bump[1])) {
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const float alpha = bump[a] ? __builtin_amdgcn_exp2f(fmaf(m_old[a], scale_log2, neg[a])) : 1.f;
+#pragma unroll
+            for (int qq = 0; qq < 4; qq++) {
+                const float f = __shfl(alpha, 4 * g4 + qq, kWave);
+#pragma unroll
+                for (int p = 0; p < 9; p++)
+                    acc[a][p][qq] *= f;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        bf16x8 aop[2];
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const bool lv = live[h][a] != 0u;
+            const float s_eff = lv ? scale_log2 : 0.f;
+            const float n_eff = lv ? neg[a] : -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                aop[a][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[h][a][i >> 2][i & 3], s_eff, n_eff));
+        }
+        wg_pv(buf, h, rr, g4, aop, acc);
+    }
+}
 
 // The 8 logits of lane group g4 are tokens 4*g4 .. +3 and 16 + 4*g4 .. +3 of the chunk.
 __device__ __forceinline__ uint32_t live8(uint32_t m32, int g4)
@@ -806,23 +824,21 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
                               ((qm & wmask) != 0ull || tile < w_init_hi || (tile >= w_win_lo && tile <= w_win_hi));
             if (need) {
                 const unsigned char *buf = sh_kv[e & 1];
+                uint32_t live[2][2];
+                bool any = false, part = false;
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int t0 = tile * 64 + 32 * h;
-                    uint32_t live[2];
-                    int act = 0;
-                    bool part = false;
 #pragma unroll
                     for (int a = 0; a < 2; a++) {
                         const bool sb = (qm >> qbit[a]) & 1ull;
-                        live[a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
-                        act |= __ballot(live[a] != 0u) != 0ull ? 1 << a : 0;
-                        part = part || (live[a] != 0u && live[a] != 0xffu);
+                        live[h][a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
+                        any = any || live[h][a] != 0u;
+                        part = part || (live[h][a] != 0u && live[h][a] != 0xffu);
                     }
-                    const bool partial = __ballot(part) != 0ull;
-                    if (act != 0)
-                        wg_half<3>(buf, h, rr, g4, qop, live, partial, P.scale_log2, lazy, m_run, acc);
                 }
+                if (__ballot(any) != 0ull)
+                    wg_tile(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, acc);
             }
             const int xn = (x + 1) % kWgStage;
             wg_write(stage[xn], sh_kv[(e + 1) & 1], tid);

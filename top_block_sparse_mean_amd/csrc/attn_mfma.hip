@@ -538,7 +538,7 @@ __device__ __forceinline__ void wg_issue(WgStage &st, const uint16_t *kb, const 
     for (int u = 0; u < 4; u++) {
         const int chunk = tid + 512 * u;       // 2048 chunks: 128 rows (64 K, 64 V) x 16
         const int row = chunk >> 4, col = chunk & 15;
-        const int t = min(t0 + (row & 63), n_k - 1);
+        const int t = min(max(t0 + (row & 63), 0), n_k - 1);
         const uint16_t *base = row < 64 ? kb : vb;
         st.c[u] = ld16(base + (long long)t * tstride + 8 * col);
     }
@@ -718,6 +718,8 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     const int qwg = kWgWaves * QPW;                       // queries per workgroup (<= 64)
     const int q_lo = qt * qwg;
     const int nq = max(0, min(qwg, s.n_q - q_lo));
+    if (nq == 0)                                          // query tile past this sequence's queries
+        return;
     const int ntile = (s.n_k + 63) / 64;
 
     for (int x = tid; x < ntile; x += 512)
@@ -805,48 +807,52 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     // the other buffer, then reuse that slot for tile e+1+kWgStage.  Issues and
     // writes are unconditional (clamped to the last tile) so the load counters the
     // compiler tracks are the same on every path.
+    // Every query attends at least its own position (window >= 1), so n_list >= 1
+    // here; the staging below reads sh_list[0 .. n_list) only.
     WgStage stage[kWgStage];
     const int last = max(n_list - 1, 0);
+    if (n_list > 0) {
 #pragma unroll
-    for (int x = 0; x < kWgStage; x++)
-        wg_issue(stage[x], kb, vb, tstride, sh_list[min(x, last)] * 64, s.n_k, tid);
-    wg_write(stage[0], sh_kv[0], tid);
-    wg_issue(stage[0], kb, vb, tstride, sh_list[min(kWgStage, last)] * 64, s.n_k, tid);
-    const int n_iter = ((n_list + kWgStage - 1) / kWgStage) * kWgStage;
-    for (int e0 = 0; e0 < n_iter; e0 += kWgStage) {
+        for (int x = 0; x < kWgStage; x++)
+            wg_issue(stage[x], kb, vb, tstride, sh_list[min(x, last)] * 64, s.n_k, tid);
+        wg_write(stage[0], sh_kv[0], tid);
+        wg_issue(stage[0], kb, vb, tstride, sh_list[min(kWgStage, last)] * 64, s.n_k, tid);
+        const int n_iter = ((n_list + kWgStage - 1) / kWgStage) * kWgStage;
+        for (int e0 = 0; e0 < n_iter; e0 += kWgStage) {
 #pragma unroll
-        for (int x = 0; x < kWgStage; x++) {
-            const int e = e0 + x;
-            __syncthreads();                               // LDS buffer e&1 holds tile e
-            const int tile = sh_list[min(e, last)];
-            const unsigned long long qm = sh_lqm[min(e, last)];
-            const bool need = e < n_list &&
-                              ((qm & wmask) != 0ull || tile < w_init_hi || (tile >= w_win_lo && tile <= w_win_hi));
-            if (need) {
-                const unsigned char *buf = sh_kv[e & 1];
-                uint32_t live[2][2];
-                bool any = false, part = false;
+            for (int x = 0; x < kWgStage; x++) {
+                const int e = e0 + x;
+                __syncthreads();                               // LDS buffer e&1 holds tile e
+                const int tile = sh_list[min(e, last)];
+                const unsigned long long qm = sh_lqm[min(e, last)];
+                const bool need = e < n_list &&
+                                  ((qm & wmask) != 0ull || tile < w_init_hi || (tile >= w_win_lo && tile <= w_win_hi));
+                if (need) {
+                    const unsigned char *buf = sh_kv[e & 1];
+                    uint32_t live[2][2];
+                    bool any = false, part = false;
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int t0 = tile * 64 + 32 * h;
+                    for (int h = 0; h < 2; h++) {
+                        const int t0 = tile * 64 + 32 * h;
 #pragma unroll
-                    for (int a = 0; a < 2; a++) {
-                        const bool sb = (qm >> qbit[a]) & 1ull;
-                        live[h][a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
-                        any = any || live[h][a] != 0u;
-                        part = part || (live[h][a] != 0u && live[h][a] != 0xffu);
+                        for (int a = 0; a < 2; a++) {
+                            const bool sb = (qm >> qbit[a]) & 1ull;
+                            live[h][a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
+                            any = any || live[h][a] != 0u;
+                            part = part || (live[h][a] != 0u && live[h][a] != 0xffu);
+                        }
                     }
+                    if (__ballot(any) != 0ull)
+                        wg_tile(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, acc);
                 }
-                if (__ballot(any) != 0ull)
-                    wg_tile(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, acc);
+                const int xn = (x + 1) % kWgStage;
+                wg_write(stage[xn], sh_kv[(e + 1) & 1], tid);
+                wg_issue(stage[xn], kb, vb, tstride, sh_list[min(e + 1 + kWgStage, last)] * 64, s.n_k, tid);
             }
-            const int xn = (x + 1) % kWgStage;
-            wg_write(stage[xn], sh_kv[(e + 1) & 1], tid);
-            wg_issue(stage[xn], kb, vb, tstride, sh_list[min(e + 1 + kWgStage, last)] * 64, s.n_k, tid);
         }
     }
     // Epilogue: lane (rr, g4) holds d = 16 p + rr of rows 4 g4 + r4; normalised bf16
-    // rows are transposed through this wavefront's 32 x 272-byte slice of the (now
+    // rows are transposed through this wavefront's 32-row slice of the (now
     // idle) staging buffers and stored as 16-byte row pieces.
     __syncthreads();
     unsigned char *ob = &sh_kv[0][0] + w * 32 * kWgPitch;

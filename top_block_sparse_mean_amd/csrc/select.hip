@@ -119,6 +119,127 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
     }
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+// Exact selection among compacted candidates sk[0 .. c) (ascending positions), whose
+// keys all lie in [t0, kmax]: the bits above the first difference of t0 and kmax
+// are common to every candidate, so the threshold search starts below them.
+template <int S>
+__device__ __forceinline__ void refine_topk(const uint32_t *sk, const int *si, int c, int need, uint32_t t0,
+                                            uint32_t kmax, int j_base, int32_t *out)
+{
+    const int lane = lane_id();
+    uint32_t key[S];
+#pragma unroll
+    for (int m = 0; m < S; m++) {
+        const int i = m * kWave + lane;
+        key[m] = i < c ? sk[i] : 0u;
+    }
+    uint32_t tau = t0;
+    if (t0 != kmax) {
+        const int hb = 31 - __clz(t0 ^ kmax);
+        tau = hb == 31 ? 0u : (t0 & ~((2u << hb) - 1u));
+        for (int bit = hb; bit >= 0; --bit) {
+            const uint32_t cand = tau | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int m = 0; m < S; m++)
+                cnt += __popcll(__ballot(m * kWave + lane < c && key[m] >= cand));
+            if (cnt >= need)
+                tau = cand;
+        }
+    }
+    int gt = 0;
+#pragma unroll
+    for (int m = 0; m < S; m++)
+        gt += __popcll(__ballot(m * kWave + lane < c && key[m] > tau));
+    const int need_eq = need - gt;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < S; m++) {
+        const int i = m * kWave + lane;
+        const bool valid = i < c;
+        const bool is_gt = valid && key[m] > tau;
+        const bool is_eq = valid && key[m] == tau;
+        const unsigned long long meq = __ballot(is_eq);
+        const int rank = eq_seen + lanes_below(meq);
+        eq_seen += __popcll(meq);
+        const bool sel = is_gt || (is_eq && rank < need_eq);
+        const unsigned long long ms = __ballot(sel);
+        const int slot = base + lanes_below(ms);
+        if (sel && slot < need)
+            out[slot] = j_base + si[i];
+        base += __popcll(ms);
+    }
+}
+
+constexpr int kFilterCap = 512;
+
+// One wavefront, need <= 64: the `need` largest of n keys (layout as wave_topk).
+// Every lane holding a key contributes its maximum, and at least need lanes hold
+// keys, so the need-th largest key is >= t0 = the smallest lane maximum.  Keys >=
+// t0 are compacted in ascending position order into sk/si (kFilterCap entries of
+// wavefront-private LDS) and the exact search runs on them alone; more than
+// kFilterCap candidates fall back to the full search.
+template <int KPL>
+__device__ __forceinline__ void wave_topk_filtered(const uint32_t (&key)[KPL], int n, int need, int j_base,
+                                                   int32_t *out, uint32_t *sk, int *si)
+{
+    const int lane = lane_id();
+    uint32_t lmax = 0u;
+    bool has = false;
+#pragma unroll
+    for (int m = 0; m < KPL; m++)
+        if (m * kWave + lane < n) {
+            lmax = max(lmax, key[m]);
+            has = true;
+        }
+    const uint32_t t0 = wave_min_u32(has ? lmax : 0xffffffffu);
+    const uint32_t kmax = wave_max_u32(lmax);
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int i = m * kWave + lane;
+        const bool cnd = i < n && key[m] >= t0;
+        const unsigned long long mk = __ballot(cnd);
+        const int pos = c + lanes_below(mk);
+        if (cnd && pos < kFilterCap) {
+            sk[pos] = key[m];
+            si[pos] = i;
+        }
+        c += __popcll(mk);
+    }
+    if (c > kFilterCap) {
+        wave_topk<KPL>(key, n, need, j_base, out);
+        return;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (c <= 64)
+        refine_topk<1>(sk, si, c, need, t0, kmax, j_base, out);
+    else if (c <= 128)
+        refine_topk<2>(sk, si, c, need, t0, kmax, j_base, out);
+    else if (c <= 256)
+        refine_topk<4>(sk, si, c, need, t0, kmax, j_base, out);
+    else
+        refine_topk<8>(sk, si, c, need, t0, kmax, j_base, out);
+}
+
 template <int NT>
 __device__ __forceinline__ int2 block_scan_flag(bool f, int *sh)
 {
@@ -381,7 +502,12 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
             int i = m * kWave + lane;
             kr[m] = i < n ? keys[i] : 0u;
         }
-        wave_topk<KPL>(kr, n, min(r.need, n), r.j_lo, out);
+        __shared__ uint32_t sh_k[kFilterCap];
+        __shared__ int sh_i[kFilterCap];
+        if (r.need <= kWave)
+            wave_topk_filtered<KPL>(kr, n, min(r.need, n), r.j_lo, out, sh_k, sh_i);
+        else
+            wave_topk<KPL>(kr, n, min(r.need, n), r.j_lo, out);
         for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
             out[s2] = -1;
     }
@@ -565,7 +691,13 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
         write_all(P, out, r, lane, kWave);
         return;
     }
-    wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
+    __shared__ uint32_t sh_k[4][kFilterCap];
+    __shared__ int sh_i[4][kFilterCap];
+    const int wv = threadIdx.x / kWave;
+    if (r.need <= kWave)
+        wave_topk_filtered<KPL>(kr, r.n_cand, r.need, r.j_lo, out, sh_k[wv], sh_i[wv]);
+    else
+        wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
     for (int s = r.need + lane; s < P.topk; s += kWave)
         out[s] = -1;
 }

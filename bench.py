@@ -12,6 +12,7 @@ instead (prefill workloads report tok/s).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -37,6 +38,49 @@ def make_params(w, device):
                                   head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk,
                                   n_init=w.n_init, window=w.window, shared_selection=w.shared_selection,
                                   topk_per_seq=w.topk_per_seq, dtype=dt)
+
+
+class TimingEvents:
+    """HIP events for the attention kernel's live duration, created with
+    hipEventDisableSystemFence: a default event's record performs a system-scope
+    release (cache write-back) between the kernels of the step, which costs several
+    microseconds per record in a decode step and is not needed to read a timestamp.
+    They live in the HIP runtime the process already loaded (torch's)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                ev = ctypes.c_void_p()
+                rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+                pair.append(ev.value)
+            self.pairs.append(tuple(pair))
+
+    def mean_ms(self):
+        tot = 0.0
+        for a, b in self.pairs:
+            ms = ctypes.c_float()
+            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            tot += ms.value
+        return tot / len(self.pairs)
+
+    def close(self):
+        for pair in self.pairs:
+            for ev in pair:
+                self.hip.hipEventDestroy(ev)
+        self.pairs = []
 
 
 class Step:
@@ -200,12 +244,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:                          # instantiate the handles before they are passed down
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    tev = TimingEvents(args.steps)
+    evs = tev.pairs
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_begin.record()
@@ -217,7 +257,8 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    attn_ms = tev.mean_ms()
+    tev.close()
 
     idx_h, n_h = step.idx.cpu().numpy(), step.n_idx.cpu().numpy()
     a_tot = attended_total_exact(w, idx_h, n_h)

@@ -137,7 +137,9 @@ sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, c
  *          ascending order, padded with -1; rows = total_q, or batch when
  *          shared_selection = 1
  *   n_idx  [h_kv, rows] int32 out: number of selected blocks, min(k, |C|)
- *   ws     workspace of at least select_bytes (sparse_attn_workspace_size).
+ *   ws     workspace of at least select_bytes (sparse_attn_workspace_size),
+ *          owned by the caller; its contents on entry do not matter.  Calls
+ *          that share one workspace must not overlap in time.
  * Scores are computed in fp32 from fp32 pooled keys and fp32-summed queries;
  * equal scores keep the lower block index. */
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp,

@@ -90,11 +90,13 @@ def _ws(p):
 
 
 def test_workspace_sizes():
-    # decode shape: one fused workgroup per row, no selection workspace; one attention split per
-    # (query, KV head) unit when there are enough units, else partials for the combine
+    # decode shape: (key, position) survivors of each 128-candidate part of every (row, KV
+    # head), min(k, 128) per part; one attention split per (query, KV head) unit when there
+    # are enough units, else partials for the combine
     sel, fwd = _ws(params())
-    assert sel == 0 and fwd > 0 and fwd % (130 * 4) == 0
-    assert _ws(params(batch=256, total_q=256, max_k=4096, total_k=256 * 4096)) == (0, 0)
+    assert sel == 2 * 2 * 1 * 8 * 8 and fwd > 0 and fwd % (130 * 4) == 0
+    assert _ws(params(batch=256, total_q=256, max_k=4096, total_k=256 * 4096)) == (2 * 256 * 1 * 8 * 8, 0)
+    assert _ws(params(max_k=32768, total_k=65536, topk=32))[0] == 2 * 2 * 4 * 32 * 8
     # prefill: scores of every (row, block) are kept: h_kv * rows * nb_max * 4
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
     sel, fwd = _ws(p)

@@ -66,6 +66,26 @@ def test_edge_cases(case):
     parity.full_check(w, x, xg)
 
 
+DECODE_EDGE = {
+    # k between the filtered search (<= 64) and the part size (128)
+    "k100": dict(topk=100, block=8),
+    # k above the part size: every part survives whole, full search over <= 512 survivors
+    "k300": dict(topk=300, block=8),
+    # per-sequence k, zero for some rows
+    "k_per_seq": dict(topk=7, topk_per_seq=[0, 5, 0, 7, 2]),
+    # a single 128-candidate part
+    "one_part": dict(block=32, topk=9),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_EDGE))
+def test_decode_selection_cases(case):
+    """One query per sequence: the part-scoring + merge selection plan."""
+    w = small("bf16_decode_32k").scaled(**DECODE_EDGE[case])
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
 def test_fp32_d64_decode_and_prefill_mix():
     w = Workload(name="mix", dtype=DTYPE_F32, h_q=4, h_kv=1, head_dim=64, seqlens_k=[300, 1200, 95],
                  seqlens_q=[300, 3, 95], block=32, pool=POOL_MEAN, topk=3, n_init=32, window=64, seed=5)
@@ -151,6 +171,29 @@ def test_deterministic():
     b = parity.run_gpu(w, xg)
     assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["n_idx"], b["n_idx"])
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_select_workspace_reuse():
+    """Decode rows are scored in parts whose survivors go through the workspace; one
+    workspace, left with stale contents, serves repeated calls."""
+    w = small("bf16_decode_32k")
+    x, xg = parity.gen_pair(w)
+    p = parity.params_for(w)
+    kc = sa.compress(p, xg["k"])
+    sel_b, _ = sa.workspace_size(p)
+    assert sel_b > 0
+    ws = torch.full((sel_b,), 0xAB, dtype=torch.uint8, device="cuda")
+    ref = None
+    for _ in range(3):
+        idx = torch.full((w.h_kv, p.rows, w.topk), -7, dtype=torch.int32, device="cuda")
+        n_idx = torch.full((w.h_kv, p.rows), -7, dtype=torch.int32, device="cuda")
+        sa.select(p, xg["q"], kc, xg["k"], idx, n_idx, ws=ws)
+        torch.cuda.synchronize()
+        got = (idx.cpu().numpy(), n_idx.cpu().numpy())
+        if ref is None:
+            ref = got
+            parity.check_select(w, x, oracle.compress(w, x["k"]), got[0], got[1])
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
 
 
 def test_compress_tail_matches_full():

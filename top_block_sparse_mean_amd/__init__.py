@@ -146,16 +146,17 @@ def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Opt
 def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, n_idx: torch.Tensor,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = False,
         ws: Optional[torch.Tensor] = None, stream=None, events=None):
-    """Sparse attention; ``events`` = (begin, end) torch.cuda.Event pair recorded around the
-    main attention kernel (both must have been recorded once, so their handles exist)."""
+    """Sparse attention; ``events`` = (begin, end) pair recorded around the main attention
+    kernel: torch.cuda.Event objects (recorded once, so their handles exist) or raw
+    hipEvent_t handles as ints."""
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((p.s.h_q, p.s.total_q), dtype=torch.float32, device=q.device)
     ws, nbytes = _ws(workspace_size(p)[1], q.device, ws)
     if events is not None:
-        p.s.timing_events[0] = events[0].cuda_event
-        p.s.timing_events[1] = events[1].cuda_event
+        p.s.timing_events[0] = events[0] if isinstance(events[0], int) else events[0].cuda_event
+        p.s.timing_events[1] = events[1] if isinstance(events[1], int) else events[1].cuda_event
     try:
         st = lib().sparse_attn_fwd(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_idx), _ptr(out),
                                    _ptr(lse), _ptr(ws), nbytes, _stream(stream))

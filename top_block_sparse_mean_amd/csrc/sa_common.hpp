@@ -198,12 +198,30 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8])
 
 // ---------------------------------------------------------------- reductions
 
-// Sum over aligned groups of W lanes (W a power of two <= 64).
+// v from another lane of the same 16-lane row (DPP: a VALU operand modifier, no LDS).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64), the total in every
+// lane.  Within a 16-lane row: swap neighbours (quad_perm 1,0,3,2), swap pairs
+// (quad_perm 2,3,0,1), mirror each half row, mirror the row; wider groups add the
+// partner row through a lane shuffle.
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
+    if (W >= 2)
+        v += dpp_f32<0xB1>(v);
+    if (W >= 4)
+        v += dpp_f32<0x4E>(v);
+    if (W >= 8)
+        v += dpp_f32<0x141>(v);
+    if (W >= 16)
+        v += dpp_f32<0x140>(v);
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1)
+    for (int o = 16; o < W; o <<= 1)
         v += __shfl_xor(v, o, kWave);
     return v;
 }

@@ -79,10 +79,10 @@ __device__ __forceinline__ void write_all(const KP &P, int32_t *out, const RowGe
 
 // ---------------------------------------------------------------- top-k cores
 
-// One wavefront: the `need` largest of n keys (key i at lane i % 64, slot i / 64),
-// indices j_base + i written ascending to out[0 .. need).
-template <int KPL>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int need, int j_base, int32_t *out)
+// One wavefront: the `need` largest of n keys (key i at lane i % 64, slot i / 64);
+// emit(slot, i) is called for each selected key, slots 0 .. need-1 in ascending i.
+template <int KPL, typename Emit>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int need, Emit emit)
 {
     const int lane = lane_id();
     // counts come from ballots (one scalar popcount per slot): no cross-lane data moves
@@ -113,11 +113,19 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
         eq_seen += __popcll(meq);
         bool s = is_gt || (is_eq && rank < need_eq);
         unsigned long long ms = __ballot(s);
-        if (s)
-            out[base + lanes_below(ms)] = j_base + i;
+        const int slot = base + lanes_below(ms);
+        if (s && slot < need)
+            emit(slot, i);
         base += __popcll(ms);
     }
 }
+
+// Writes the selected block indices j_base + i to out[slot].
+struct EmitIdx {
+    int32_t *out;
+    int j_base;
+    __device__ void operator()(int slot, int i) const { out[slot] = j_base + i; }
+};
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
@@ -138,9 +146,9 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 // Exact selection among compacted candidates sk[0 .. c) (ascending positions), whose
 // keys all lie in [t0, kmax]: the bits above the first difference of t0 and kmax
 // are common to every candidate, so the threshold search starts below them.
-template <int S>
+template <int S, typename Emit>
 __device__ __forceinline__ void refine_topk(const uint32_t *sk, const int *si, int c, int need, uint32_t t0,
-                                            uint32_t kmax, int j_base, int32_t *out)
+                                            uint32_t kmax, Emit emit)
 {
     const int lane = lane_id();
     uint32_t key[S];
@@ -182,7 +190,7 @@ __device__ __forceinline__ void refine_topk(const uint32_t *sk, const int *si, i
         const unsigned long long ms = __ballot(sel);
         const int slot = base + lanes_below(ms);
         if (sel && slot < need)
-            out[slot] = j_base + si[i];
+            emit(slot, si[i]);
         base += __popcll(ms);
     }
 }
@@ -195,9 +203,9 @@ constexpr int kFilterCap = 512;
 // t0 are compacted in ascending position order into sk/si (kFilterCap entries of
 // wavefront-private LDS) and the exact search runs on them alone; more than
 // kFilterCap candidates fall back to the full search.
-template <int KPL>
-__device__ __forceinline__ void wave_topk_filtered(const uint32_t (&key)[KPL], int n, int need, int j_base,
-                                                   int32_t *out, uint32_t *sk, int *si)
+template <int KPL, typename Emit>
+__device__ __forceinline__ void wave_topk_filtered(const uint32_t (&key)[KPL], int n, int need, Emit emit,
+                                                   uint32_t *sk, int *si)
 {
     const int lane = lane_id();
     uint32_t lmax = 0u;
@@ -224,20 +232,31 @@ __device__ __forceinline__ void wave_topk_filtered(const uint32_t (&key)[KPL], i
         c += __popcll(mk);
     }
     if (c > kFilterCap) {
-        wave_topk<KPL>(key, n, need, j_base, out);
+        wave_topk<KPL>(key, n, need, emit);
         return;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (c <= 64)
-        refine_topk<1>(sk, si, c, need, t0, kmax, j_base, out);
+        refine_topk<1>(sk, si, c, need, t0, kmax, emit);
     else if (c <= 128)
-        refine_topk<2>(sk, si, c, need, t0, kmax, j_base, out);
+        refine_topk<2>(sk, si, c, need, t0, kmax, emit);
     else if (c <= 256)
-        refine_topk<4>(sk, si, c, need, t0, kmax, j_base, out);
+        refine_topk<4>(sk, si, c, need, t0, kmax, emit);
     else
-        refine_topk<8>(sk, si, c, need, t0, kmax, j_base, out);
+        refine_topk<8>(sk, si, c, need, t0, kmax, emit);
+}
+
+// The `need` largest of n keys in one wavefront (filtered search for need <= 64).
+template <int KPL, typename Emit>
+__device__ __forceinline__ void wave_select(const uint32_t (&key)[KPL], int n, int need, Emit emit, uint32_t *sk,
+                                            int *si)
+{
+    if (need <= kWave)
+        wave_topk_filtered<KPL>(key, n, need, emit, sk, si);
+    else
+        wave_topk<KPL>(key, n, need, emit);
 }
 
 template <int NT>
@@ -452,65 +471,133 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     }
 }
 
-// ---------------------------------------------------------------- select_row (fused)
+// ---------------------------------------------------------------- select_part + select_merge
 
-// One 1024-thread workgroup per (row, KV head) for rows with at most 64*KPL
-// candidates: every lane issues the loads of all its key rows at once, the
-// order keys go to LDS, wavefront 0 selects.  No workspace, one launch.
-template <typename T, typename KT, int D, int KPL>
-__global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
-                                                          const KT *__restrict__ kbase,
-                                                          int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+// Rows with at most 64*KPL candidates and few rows (decode).  select_part: the
+// candidates of a row are scored by ceil(n_cand / kPartCand) workgroups of 256
+// threads (four share a compute unit, so the loads of the whole table are in
+// flight at once); each keeps its part's `need` best (ascending position) as
+// (order key, position) pairs in the workspace.  select_merge: one wavefront per
+// row selects the row's `need` best among the parts' survivors, which contain it.
+constexpr int kPartCand = 128;
+
+__host__ __device__ inline int part_cap(int topk) { return topk < kPartCand ? topk : kPartCand; }
+
+template <typename T, typename KT, int D>
+__global__ __launch_bounds__(256) void select_part_kernel(KP P, const T *__restrict__ q,
+                                                          const KT *__restrict__ kbase, uint32_t *__restrict__ ws_k,
+                                                          int32_t *__restrict__ ws_i, int n_part)
 {
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
-    constexpr int GPW = kWave / L, NG = 16 * GPW, MAXC = 64 * KPL;
-    constexpr int U = (MAXC + NG - 1) / NG;
-    __shared__ uint32_t keys[MAXC];
-    const long long row = blockIdx.x;
+    constexpr int GPW = kWave / L, NG = 4 * GPW;
+    constexpr int U = (kPartCand + NG - 1) / NG;
+    __shared__ uint32_t sh_key[kPartCand];
+    __shared__ uint32_t sh_k[kFilterCap];
+    __shared__ int sh_i[kFilterCap];
+    const long long row = blockIdx.x / n_part;
+    const int part = (int)(blockIdx.x % n_part);
     const int c = blockIdx.y;
     const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
     RowGeo r = row_geo(P, row);
-    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
-    if (tid == 0)
-        n_idx[(long long)c * P.rows + row] = r.need;
-    if (r.need == r.n_cand) {
-        write_all(P, out, r, tid, 1024);
+    if (r.need == r.n_cand || r.need == 0)                // the merge writes these rows alone
         return;
-    }
-    const int n = min(r.n_cand, MAXC);
+    const int i0 = part * kPartCand, i1 = min(i0 + kPartCand, r.n_cand);
+    if (i0 >= i1)
+        return;
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        int jj = min(u * NG + grp, n - 1);
-        raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, r.j_lo + jj))[sub];
+        const int i = min(i0 + u * NG + grp, i1 - 1);
+        raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, r.j_lo + i))[sub];
     }
     float qv[VPL];
     selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
-        int jj = u * NG + grp;
-        if (sub == 0 && jj < n)
-            keys[jj] = order_key(sc);
+        const float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
+        const int i = u * NG + grp;
+        if (sub == 0 && i0 + i < i1)
+            sh_key[i] = order_key(sc);
     }
     __syncthreads();
-    if (tid < kWave) {
-        uint32_t kr[KPL];
+    if (tid >= kWave)
+        return;
+    const int n = i1 - i0, cap = part_cap(P.topk);
+    const long long slot0 = (((long long)c * P.rows + row) * n_part + part) * cap;
+    uint32_t kr[kPartCand / kWave];
 #pragma unroll
-        for (int m = 0; m < KPL; m++) {
-            int i = m * kWave + lane;
-            kr[m] = i < n ? keys[i] : 0u;
-        }
-        __shared__ uint32_t sh_k[kFilterCap];
-        __shared__ int sh_i[kFilterCap];
-        if (r.need <= kWave)
-            wave_topk_filtered<KPL>(kr, n, min(r.need, n), r.j_lo, out, sh_k, sh_i);
-        else
-            wave_topk<KPL>(kr, n, min(r.need, n), r.j_lo, out);
-        for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
-            out[s2] = -1;
+    for (int m = 0; m < kPartCand / kWave; m++) {
+        const int i = m * kWave + lane;
+        kr[m] = i < n ? sh_key[i] : 0u;
     }
+    const int keep = min(r.need, n);
+    if (keep == n) {                                     // the whole part survives
+        for (int i = lane; i < n; i += kWave) {
+            ws_k[slot0 + i] = sh_key[i];
+            ws_i[slot0 + i] = i0 + i;
+        }
+        return;
+    }
+    auto emit = [&](int slot, int i) {
+        ws_k[slot0 + slot] = sh_key[i];
+        ws_i[slot0 + slot] = i0 + i;
+    };
+    wave_select<kPartCand / kWave>(kr, n, keep, emit, sh_k, sh_i);
+}
+
+// 4 wavefronts per workgroup, one row each.  grid: (ceil(rows / 4), h_kv).
+template <int KPL>
+__global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t *__restrict__ ws_k,
+                                                           const int32_t *__restrict__ ws_i, int n_part,
+                                                           int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+{
+    __shared__ uint32_t sh_k[4][kFilterCap];
+    __shared__ int sh_i[4][kFilterCap];
+    __shared__ int sh_pos[4][64 * KPL];
+    const long long row = (long long)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int c = blockIdx.y, lane = lane_id(), wv = threadIdx.x / kWave;
+    if (row >= P.rows)
+        return;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (lane == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    if (r.need == r.n_cand) {
+        write_all(P, out, r, lane, kWave);
+        return;
+    }
+    if (r.need == 0) {
+        for (int s2 = lane; s2 < P.topk; s2 += kWave)
+            out[s2] = -1;
+        return;
+    }
+    // survivors: full parts keep m_full = min(need, kPartCand), the last part m_last
+    const int cap = part_cap(P.topk);
+    const int n_part_row = (r.n_cand + kPartCand - 1) / kPartCand;
+    const int m_full = min(r.need, kPartCand);
+    const int m_last = min(r.need, r.n_cand - (n_part_row - 1) * kPartCand);
+    const int m_tot = (n_part_row - 1) * m_full + m_last;
+    const long long base = ((long long)c * P.rows + row) * n_part * cap;
+    uint32_t kr[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int j = m * kWave + lane;
+        const int pt = j / m_full, sl = j - pt * m_full;
+        const long long o = base + (long long)pt * cap + sl;
+        kr[m] = j < m_tot ? ws_k[o] : 0u;
+        if (j < m_tot)
+            sh_pos[wv][j] = ws_i[o];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the survivors are in ascending position order, so selecting among them by their
+    // rank keeps the lower block index on equal scores
+    auto emit = [&](int slot, int j) { out[slot] = r.j_lo + sh_pos[wv][j]; };
+    wave_select<KPL>(kr, m_tot, r.need, emit, sh_k[wv], sh_i[wv]);
+    for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
+        out[s2] = -1;
 }
 
 // ---------------------------------------------------------------- score_tile (MFMA fp32)
@@ -694,10 +781,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     __shared__ uint32_t sh_k[4][kFilterCap];
     __shared__ int sh_i[4][kFilterCap];
     const int wv = threadIdx.x / kWave;
-    if (r.need <= kWave)
-        wave_topk_filtered<KPL>(kr, r.n_cand, r.need, r.j_lo, out, sh_k[wv], sh_i[wv]);
-    else
-        wave_topk<KPL>(kr, r.n_cand, r.need, r.j_lo, out);
+    wave_select<KPL>(kr, r.n_cand, r.need, EmitIdx{out, r.j_lo}, sh_k[wv], sh_i[wv]);
     for (int s = r.need + lane; s < P.topk; s += kWave)
         out[s] = -1;
 }
@@ -950,9 +1034,13 @@ static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (8 
 
 size_t select_workspace_bytes(const KP &P, int plan)
 {
-    if (plan == kSelectEmpty || plan == kSelectRow)
+    if (plan == kSelectEmpty)
         return 0;
     long long stride = P.g == 1 ? P.max_k : P.nb_max;
+    if (plan == kSelectRow) {                             // (key, position) survivors of every part
+        const long long n_part = (stride + kPartCand - 1) / kPartCand;
+        return (size_t)P.h_kv * (size_t)P.rows * (size_t)n_part * (size_t)part_cap(P.topk) * 2 * sizeof(uint32_t);
+    }
     return (size_t)P.h_kv * (size_t)P.rows * (size_t)stride * sizeof(uint32_t);
 }
 
@@ -985,18 +1073,30 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         return hipGetLastError();
     }
     if (plan == kSelectRow) {
-        dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
-        if (P.g == 1) {
-            if (stride <= 512)
-                select_row_kernel<T, T, D, 8><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
-            else
-                select_row_kernel<T, T, D, 16><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
-        } else {
-            if (stride <= 512)
-                select_row_kernel<T, float, D, 8><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
-            else
-                select_row_kernel<T, float, D, 16><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
-        }
+        const int n_part = (int)((stride + kPartCand - 1) / kPartCand);
+        const size_t n_slot = (size_t)P.h_kv * (size_t)P.rows * (size_t)n_part * (size_t)part_cap(P.topk);
+        uint32_t *ws_k = wsk;
+        int32_t *ws_i = (int32_t *)(wsk + n_slot);
+        dim3 grid((unsigned)(P.rows * n_part), (unsigned)P.h_kv);
+        if (P.g == 1)
+            select_part_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, ws_k, ws_i, n_part);
+        else
+            select_part_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, ws_k, ws_i, n_part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        // survivors per row <= n_part * min(need, kPartCand) <= the row's candidates
+        const long long m_max = (long long)n_part * part_cap(P.topk) < stride ? (long long)n_part * part_cap(P.topk)
+                                                                             : stride;
+        dim3 mgrid((unsigned)((P.rows + 3) / 4), (unsigned)P.h_kv);
+        if (m_max <= 128)
+            select_merge_kernel<2><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
+        else if (m_max <= 256)
+            select_merge_kernel<4><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
+        else if (m_max <= 512)
+            select_merge_kernel<8><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
+        else
+            select_merge_kernel<16><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
         return hipGetLastError();
     }
     if (plan == kSelectSplit) {

@@ -113,8 +113,11 @@ class Step:
                events=events)
 
 
-def attended_total_exact(w, idx_host, n_idx_host):
-    """Like attended_total but clipping the edge blocks exactly (prefill workloads)."""
+def attended_total_exact(w, idx_host, n_idx_host, per_unit=False):
+    """Sum over (query, KV head) of the attended-set size |A|, edge blocks clipped exactly.
+    per_unit: with a shared selection, count each (sequence, KV head) once with its largest
+    set (the last draft's, which holds every other draft's) -- the positions the attention
+    kernel reads once per unit."""
     import numpy as np
     tot = 0
     qi = 0
@@ -137,29 +140,91 @@ def attended_total_exact(w, idx_host, n_idx_host):
             lf = np.maximum(0, np.minimum(np.minimum((first + 1) * g, nk), hi) - f0)
             ll = np.maximum(0, np.minimum(np.minimum((last + 1) * g, nk), hi) - last * g)
             n2 = np.where(ns == 0, 0, np.where(ns == 1, lf, lf + (ns - 2) * g + ll))
-            tot += int((n1 + n2 + n3).sum())
+            a = n1 + n2 + n3
+            tot += int(a.max()) if (per_unit and w.shared_selection and len(a)) else int(a.sum())
         qi += nq
     return tot
+
+
+# Dominant kernel of each workload and the sources it is built from: a counter record
+# is used only while these files are unchanged.
+CSRC = "top_block_sparse_mean_amd/csrc/"
+KERNEL_SOURCES = {
+    "sa::attn_mfma_kernel": [CSRC + "attn_decode.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
+                             CSRC + "sa_internal.hpp"],
+    "sa::attn_wg_kernel": [CSRC + "attn_prefill.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
+                           CSRC + "sa_internal.hpp"],
+}
+DOMINANT = {"bf16_decode_32k": "sa::attn_mfma_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel"}
+
+
+def sources_sha256(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(HERE, f), "rb").read())
+    return h.hexdigest()
+
+
+def counter_record_path(kernel, workload):
+    name = kernel.split("::")[-1].replace("_kernel", "")
+    return os.path.join(HERE, "profiles", f"{name}_{workload}_counters.json")
 
 
 def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     record (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain
-    1 GiB device copy), or None when the record is for another workload or the kernel's
-    source has changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(HERE, "profiles", "attn_mfma_decode_32k_counters.json")
+    1 GiB device copy), or None when there is no record for the workload or the kernel's
+    sources have changed since the counters were taken."""
+    kernel = DOMINANT.get(workload)
+    if kernel is None:
+        return None
+    path = counter_record_path(kernel, workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("workload") != workload:
-        return None
-    src = open(os.path.join(HERE, rec["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if rec.get("workload") != workload or rec.get("sources_sha256") != sources_sha256(rec["sources"]):
         return None
     kib = (rec["fetch_kib_per_dispatch"] * rec["fetch_calibration"]["factor"]
            + rec["write_kib_per_dispatch"] * rec["write_calibration"]["factor"])
     return int(kib * 1024)
+
+
+def record_counters(workload, fetch_dir, write_dir, commands):
+    """Write the counter record of the workload's dominant kernel from two rocprofv3
+    --pmc runs of this script with --copy-probe-mib 1024 (FETCH_SIZE, then WRITE_SIZE)."""
+    import csv
+    import glob
+    kernel = DOMINANT[workload]
+
+    def load(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        rows = [r for f in files for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        mine = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].replace("void ", "").startswith(kernel)]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not mine or not copies:
+            raise SystemExit(f"no {counter} rows for {kernel} or for the calibration copy in {d}")
+        return sum(mine) / len(mine), max(copies)
+
+    fetch, fetch_copy = load(fetch_dir, "FETCH_SIZE")
+    write, write_copy = load(write_dir, "WRITE_SIZE")
+    expected = 1024 * 1024                          # KiB moved each way by the 1 GiB copy
+    srcs = KERNEL_SOURCES[kernel]
+    rec = {
+        "kernel": kernel, "workload": workload, "sources": srcs, "sources_sha256": sources_sha256(srcs),
+        "fetch_kib_per_dispatch": round(fetch, 2), "write_kib_per_dispatch": round(write, 2),
+        "fetch_calibration": {"kernel": "__amd_rocclr_copyBuffer (1 GiB device copy)", "expected_kib": expected,
+                              "counted_kib": fetch_copy, "factor": round(expected / fetch_copy, 4)},
+        "write_calibration": {"kernel": "__amd_rocclr_copyBuffer (1 GiB device copy)", "expected_kib": expected,
+                              "counted_kib": write_copy, "factor": round(expected / write_copy, 4)},
+        "commands": commands,
+    }
+    path = counter_record_path(kernel, workload)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(path)
 
 
 def cpu_baseline(w, x, seconds=10.0):
@@ -221,7 +286,18 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a known-size kernel that "
                          "calibrates HBM byte counters in a profiled run)")
+    ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: write the workload's counter record under profiles/ from the output "
+                         "directories of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
     args = ap.parse_args()
+    if args.record_counters:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $REPO/{d} -o run "
+               "-- python3 $REPO/bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline "
+               "--copy-probe-mib 1024")
+        record_counters(args.workload, *args.record_counters,
+                        [cmd.format(c="FETCH_SIZE", d=args.record_counters[0], w=args.workload),
+                         cmd.format(c="WRITE_SIZE", d=args.record_counters[1], w=args.workload)])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)
@@ -266,7 +342,8 @@ def main():
     elt = 2 if w.dtype == DTYPE_BF16 else 4
     decode = w.name in DECODE
     if decode:
-        attn_bytes = a_tot * 2 * d * elt + 2 * w.total_q * w.h_q * d * elt
+        a_read = attended_total_exact(w, idx_h, n_h, per_unit=True)
+        attn_bytes = a_read * 2 * d * elt + 2 * w.total_q * w.h_q * d * elt
         roof = dict(bound="hbm", achieved=round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s")
         roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)

@@ -1,304 +1,11 @@
-// attn_mfma.hip -- bf16 sparse attention on gfx950 matrix cores for units of
-// up to 16 query rows that share one attended set: the GQA heads of one query
-// (per-query selection), or every head of every draft of a sequence (shared
-// selection; drafts differ only by their causal limit).  Online softmax with
-// fp32 running max / sum / output (PulseCol §3.1 Eq. (2); S3R review, sparse
-// drafting formula).
-//
-// Per wavefront, 32 attended positions at a time:
-//   S^T = K Q^T   two 16x16x32 bf16 MFMA tiles per k-step (16 tokens x 16 rows);
-//                 A = K rows loaded straight from HBM (lane l: token l%16, 16 B
-//                 of the head dimension), B = Q^T kept in registers.
-//   P   = softmax numerators, fp32 -> bf16 in the layout the next MFMA reads as
-//         its A operand (the 8 logits a lane holds are the 8 tokens its A row needs).
-//   O   += P V    eight 16x16x32 tiles; B = V loaded straight from HBM as one
-//                 256 B row per 16 lanes, transposed 8x8 in registers with
-//                 v_perm, output column n of tile p is head-dim index 8n + p.
-// The next chunk's K/V loads are issued before the current chunk is computed.
-// The attended positions of the workgroup's split are first mapped to tokens
-// into LDS (the selection row is read like a page table).  Splits write
-// (max, sum, unnormalised output) partials that attn_combine merges.
-#include <stdlib.h>
-
-#include "sa_common.hpp"
-#include "sa_internal.hpp"
+// attn_prefill.hip -- bf16 sparse attention on gfx950 matrix cores for many
+// consecutive queries with per-query selections (prefill): queries whose
+// attended sets overlap are processed together over the union of their tiles,
+// each row masked to its own set (PulseCol §3.1 Eq. (2); SparDA summary,
+// Method).
+#include "mfma_common.hpp"
 
 namespace sa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-template <int D>
-struct ChunkRegs {
-    u32x4 k[2][D / 32];   // K rows of the two 16-token subtiles, A-operand layout
-    u32x4 v[8];           // V rows of the lane's 8 tokens, head-dim slice 8*(l%16) .. +8
-    uint32_t live;        // bit i: logit i of this lane is inside the split and causal for its row
-};
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-template <int D>
-__device__ __forceinline__ void load_chunk(ChunkRegs<D> &r, const int *tok, int base, int n, const uint16_t *kb,
-                                           const uint16_t *vb, long long tstride, int rr, int g4, int p_row)
-{
-    constexpr int KS = D / 32;
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-        int pos = min(base + 16 * s + rr, n - 1);
-        long long off = (long long)tok[pos] * tstride + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            r.k[s][ks] = ld16(kb + off + 32 * ks);
-    }
-    r.live = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        int pos = base + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + (i - 4));
-        int t = tok[min(pos, n - 1)];
-        r.live |= (pos < n && t <= p_row) ? (1u << i) : 0u;
-        if (D == 128 || rr < D / 8)
-            r.v[i] = ld16(vb + (long long)t * tstride + 8 * rr);
-        else
-            r.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, uint32_t live, const bf16x8 (&qop)[D / 32],
-                                              float scale_log2, int g4, float &m_run, float &l_part, f32x4 (&acc)[8])
-{
-    constexpr int KS = D / 32;
-    f32x4 st[2];
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-        st[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            st[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[s][ks]), qop[ks],
-                                                            st[s], 0, 0, 0);
-    }
-    float sv[8];
-    float mc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float x = st[i >> 2][i & 3] * scale_log2;
-        sv[i] = (live >> i) & 1u ? x : -INFINITY;
-        mc = fmaxf(mc, sv[i]);
-    }
-    mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
-    mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
-    const float m_new = fmaxf(m_run, mc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float sum = 0.f;
-    bf16x8 aop;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float pe = exp2f(sv[i] - m_use);
-        sum += pe;
-        aop[i] = (__bf16)pe;
-    }
-    l_part = l_part * alpha + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        float a = __shfl(alpha, 4 * g4 + q, kWave);
-#pragma unroll
-        for (int p = 0; p < 8; p++)
-            acc[p][q] *= a;
-    }
-#pragma unroll
-    for (int p = 0; p < 8; p++) {
-        const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 b;
-#pragma unroll
-        for (int w = 0; w < 4; w++)
-            b[w] = __builtin_amdgcn_perm(r.v[2 * w + 1][p >> 1], r.v[2 * w][p >> 1], sel);
-        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, b), acc[p], 0, 0, 0);
-    }
-}
-
-constexpr int kTokCap = 8192;
-
-// Exclusive scan of one int per thread over a 512-thread workgroup; (exclusive, total).
-__device__ __forceinline__ int2 block_scan_int_512(int v, int *sh)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(incl, o, kWave);
-        if (lane >= o)
-            incl += t;
-    }
-    if (lane == kWave - 1)
-        sh[w] = incl;
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        int c = sh[i];
-        off += i < w ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    return make_int2(off + incl - v, tot);
-}
-constexpr int kSelCap = 4096;
-
-// grid: (units * h_kv, splits); 256 threads.  unit = query (per-query selection) or sequence (shared).
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t *__restrict__ q,
-                                                           const uint16_t *__restrict__ k,
-                                                           const uint16_t *__restrict__ v,
-                                                           const int32_t *__restrict__ idx,
-                                                           const int32_t *__restrict__ n_idx,
-                                                           uint16_t *__restrict__ out, float *__restrict__ lse,
-                                                           float *__restrict__ part, int n_split)
-{
-    constexpr int KS = D / 32;
-    __shared__ int sh_tok[kTokCap];            // token list; reused for the wave merge
-    __shared__ int sh_sel[kSelCap];            // the unit's selection row
-    __shared__ float sh_m[4][16], sh_l[4][16];
-    const int c = blockIdx.x % P.h_kv;
-    const long long u = blockIdx.x / P.h_kv;
-    const int split = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int rr = lane & 15, g4 = lane >> 4;
-    // the selection row is known from the unit alone: start its loads first
-    const long long row0 = u;                 // query (per-query selection) or sequence (shared)
-    const int32_t *sel_g = idx + ((long long)c * P.rows + row0) * P.topk;
-    const bool sel_in_lds = P.topk <= kSelCap;
-    if (sel_in_lds)
-        for (int x = tid; x < P.topk; x += 256)
-            sh_sel[x] = sel_g[x];
-    int nsel = n_idx[(long long)c * P.rows + row0];
-
-    int b, p_sel, p_max;
-    long long q_first, row;
-    int nq_u;
-    if (P.shared) {
-        b = (int)u;
-        row = b;
-    } else {
-        b = seq_of_query(P, u);
-        row = u;
-    }
-    const Seq s = seq_info(P, b);
-    if (P.shared) {
-        q_first = s.q_off;
-        nq_u = s.n_q;
-        p_sel = s.q0 - 1;
-        p_max = s.q0 + s.n_q - 1;
-    } else {
-        q_first = u;
-        nq_u = 1;
-        p_max = s.q0 + (int)(u - s.q_off);
-        p_sel = p_max;
-    }
-    const int R = nq_u * P.G;                 // <= 16 (checked by the host)
-    (void)row;
-    nsel = nsel < 0 ? 0 : (nsel > P.topk ? P.topk : nsel);
-    __syncthreads();                          // sh_sel complete
-    const int32_t *sel = sel_in_lds ? sh_sel : sel_g;
-    const ASet a = aset_make(P, s.n_k, p_max, p_sel, sel, nsel);
-    const int chunk = (a.total + n_split - 1) / n_split;
-    const int s0 = split * chunk;
-    const int n = max(0, min(a.total, s0 + chunk) - s0);
-    for (int x = tid; x < n; x += 256)
-        sh_tok[x] = aset_token(a, sel, s0 + x);
-
-    // B operand of S^T = K Q^T: lane l holds Q[row l%16][32 ks + 8 (l/16) .. +8]
-    bf16x8 qop[KS];
-    int p_row = -1;
-    if (rr < R) {
-        const long long qi = q_first + rr / P.G;
-        const int h = c * P.G + rr % P.G;
-        const uint16_t *qp = q + (qi * P.h_q + h) * D + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            qop[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
-        p_row = s.q0 + (int)(q_first - s.q_off) + rr / P.G;
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-    __syncthreads();
-
-    const long long tstride = (long long)P.h_kv * D;
-    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
-    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int p = 0; p < 8; p++)
-        acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    ChunkRegs<D> ra, rb;
-    if (32 * w < n)
-        load_chunk<D>(ra, sh_tok, 32 * w, n, kb, vb, tstride, rr, g4, p_row);
-    for (int ch = w; 32 * ch < n; ch += 8) {
-        const int c1 = ch + 4;
-        if (32 * c1 < n)
-            load_chunk<D>(rb, sh_tok, 32 * c1, n, kb, vb, tstride, rr, g4, p_row);
-        compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
-        if (32 * c1 >= n)
-            break;
-        const int c2 = c1 + 4;
-        if (32 * c2 < n)
-            load_chunk<D>(ra, sh_tok, 32 * c2, n, kb, vb, tstride, rr, g4, p_row);
-        compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
-    }
-    float l_row = l_part + __shfl_xor(l_part, 16, kWave);
-    l_row += __shfl_xor(l_row, 32, kWave);
-    __syncthreads();                           // every wave is done with the token list
-    float *sh_o = reinterpret_cast<float *>(sh_tok);    // [4 waves][16 rows][D]
-    if (g4 == 0) {
-        sh_m[w][rr] = m_run;
-        sh_l[w][rr] = l_row;
-    }
-    if (D == 128 || rr < D / 8) {
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-            float *dst = sh_o + (w * 16 + 4 * g4 + qq) * D + 8 * rr;
-#pragma unroll
-            for (int p = 0; p < 8; p++)
-                dst[p] = acc[p][qq];
-        }
-    }
-    __syncthreads();
-    for (int it = tid; it < R * D; it += 256) {
-        const int r = it / D, e = it % D;
-        float M = fmaxf(fmaxf(sh_m[0][r], sh_m[1][r]), fmaxf(sh_m[2][r], sh_m[3][r]));
-        float Ls = 0.f, O = 0.f;
-        if (M > -INFINITY) {
-#pragma unroll
-            for (int ww = 0; ww < 4; ww++) {
-                float f = exp2f(sh_m[ww][r] - M);
-                Ls += sh_l[ww][r] * f;
-                O += sh_o[(ww * 16 + r) * D + e] * f;
-            }
-        }
-        const long long qi = q_first + r / P.G;
-        const int h = c * P.G + r % P.G;
-        if (n_split == 1) {
-            out[(qi * P.h_q + h) * D + e] = f32_to_bf16(O / Ls);
-            if (lse && e == 0)
-                lse[(long long)h * P.total_q + qi] = (M + log2f(Ls)) * 0.69314718055994531f;
-        } else {
-            float *dst = part + ((qi * P.h_q + h) * n_split + split) * (D + 2);
-            dst[e] = O;
-            if (e == 0) {
-                dst[D] = M;
-                dst[D + 1] = Ls;
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------- union tiles (prefill)
 
@@ -938,56 +645,6 @@ hipError_t launch_fwd_tile(const KP &P, const void *q, const void *k, const void
         attn_tile_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, st>>>(
             P, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
             n_qtile);
-    if (ev0 && ev1)
-        (void)hipEventRecord((hipEvent_t)ev1, st);
-    return hipGetLastError();
-}
-
-bool mfma_fwd_ok(const KP &P, int dtype)
-{
-    if (dtype != 1)
-        return false;
-    long long rows = P.shared ? (long long)P.max_q * P.G : P.G;
-    return rows <= 16;
-}
-
-int mfma_fwd_splits(const KP &P)
-{
-    long long a_max = (long long)P.n_init + (long long)P.topk * P.g + P.window + (P.shared ? P.max_q : 0);
-    if (a_max > P.max_k)
-        a_max = P.max_k;
-    long long units = (P.shared ? P.batch : P.total_q) * P.h_kv;
-    long long need = (a_max + kTokCap - 1) / kTokCap;          // the token list must fit in LDS
-    long long fill = (256 + units - 1) / units;                // at least one workgroup per CU
-    long long by_len = (a_max + 255) / 256;                    // >= 2 chunks per wavefront
-    long long sp = fill < by_len ? fill : by_len;
-    if (sp < need)
-        sp = need;
-    if (const char *e = getenv("SPARSE_ATTN_FWD_SPLITS")) {     // tuning override
-        int v = atoi(e);
-        if (v > 0)
-            sp = v > need ? v : need;
-    }
-    if (sp > 64)
-        sp = 64;
-    return sp < 1 ? 1 : (int)sp;
-}
-
-hipError_t launch_fwd_mfma(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,
-                           const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev0, void *ev1,
-                           hipStream_t st)
-{
-    long long units = (P.shared ? P.batch : P.total_q) * P.h_kv;
-    if (ev0 && ev1)
-        (void)hipEventRecord((hipEvent_t)ev0, st);
-    if (P.d == 128)
-        attn_mfma_kernel<128><<<dim3((unsigned)units, (unsigned)splits), dim3(256), 0, st>>>(
-            P, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
-            (float *)ws, splits);
-    else
-        attn_mfma_kernel<64><<<dim3((unsigned)units, (unsigned)splits), dim3(256), 0, st>>>(
-            P, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
-            (float *)ws, splits);
     if (ev0 && ev1)
         (void)hipEventRecord((hipEvent_t)ev1, st);
     return hipGetLastError();

@@ -334,6 +334,9 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
     wg_qk(buf, 0, rr, g4, qop, st[0]);
     wg_qk(buf, 1, rr, g4, qop, st[1]);
     if (partial) {                       // finite sentinel: a dead lane multiplies it by scale 0
+        // keep this a branch: executed unconditionally (as selects) it costs ~100
+        // vector instructions per tile, and it is needed only at set boundaries
+        __asm__ volatile("" ::);
 #pragma unroll
         for (int h = 0; h < 2; h++)
 #pragma unroll
@@ -499,6 +502,8 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     const int wp_first = s.q0 + q_lo + wq_lo, wp_last = wp_first + wq_n - 1;
     const int w_init_hi = wq_n > 0 ? (min(P.n_init, wp_last + 1) + 63) / 64 : 0;
     const int w_win_lo = max(P.n_init, wp_first - P.window + 1) / 64, w_win_hi = wq_n > 0 ? wp_last / 64 : -1;
+    // the wave's rows' window starts span [w_lo_min, w_lo_max]
+    const int w_lo_min = max(P.n_init, wp_first - P.window + 1), w_lo_max = max(P.n_init, wp_last - P.window + 1);
 
     float m_run[2] = {-INFINITY, -INFINITY};
     const float lazy = 8.f / P.scale_log2;
@@ -538,15 +543,30 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
                     const unsigned char *buf = sh_kv[e & 1];
                     uint32_t live[2][2];
                     bool any = false, part = false;
-#pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const int t0 = tile * 64 + 32 * h;
+                    const int t_lo = tile * 64, t_hi = t_lo + 63;
+                    if ((t_lo >= P.n_init && t_hi < w_lo_min) ||
+                        ((t_lo >= w_lo_max || t_hi < P.n_init) && t_hi <= wp_first)) {
+                        // tile wholly before every row's window and past the sinks (live
+                        // where selected), or wholly inside every row's window or sinks
+                        const bool fixed = t_lo < P.n_init || t_lo >= w_lo_max;
 #pragma unroll
                         for (int a = 0; a < 2; a++) {
-                            const bool sb = (qm >> qbit[a]) & 1ull;
-                            live[h][a] = row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
-                            any = any || live[h][a] != 0u;
-                            part = part || (live[h][a] != 0u && live[h][a] != 0xffu);
+                            const bool on = row_ok[a] && (fixed || ((qm >> qbit[a]) & 1ull));
+                            live[0][a] = live[1][a] = on ? 0xffu : 0u;
+                            any = any || on;
+                        }
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < 2; h++) {
+                            const int t0 = t_lo + 32 * h;
+#pragma unroll
+                            for (int a = 0; a < 2; a++) {
+                                const bool sb = (qm >> qbit[a]) & 1ull;
+                                live[h][a] =
+                                    row_ok[a] ? live8(tile_mask(t0, p_row[a], P.n_init, lo_w[a], sb), g4) : 0u;
+                                any = any || live[h][a] != 0u;
+                                part = part || (live[h][a] != 0u && live[h][a] != 0xffu);
+                            }
                         }
                     }
                     if (__ballot(any) != 0ull)

@@ -224,14 +224,15 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
 // MFMA tiles) = 32/G queries x G heads.  The workgroup's tile list is the union
 // of its queries' init tiles, windows and selected blocks (block = tile, g = 64);
 // for each listed tile a 64-bit mask says which of its queries selected it.  The
-// list is walked in lockstep: while tile e is computed from LDS, the loads of
-// tile e + kWgStage are in flight in registers and tile e + 1 is written to the
-// other LDS buffer at the end of the iteration (one barrier per tile).  A
-// wavefront skips the MFMA work of tiles none of its rows attends.
+// list is walked in lockstep, kWgStep tiles per barrier: while step i's tiles are
+// computed from one LDS buffer, step i+1's tiles are written from registers into
+// the other and step i+2's loads are in flight.  Fewer barriers let the
+// wavefronts' uneven per-tile work (a wavefront skips the MFMA work of tiles none
+// of its rows attends) even out within a step.
 constexpr int kWgWaves = 8;
 constexpr int kWgQueries = 64;                 // 8 waves x 8 queries (G = 4)
 constexpr int kWgMaxTiles = 2048;              // 64-token tiles per sequence (max_k <= 131072)
-constexpr int kWgStage = 2;                    // tiles in flight in registers
+constexpr int kWgStep = 2;                     // tiles per barrier step (per LDS buffer)
 constexpr int kWgPitch = 272;                  // LDS bytes per staged 256-byte row (bank spread)
 
 struct WgStage {
@@ -408,10 +409,11 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
                                                          int n_qtile)
 {
     constexpr int D = 128, KS = D / 32;
-    __shared__ unsigned long long sh_qm[kWgMaxTiles];      // per tile: queries that selected it
-    __shared__ int sh_list[kWgMaxTiles];
-    __shared__ unsigned long long sh_lqm[kWgMaxTiles];
-    __shared__ __attribute__((aligned(16))) unsigned char sh_kv[2][128 * kWgPitch];
+    // per tile: queries that selected it; after the list is built, entry i is the mask
+    // of list entry i
+    __shared__ unsigned long long sh_qm[kWgMaxTiles];
+    __shared__ unsigned short sh_list[kWgMaxTiles];
+    __shared__ __attribute__((aligned(16))) unsigned char sh_kv[2][kWgStep * 128 * kWgPitch];
     __shared__ int sh_scan[kWgWaves];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rr = lane & 15, g4 = lane >> 4;
@@ -451,23 +453,29 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     const int p_first = s.q0 + q_lo, p_last = s.q0 + q_lo + nq - 1;
     const int init_hi = (min(P.n_init, p_last + 1) + 63) / 64;
     const int win_lo = max(P.n_init, p_first - P.window + 1) / 64, win_hi = p_last / 64;
+    constexpr int kPer = kWgMaxTiles / 512;               // tiles per thread
     const int per = (ntile + 511) / 512;
+    unsigned long long qv[kPer];
     int cnt = 0;
-    for (int u = 0; u < per; u++) {
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
         const int j = tid * per + u;
-        cnt += (j < ntile && (sh_qm[j] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) ? 1 : 0;
+        qv[u] = u < per && j < ntile ? sh_qm[j] : 0ull;
+        cnt += (u < per && j < ntile && (qv[u] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) ? 1 : 0;
     }
-    int2 sc = block_scan_int_512(cnt, sh_scan);
+    int2 sc = block_scan_int_512(cnt, sh_scan);          // ends with a barrier: every read is done
     int pos = sc.x;
-    for (int u = 0; u < per; u++) {
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
         const int j = tid * per + u;
-        if (j < ntile && (sh_qm[j] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) {
-            sh_list[pos] = j;
-            sh_lqm[pos] = sh_qm[j];
+        if (u < per && j < ntile && (qv[u] != 0ull || j < init_hi || (j >= win_lo && j <= win_hi))) {
+            sh_list[pos] = (unsigned short)j;
+            sh_qm[pos] = qv[u];                          // compacted in place
             pos++;
         }
     }
     const int n_list = sc.y;
+    __syncthreads();                                      // the list is complete
 
     // this wavefront's rows: a = 0, 1 -> rows 16a + rr of its 32
     const long long tstride = (long long)P.h_kv * D;
@@ -514,33 +522,36 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
         for (int p = 0; p < 9; p++)
             acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Tile t lives in register slot t % kWgStage.  Every iteration: barrier (LDS
-    // buffer e&1 holds tile e), compute tile e, write tile e+1 from its slot into
-    // the other buffer, then reuse that slot for tile e+1+kWgStage.  Issues and
-    // writes are unconditional (clamped to the last tile) so the load counters the
-    // compiler tracks are the same on every path.
+    // Step i: barrier (LDS buffer i&1 holds tiles kWgStep*i ..), compute those tiles,
+    // write step i+1's tiles from registers into the other buffer, then issue the
+    // loads of step i+2.  Issues and writes are unconditional (clamped to the last
+    // tile) so the load counters the compiler tracks are the same on every path.
     // Every query attends at least its own position (window >= 1), so n_list >= 1
     // here; the staging below reads sh_list[0 .. n_list) only.
-    WgStage stage[kWgStage];
+    WgStage stage[kWgStep];
     const int last = max(n_list - 1, 0);
+    constexpr int kTileBytes = 128 * kWgPitch;
     if (n_list > 0) {
 #pragma unroll
-        for (int x = 0; x < kWgStage; x++)
+        for (int x = 0; x < kWgStep; x++)
             wg_issue(stage[x], kb, vb, tstride, sh_list[min(x, last)] * 64, s.n_k, tid);
-        wg_write(stage[0], sh_kv[0], tid);
-        wg_issue(stage[0], kb, vb, tstride, sh_list[min(kWgStage, last)] * 64, s.n_k, tid);
-        const int n_iter = ((n_list + kWgStage - 1) / kWgStage) * kWgStage;
-        for (int e0 = 0; e0 < n_iter; e0 += kWgStage) {
 #pragma unroll
-            for (int x = 0; x < kWgStage; x++) {
-                const int e = e0 + x;
-                __syncthreads();                               // LDS buffer e&1 holds tile e
+        for (int x = 0; x < kWgStep; x++) {
+            wg_write(stage[x], sh_kv[0] + x * kTileBytes, tid);
+            wg_issue(stage[x], kb, vb, tstride, sh_list[min(kWgStep + x, last)] * 64, s.n_k, tid);
+        }
+        const int n_step = (n_list + kWgStep - 1) / kWgStep;
+        for (int i = 0; i < n_step; i++) {
+            __syncthreads();                                   // LDS buffer i&1 holds step i's tiles
+#pragma unroll
+            for (int x = 0; x < kWgStep; x++) {
+                const int e = kWgStep * i + x;
                 const int tile = sh_list[min(e, last)];
-                const unsigned long long qm = sh_lqm[min(e, last)];
+                const unsigned long long qm = sh_qm[min(e, last)];
                 const bool need = e < n_list &&
                                   ((qm & wmask) != 0ull || tile < w_init_hi || (tile >= w_win_lo && tile <= w_win_hi));
                 if (need) {
-                    const unsigned char *buf = sh_kv[e & 1];
+                    const unsigned char *buf = sh_kv[i & 1] + x * kTileBytes;
                     uint32_t live[2][2];
                     bool any = false, part = false;
                     const int t_lo = tile * 64, t_hi = t_lo + 63;
@@ -572,9 +583,11 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
                     if (__ballot(any) != 0ull)
                         wg_tile(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, acc);
                 }
-                const int xn = (x + 1) % kWgStage;
-                wg_write(stage[xn], sh_kv[(e + 1) & 1], tid);
-                wg_issue(stage[xn], kb, vb, tstride, sh_list[min(e + 1 + kWgStage, last)] * 64, s.n_k, tid);
+            }
+#pragma unroll
+            for (int x = 0; x < kWgStep; x++) {
+                wg_write(stage[x], sh_kv[(i + 1) & 1] + x * kTileBytes, tid);
+                wg_issue(stage[x], kb, vb, tstride, sh_list[min(kWgStep * (i + 2) + x, last)] * 64, s.n_k, tid);
             }
         }
     }

@@ -815,7 +815,38 @@ __device__ __forceinline__ int2 block_scan_int(int v, int *sh)
 constexpr int kCompactMaxN = 262144;     // candidates per row (bitmap of 8192 words in LDS)
 constexpr int kCompactCap = 4096;        // keys kept for the exact last step
 
+// Calls f(i, key) for every key i in [0, n) of a row whose keys start at element
+// j_lo of a 16-byte aligned row base: 16-byte loads, eight per thread in flight.
+template <int NT, typename F>
+__device__ __forceinline__ void for_each_key(const uint32_t *row, int j_lo, int n, F f)
+{
+    const uint4 *p = reinterpret_cast<const uint4 *>(row);
+    const int q_lo = j_lo >> 2, q_hi = (j_lo + n + 3) >> 2;
+    constexpr int U = 8;
+    for (int q0 = q_lo + (int)threadIdx.x; q0 < q_hi; q0 += NT * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int q = q0 + u * NT;
+            v[u] = q < q_hi ? p[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int q = q0 + u * NT;
+            const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int i = 4 * q + e - j_lo;
+                if (q < q_hi && i >= 0 && i < n)
+                    f(i, e4[e]);
+            }
+        }
+    }
+}
+
 // One 1024-thread workgroup per row, 2048 < candidates <= 262144.
+//  0. for k <= 512: gather the keys >= the k-th largest per-thread maximum (below);
+//     otherwise, or when more than kCompactCap keys pass:
 //  1. histograms of 12, 12 and 8 key bits (most significant first), each restricted to
 //     the prefix chosen so far, until the bin holding the k-th largest key has at most
 //     kCompactCap keys (usually after the first histogram: the selected tail is thin);
@@ -852,72 +883,106 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
             out[s2] = -1;
         return;
     }
-    const uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + r.j_lo;
+    const uint32_t *row_keys = ws + ((long long)c * P.rows + row) * stride;   // 16-byte aligned
+    const uint32_t *keys = row_keys + r.j_lo;
     const int nword = (n + 31) / 32;
     for (int x = tid; x < nword; x += NT)
         bitmap[x] = 0u;
     uint32_t prefix = 0, pmask = 0;
-    int rem = need, cnt_bin = 0;
-    const int shifts[3] = {20, 8, 0};
-    const int widths[3] = {12, 12, 8};
-    for (int level = 0; level < 3; level++) {
-        const int shift = shifts[level], nb = 1 << widths[level];
-        for (int x = tid; x < nb; x += NT)
-            hist[x] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-            uint32_t k = keys[i];
-            if ((k & pmask) == prefix)
-                atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
+    int rem = need;
+    bool gather = false;
+    if (need <= NT / 2) {
+        // Threshold from the per-thread maxima: at least min(n, NT) >= need threads hold
+        // keys, so at least `need` keys are >= t0 = the need-th largest thread maximum
+        // and every selected key is >= t0 (threads without keys keep 0, below every
+        // key).  One pass of maxima, one pass gathering the keys >= t0 (about 0.3% of
+        // the row for need = 512 of 262144) -- no histogram atomics on the crowded
+        // exponent bins.  More than kCompactCap such keys fall back to the histograms.
+        uint32_t mx = 0u;
+        for_each_key<NT>(row_keys, r.j_lo, n, [&](int, uint32_t k) { mx = max(mx, k); });
+        uint32_t t0 = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = t0 | (1u << bit);
+            if (block_scan_int<NT>(mx >= cand ? 1 : 0, sh_scan).y >= need)
+                t0 = cand;
         }
+        if (tid == 0)
+            sh_ncand = 0;
         __syncthreads();
-        // digit holding the rem-th largest key: scan the bins from the top
-        const int per = nb / NT > 0 ? nb / NT : 1;           // bins per thread (4 or 1)
-        int loc = 0;
-        const int b0 = nb - 1 - tid * per;                   // this thread's bins: b0, b0-1, ...
-        for (int q = 0; q < per; q++)
-            if (tid * per + q < nb)
-                loc += hist[b0 - q];
-        int2 sc = block_scan_int<NT>(tid * per < nb ? loc : 0, sh_scan);
-        if (tid * per < nb && sc.x < rem && sc.x + loc >= rem) {
-            int run = sc.x;
-            for (int q = 0; q < per; q++) {
-                int h = hist[b0 - q];
-                if (run + h >= rem) {
-                    sh_digit = b0 - q;
-                    sh_above = run;
-                    break;
+        for_each_key<NT>(row_keys, r.j_lo, n, [&](int i, uint32_t k) {
+            if (k >= t0) {
+                const int slot = atomicAdd(&sh_ncand, 1);
+                if (slot < kCompactCap) {
+                    cand_key[slot] = k;
+                    cand_idx[slot] = i;
                 }
-                run += h;
             }
-        }
+        });
         __syncthreads();
-        const int d = sh_digit;
-        prefix |= ((uint32_t)d) << shift;
-        pmask |= ((uint32_t)(nb - 1)) << shift;
-        rem -= sh_above;
-        cnt_bin = hist[d];
+        gather = sh_ncand <= kCompactCap;
         __syncthreads();
-        if (cnt_bin <= kCompactCap)
-            break;
     }
-    // mark keys above the bin, gather the bin
-    if (tid == 0)
-        sh_ncand = 0;
-    __syncthreads();
-    const uint32_t top_of_bin = prefix | ~pmask;
-    const bool gather = cnt_bin <= kCompactCap;
-    for (int i = tid; i < n; i += NT) {
-        uint32_t k = keys[i];
-        if (k > top_of_bin) {
-            atomicOr(&bitmap[i >> 5], 1u << (i & 31));
-        } else if (gather && (k & pmask) == prefix) {
-            int slot = atomicAdd(&sh_ncand, 1);
-            cand_key[slot] = k;
-            cand_idx[slot] = i;
+    if (!gather) {
+        int cnt_bin = 0;
+        const int shifts[3] = {20, 8, 0};
+        const int widths[3] = {12, 12, 8};
+        for (int level = 0; level < 3; level++) {
+            const int shift = shifts[level], nb = 1 << widths[level];
+            for (int x = tid; x < nb; x += NT)
+                hist[x] = 0;
+            __syncthreads();
+            for_each_key<NT>(row_keys, r.j_lo, n, [&](int, uint32_t k) {
+                if ((k & pmask) == prefix)
+                    atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
+            });
+            __syncthreads();
+            // digit holding the rem-th largest key: scan the bins from the top
+            const int per = nb / NT > 0 ? nb / NT : 1;           // bins per thread (4 or 1)
+            int loc = 0;
+            const int b0 = nb - 1 - tid * per;                   // this thread's bins: b0, b0-1, ...
+            for (int q = 0; q < per; q++)
+                if (tid * per + q < nb)
+                    loc += hist[b0 - q];
+            int2 sc = block_scan_int<NT>(tid * per < nb ? loc : 0, sh_scan);
+            if (tid * per < nb && sc.x < rem && sc.x + loc >= rem) {
+                int run = sc.x;
+                for (int q = 0; q < per; q++) {
+                    int h = hist[b0 - q];
+                    if (run + h >= rem) {
+                        sh_digit = b0 - q;
+                        sh_above = run;
+                        break;
+                    }
+                    run += h;
+                }
+            }
+            __syncthreads();
+            const int d = sh_digit;
+            prefix |= ((uint32_t)d) << shift;
+            pmask |= ((uint32_t)(nb - 1)) << shift;
+            rem -= sh_above;
+            cnt_bin = hist[d];
+            __syncthreads();
+            if (cnt_bin <= kCompactCap)
+                break;
         }
+        // mark keys above the bin, gather the bin
+        if (tid == 0)
+            sh_ncand = 0;
+        __syncthreads();
+        const uint32_t top_of_bin = prefix | ~pmask;
+        gather = cnt_bin <= kCompactCap;
+        for_each_key<NT>(row_keys, r.j_lo, n, [&](int i, uint32_t k) {
+            if (k > top_of_bin) {
+                atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+            } else if (gather && (k & pmask) == prefix) {
+                int slot = atomicAdd(&sh_ncand, 1);
+                cand_key[slot] = k;
+                cand_idx[slot] = i;
+            }
+        });
+        __syncthreads();
     }
-    __syncthreads();
     if (gather) {
         // exact pick of rem among the gathered keys: tau = rem-th largest key
         const int nc = sh_ncand;
@@ -1032,11 +1097,16 @@ static constexpr int kWaveTopkMax = 2048;
 static constexpr int kRowMaxCand = 1024;
 static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (8 rounds of 64)
 
+// Candidate capacity of a row, and the row stride of the score-key workspace (a
+// multiple of 4, so every row starts 16-byte aligned).
+static long long cand_cap(const KP &P) { return P.g == 1 ? P.max_k : P.nb_max; }
+static long long key_stride(const KP &P) { return (cand_cap(P) + 3) / 4 * 4; }
+
 size_t select_workspace_bytes(const KP &P, int plan)
 {
     if (plan == kSelectEmpty)
         return 0;
-    long long stride = P.g == 1 ? P.max_k : P.nb_max;
+    const long long stride = plan == kSelectRow ? cand_cap(P) : key_stride(P);
     if (plan == kSelectRow) {                             // (key, position) survivors of every part
         const long long n_part = (stride + kPartCand - 1) / kPartCand;
         return (size_t)P.h_kv * (size_t)P.rows * (size_t)n_part * (size_t)part_cap(P.topk) * 2 * sizeof(uint32_t);
@@ -1065,7 +1135,7 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
 {
     const T *q = (const T *)q_sel;
     int plan = select_plan(P);
-    long long stride = P.g == 1 ? P.max_k : P.nb_max;
+    const long long stride = plan == kSelectRow ? cand_cap(P) : key_stride(P);
     uint32_t *wsk = (uint32_t *)ws;
     if (plan == kSelectEmpty) {
         long long n = P.rows * P.h_kv;

@@ -614,12 +614,52 @@ __device__ __forceinline__ float4 ld4f(const uint16_t *p)
 // Prefill rows (one per query).  grid: (column chunks of kColTiles x 64 candidates,
 // row tiles of 64, h_kv * batch).  4 wavefronts in 2 x 2, each a 32 x 32 block of
 // 2 x 2 MFMA 16x16x4 f32 tiles.  The selector-query operands (the group's heads
-// summed in fp32) are built once per workgroup and stay in registers; each
-// column tile's key operands are loaded straight from memory as float4 per lane
-// (lane l: key row l%16, head-dim elements 16k + 4(l/16) .. +4, which is the
-// MFMA k index l/16 of the four steps s = 0..3) while the previous tile computes.
-// The head dimension is contracted in the order (k, s, l/16); fp32 products and sums.
+// summed in fp32) are built once per workgroup and stay in registers.  Key tiles
+// (64 candidate rows) go through a two-buffer LDS ring shared by the four
+// wavefronts: while tile t is computed from LDS, tile t+1 is written from
+// registers into the other buffer and the loads of tile t+2 are in flight (one
+// barrier per tile).  Operand lane l reads key row l%16, head-dim elements
+// 16k + 4(l/16) .. +4 (the MFMA k index l/16 of the four steps s = 0..3).  The head
+// dimension is contracted in the order (k, s, l/16); fp32 products and sums.
 constexpr int kColTiles = 16;
+
+__device__ __forceinline__ float4 lds4f(const unsigned char *p, float) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 lds4f(const unsigned char *p, uint16_t)
+{
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+}
+
+// A thread's share of one staged 64-row key tile (pieces tid + 256 u, 16 bytes each);
+// a native vector type, so the copies stay in registers.
+typedef uint32_t kv4u __attribute__((ext_vector_type(4)));
+template <int N>
+struct KeyStage {
+    kv4u c[N];
+};
+
+template <int N, int kRowBytes>
+__device__ __forceinline__ void key_issue(KeyStage<N> &st, const unsigned char *base, long long row_stride, int jt,
+                                          int j_end, int tid)
+{
+#pragma unroll
+    for (int u = 0; u < N; u++) {
+        const int piece = tid + 256 * u, row = piece / (kRowBytes / 16), col = piece % (kRowBytes / 16);
+        const int j = min(jt + row, j_end - 1);          // rows past the end re-read the last one
+        st.c[u] = *reinterpret_cast<const kv4u *>(base + (long long)j * row_stride + 16 * col);
+    }
+}
+
+template <int N, int kRowBytes, int kPitch>
+__device__ __forceinline__ void key_write(const KeyStage<N> &st, unsigned char *buf, int tid)
+{
+#pragma unroll
+    for (int u = 0; u < N; u++) {
+        const int piece = tid + 256 * u, row = piece / (kRowBytes / 16), col = piece % (kRowBytes / 16);
+        *reinterpret_cast<kv4u *>(buf + row * kPitch + 16 * col) = st.c[u];
+    }
+}
 
 template <typename T, typename KT, int D>
 __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__restrict__ q,
@@ -627,6 +667,10 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
                                                             uint32_t *__restrict__ ws, long long stride)
 {
     constexpr int KG = D / 16;
+    constexpr int kRowBytes = D * (int)sizeof(KT);       // one candidate key row
+    constexpr int kPitch = kRowBytes + 16;               // LDS row pitch: 16 rows hit 16 bank groups
+    constexpr int kChunks = 64 * kRowBytes / 16 / 256;   // 16-byte pieces per thread per tile
+    __shared__ __attribute__((aligned(16))) unsigned char sh_k[2][64 * kPitch];
     const int b = blockIdx.z % P.batch, c = blockIdx.z / P.batch;
     const Seq s = seq_info(P, b);
     const int r0 = blockIdx.y * 64;
@@ -667,12 +711,6 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
             }
         }
     }
-    auto key_ptr = [&](int j) -> const KT * {
-        j = min(j, jhi_last - 1);
-        if (P.g == 1)
-            return kbase + ((s.k_off + j) * P.h_kv + c) * D;
-        return kbase + (((long long)c * P.batch + b) * P.nb_max + j) * D;
-    };
     // candidate upper bound of each output row this lane writes (rows are fixed per workgroup);
     // the lower bound n_init / g is the same for every row that has candidates
     int jh_row[2][4];
@@ -687,17 +725,13 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
             jh_row[a][i] = jh > jl ? min(jh, (int)stride) : 0;
         }
     const int j_first = P.n_init / P.g;
-    float4 ka[2][KG], kb[2][KG];
-    auto load_keys = [&](float4 (&kk)[2][KG], int jt) {
-#pragma unroll
-        for (int bb = 0; bb < 2; bb++) {
-            const KT *kp = key_ptr(jt + wc + 16 * bb + li) + 4 * lk;
-#pragma unroll
-            for (int k = 0; k < KG; k++)
-                kk[bb][k] = ld4f(kp + 16 * k);
-        }
-    };
-    auto tile = [&](const float4 (&kk)[2][KG], int jt) {
+    // staging: thread tid holds pieces tid + 256 u of the tile (row = piece / pieces per row)
+    const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(kbase);
+    const long long row_stride = P.g == 1 ? (long long)P.h_kv * kRowBytes : kRowBytes;
+    const long long base_off = P.g == 1 ? ((long long)s.k_off * P.h_kv + c) * kRowBytes
+                                        : (((long long)c * P.batch + b) * P.nb_max) * kRowBytes;
+    const unsigned char *kb0 = kbytes + base_off;
+    auto tile = [&](const unsigned char *buf, int jt) {
         floatx4 acc[2][2];
 #pragma unroll
         for (int a = 0; a < 2; a++)
@@ -706,10 +740,17 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
                 acc[a][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KG; k++) {
+            float bv[2][4];
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++) {
+                const float4 x = lds4f(buf + (wc + 16 * bb + li) * kPitch + (16 * k + 4 * lk) * (int)sizeof(KT), KT{});
+                bv[bb][0] = x.x;
+                bv[bb][1] = x.y;
+                bv[bb][2] = x.z;
+                bv[bb][3] = x.w;
+            }
             const float av[2][4] = {{qa[0][k].x, qa[0][k].y, qa[0][k].z, qa[0][k].w},
                                     {qa[1][k].x, qa[1][k].y, qa[1][k].z, qa[1][k].w}};
-            const float bv[2][4] = {{kk[0][k].x, kk[0][k].y, kk[0][k].z, kk[0][k].w},
-                                    {kk[1][k].x, kk[1][k].y, kk[1][k].z, kk[1][k].w}};
 #pragma unroll
             for (int st = 0; st < 4; st++)
 #pragma unroll
@@ -734,17 +775,16 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
             }
         }
     };
-    load_keys(ka, jc0);
-    for (int jt = jc0; jt < jc1; jt += 128) {
-        const int jn = jt + 64;
-        if (jn < jc1)
-            load_keys(kb, jn);
-        tile(ka, jt);
-        if (jn >= jc1)
-            break;
-        if (jn + 64 < jc1)
-            load_keys(ka, jn + 64);
-        tile(kb, jn);
+    const int n_t = (jc1 - jc0 + 63) / 64;
+    KeyStage<kChunks> stage;
+    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0, jhi_last, tid);
+    key_write<kChunks, kRowBytes, kPitch>(stage, sh_k[0], tid);
+    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0 + 64, jhi_last, tid);   // past the end: reloads
+    for (int t = 0; t < n_t; t++) {
+        __syncthreads();                                  // buffer t&1 holds tile t
+        tile(sh_k[t & 1], jc0 + 64 * t);
+        key_write<kChunks, kRowBytes, kPitch>(stage, sh_k[(t + 1) & 1], tid);
+        key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0 + 64 * (t + 2), jhi_last, tid);
     }
 }
 

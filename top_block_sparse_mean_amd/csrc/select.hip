@@ -885,7 +885,8 @@ __device__ __forceinline__ void for_each_key(const uint32_t *row, int j_lo, int 
 }
 
 // One 1024-thread workgroup per row, 2048 < candidates <= 262144.
-//  0. for k <= 512: gather the keys >= the k-th largest per-thread maximum (below);
+//  0. for k <= 512 and rows of >= 65536 keys: gather the keys >= the k-th largest
+//     per-thread maximum (below);
 //     otherwise, or when more than kCompactCap keys pass:
 //  1. histograms of 12, 12 and 8 key bits (most significant first), each restricted to
 //     the prefix chosen so far, until the bin holding the k-th largest key has at most
@@ -931,8 +932,9 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
     uint32_t prefix = 0, pmask = 0;
     int rem = need;
     bool gather = false;
-    if (need <= NT / 2) {
-        // Threshold from the per-thread maxima: at least min(n, NT) >= need threads hold
+    if (need <= NT / 2 && n >= 65536) {
+        // Long rows (its 32 block-wide counting rounds cost more than a histogram on
+        // short ones).  Threshold from the per-thread maxima: at least min(n, NT) >= need threads hold
         // keys, so at least `need` keys are >= t0 = the need-th largest thread maximum
         // and every selected key is >= t0 (threads without keys keep 0, below every
         // key).  One pass of maxima, one pass gathering the keys >= t0 (about 0.3% of

@@ -23,6 +23,8 @@
 // in ascending index order by ballot compaction.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
@@ -611,7 +613,7 @@ __device__ __forceinline__ float4 ld4f(const uint16_t *p)
                        __uint_as_float(u.y & 0xffff0000u));
 }
 
-// Prefill rows (one per query).  grid: (column chunks of kColTiles x 64 candidates,
+// Prefill rows (one per query).  grid: (column chunks of col_tiles x 64 candidates,
 // row tiles of 64, h_kv * batch).  4 wavefronts in 2 x 2, each a 32 x 32 block of
 // 2 x 2 MFMA 16x16x4 f32 tiles.  The selector-query operands (the group's heads
 // summed in fp32) are built once per workgroup and stay in registers.  Key tiles
@@ -621,7 +623,15 @@ __device__ __forceinline__ float4 ld4f(const uint16_t *p)
 // barrier per tile).  Operand lane l reads key row l%16, head-dim elements
 // 16k + 4(l/16) .. +4 (the MFMA k index l/16 of the four steps s = 0..3).  The head
 // dimension is contracted in the order (k, s, l/16); fp32 products and sums.
-constexpr int kColTiles = 16;
+// Column tiles per workgroup: at least 16, more when there are few row tiles (long
+// rows, few queries), so each workgroup builds its selector operands for more work
+// while the grid still holds >= 2048 workgroups.
+static int score_col_tiles(long long stride, long long row_tiles)
+{
+    const long long n_tiles = (stride + 63) / 64;
+    const long long chunks = std::max(1LL, 2048 / std::max(1LL, row_tiles));
+    return (int)std::max(16LL, (n_tiles + chunks - 1) / chunks);
+}
 
 __device__ __forceinline__ float4 lds4f(const unsigned char *p, float) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ float4 lds4f(const unsigned char *p, uint16_t)
@@ -664,7 +674,8 @@ __device__ __forceinline__ void key_write(const KeyStage<N> &st, unsigned char *
 template <typename T, typename KT, int D>
 __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__restrict__ q,
                                                             const KT *__restrict__ kbase,
-                                                            uint32_t *__restrict__ ws, long long stride)
+                                                            uint32_t *__restrict__ ws, long long stride,
+                                                            int col_tiles)
 {
     constexpr int KG = D / 16;
     constexpr int kRowBytes = D * (int)sizeof(KT);       // one candidate key row
@@ -680,10 +691,10 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
     int jlo_last, jhi_last;
     cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
     jhi_last = min(jhi_last, (int)stride);
-    const int jc0 = jlo_last + blockIdx.x * kColTiles * 64;
+    const int jc0 = jlo_last + blockIdx.x * col_tiles * 64;
     if (jc0 >= jhi_last)
         return;
-    const int jc1 = min(jc0 + kColTiles * 64, jhi_last);
+    const int jc1 = min(jc0 + col_tiles * 64, jhi_last);
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int li = lane % 16, lk = lane / 16;
     const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
@@ -1221,12 +1232,14 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             score_rows_kernel<T, float, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride,
                                                                                   n_chunk);
     } else {
-        dim3 grid((unsigned)((stride + kColTiles * 64 - 1) / (kColTiles * 64)), (unsigned)((P.max_q + 63) / 64),
+        const long long row_tiles = (long long)((P.max_q + 63) / 64) * P.h_kv * P.batch;
+        const int col_tiles = score_col_tiles(stride, row_tiles);
+        dim3 grid((unsigned)((stride + col_tiles * 64 - 1) / (col_tiles * 64)), (unsigned)((P.max_q + 63) / 64),
                   (unsigned)(P.h_kv * P.batch));
         if (P.g == 1)
-            score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride);
+            score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, col_tiles);
         else
-            score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride);
+            score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride, col_tiles);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

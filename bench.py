@@ -24,11 +24,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 import top_block_sparse_mean_amd as sa  # noqa: E402
-from workloads import DTYPE_BF16, FULL, generate, hot_blocks  # noqa: E402
+from workloads import DTYPE_BF16, FULL, generate, hot_blocks, needle_groups  # noqa: E402
 
 METRIC = "sparse-attn prefill tok/s + decode µs/step; % HBM GB/s / % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 DECODE = ("bf16_decode_32k", "bf16_draft_decode")
 
 
@@ -49,16 +50,17 @@ class TimingEvents:
 
     DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def __init__(self, n):
+    def __init__(self, n, width=2):
         path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
         self.hip = ctypes.CDLL(path)
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.pairs = []
         for _ in range(n):
             pair = []
-            for _ in range(2):
+            for _ in range(width):
                 ev = ctypes.c_void_p()
                 rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
                 if rc != 0:
@@ -66,15 +68,21 @@ class TimingEvents:
                 pair.append(ev.value)
             self.pairs.append(tuple(pair))
 
-    def mean_ms(self):
-        tot = 0.0
-        for a, b in self.pairs:
-            ms = ctypes.c_float()
-            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
-            if rc != 0:
-                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-            tot += ms.value
-        return tot / len(self.pairs)
+    def record(self, ev):
+        rc = self.hip.hipEventRecord(ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def mean_ms(self, i=0, j=1):
+        """Mean over the recorded sets of the time from event i to event j."""
+        return sum(self.elapsed_ms(evs[i], evs[j]) for evs in self.pairs) / len(self.pairs)
 
     def close(self):
         for pair in self.pairs:
@@ -101,16 +109,23 @@ class Step:
         if self.k_cmp is not None and self.decode:
             sa.compress(self.p, x["k"], self.k_cmp)       # the cache's pooled keys, built before decoding
 
-    def __call__(self, events=None):
+    def __call__(self, events=None, stages=None):
+        """stages: (TimingEvents, four events) recorded before compress, after compress,
+        after select and after fwd."""
         x = self.x
+        mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
+        mark(0)
         if self.k_cmp is not None:
             if self.decode:
                 sa.compress_tail(self.p, 1, x["k"], self.k_cmp)
             else:
                 sa.compress(self.p, x["k"], self.k_cmp)
+        mark(1)
         sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
+        mark(2)
         sa.fwd(self.p, x["q"], x["k"], x["v"], self.idx, self.n_idx, out=self.out, ws=self.ws_fwd,
                events=events)
+        mark(3)
 
 
 def attended_total_exact(w, idx_host, n_idx_host, per_unit=False):
@@ -144,6 +159,100 @@ def attended_total_exact(w, idx_host, n_idx_host, per_unit=False):
             tot += int(a.max()) if (per_unit and w.shared_selection and len(a)) else int(a.sum())
         qi += nq
     return tot
+
+
+def measured_peaks(device, prefill):
+    """Achievable rates on this GPU, measured beside the published peaks: a 1 GiB
+    device-to-device copy (GB/s, bytes read + written) and, for prefill workloads,
+    8192^3 library GEMMs in bf16 and fp32 (TFLOP/s)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    out = {}
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    out["copy_gbs"] = round(2 * n * 4 / timed(lambda: dst.copy_(src), 20) / 1e9, 1)
+    del src, dst
+    if prefill:
+        m = 8192
+        for name, dt in (("bf16_gemm_tflops", torch.bfloat16), ("fp32_gemm_tflops", torch.float32)):
+            a = torch.randn(m, m, device=device).to(dt)
+            bm = torch.randn(m, m, device=device).to(dt)
+            c = torch.empty(m, m, device=device, dtype=dt)
+            out[name] = round(2.0 * m ** 3 / timed(lambda: torch.mm(a, bm, out=c), 5) / 1e12, 1)
+            del a, bm, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks):
+    """Each stage of one step against its own bound, on algorithmic work.
+    compress: keys read once + pooled keys written (HBM).  select: decode reads the
+    pooled keys (or, with g = 1, the raw keys) once per step (HBM); prefill scores every
+    causally visible block of every row per KV head (2 d flop each, fp32 MFMA).  fwd:
+    the attention kernel's own figure (bytes for decode, useful flops for prefill)."""
+    d, g = w.head_dim, w.block
+    elt = 2 if w.dtype == DTYPE_BF16 else 4
+    decode = w.name in DECODE
+    nb = [-(-nk // g) for nk in w.seqlens_k]
+    rep = {}
+
+    def add(name, ms, amount, bound):
+        r = {"ms": round(ms, 5), "bound": bound}
+        if amount is not None and ms > 0:
+            if bound == "hbm":
+                r.update(achieved=round(amount / (ms * 1e-3) / 1e9, 1), unit="GB/s",
+                         frac=round(amount / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         frac_of_measured=round(amount / (ms * 1e-3) / 1e9 / peaks["copy_gbs"], 4))
+            else:
+                peak, mkey = (FP32_PEAK_TFLOPS, "fp32_gemm_tflops") if bound == "mfma_fp32" else \
+                             (BF16_PEAK_TFLOPS, "bf16_gemm_tflops")
+                ach = amount / (ms * 1e-3) / 1e12
+                r.update(achieved=round(ach, 2), unit="TFLOP/s", frac=round(ach / peak, 4))
+                if mkey in peaks:
+                    r["frac_of_measured"] = round(ach / peaks[mkey], 4)
+        rep[name] = r
+
+    if g > 1 and decode:
+        # newest block of every sequence re-pooled: launch-bound, no roofline figure
+        add("compress", stage_ms[0], None, "launch")
+    elif g > 1:
+        add("compress", stage_ms[0], w.total_k * w.h_kv * d * elt + w.h_kv * sum(nb) * d * 4, "hbm")
+    if decode:
+        sel_bytes = (w.h_kv * sum(nb) * d * 4) if g > 1 else (w.h_kv * w.total_k * d * elt)
+        add("select", stage_ms[1], sel_bytes + w.total_q * w.h_q * d * elt, "hbm")
+        add("fwd", stage_ms[2], attn_bytes, "hbm")
+    else:
+        cand = 0
+        for nk, nq in zip(w.seqlens_k, w.seqlens_q):
+            p = range(nk - nq, nk)
+            cand += sum(q // g + 1 for q in p)
+        add("select", stage_ms[1], 2.0 * d * w.h_kv * cand, "mfma_fp32")
+        add("fwd", stage_ms[2], attn_flops, "mfma_bf16" if w.dtype == DTYPE_BF16 else "mfma_fp32")
+    return rep
+
+
+def needle_recall(w, idx_host, n_idx_host):
+    """Fraction of the chunk's query rows in segment i whose selected groups hold needle
+    group i, averaged over the planted needles (KV head 0)."""
+    groups = needle_groups(w, 0)
+    if not groups:
+        return None
+    fr = []
+    for i, jg in enumerate(groups):
+        r0, r1 = i * w.needle_segment, min((i + 1) * w.needle_segment, w.seqlens_q[0])
+        hit = sum(1 for r in range(r0, r1) if jg in set(idx_host[0, r, :n_idx_host[0, r]].tolist()))
+        fr.append(hit / (r1 - r0))
+    return round(sum(fr) / len(fr), 4)
 
 
 # Dominant kernel of each workload and the sources it is built from: a counter record
@@ -227,52 +336,88 @@ def record_counters(workload, fetch_dir, write_dir, commands):
     print(path)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, x, seconds=10.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload, timed stage by
+    stage (compress, select, attend) on the host cores."""
     import numpy as np
 
     import oracle
     oracle.lib()
-    nb = 2 if w.name in DECODE else 1
-    if w.name == "bf16_decode_32k":
-        sub = w.scaled(seqlens_k=w.seqlens_k[:nb], seqlens_q=w.seqlens_q[:nb])
+    clock = time.perf_counter
+    if w.name in DECODE:
+        nb = 2 if w.name == "bf16_decode_32k" else 4
+        sub = w.scaled(seqlens_k=w.seqlens_k[:nb], seqlens_q=w.seqlens_q[:nb],
+                       topk_per_seq=w.topk_per_seq[:nb] if w.topk_per_seq else w.topk_per_seq)
         xs = {k: x[k][:sum(sub.seqlens_q if k == "q" else sub.seqlens_k)].cpu().contiguous()
               for k in ("q", "k", "v")}
-        kc = oracle.compress(sub, xs["k"])
-        reps, t0 = 0, time.perf_counter()
-        while True:
+        t = clock()
+        kc = oracle.compress(sub, xs["k"]) if w.block > 1 else None
+        t_cmp = clock() - t
+        reps, t_sel, t_att = 0, 0.0, 0.0
+        while t_sel + t_att < seconds:
+            t = clock()
             sel = oracle.select(sub, xs["q"], kc, xs["k"])
             idx, n = oracle.table(sub, sel)
+            t2 = clock()
             oracle.attend(sub, xs["q"], xs["k"], xs["v"], idx, n)
+            t_sel += t2 - t
+            t_att += clock() - t2
             reps += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        per_seq_s = (time.perf_counter() - t0) / reps / nb
-        return dict(value=per_seq_s * w.batch * 1e6, unit="µs/step", cores=oracle.num_threads(),
-                    kind="oracle",
-                    sample=f"select + attend of {nb} of {w.batch} sequences (all 8 KV heads, 32 query heads), "
-                           f"{reps} repetitions, pooled keys precomputed; scaled x{w.batch // nb} to one step")
-    # prefill workloads: a contiguous sample of query rows, scaled to the whole chunk
-    kc = oracle.compress(w, x["k"].cpu()) if w.block > 1 else None
+        # the work of a sequence grows with its cached length: scale by cached tokens
+        grow = w.total_k / sub.total_k
+        scale = grow / reps
+        stages = {"select": round(t_sel * scale * 1e6, 1), "attend": round(t_att * scale * 1e6, 1)}
+        if kc is not None:
+            stages["compress_whole_cache"] = round(t_cmp * grow * 1e6, 1)
+        return dict(value=(t_sel + t_att) * scale * 1e6, unit="µs/step", cores=oracle.num_threads(),
+                    kind="oracle", cpu_model=cpu_model(), stages_us=stages,
+                    sample=f"select + attend of the first {nb} of {w.batch} sequences (all {w.h_kv} KV heads, "
+                           f"{w.h_q} query heads), {reps} repetitions, scaled x{grow:.1f} by cached tokens to "
+                           f"one step" + ("; the step's re-pooling of one block per sequence is not timed (the "
+                                          "whole cache's pooling is shown apart)" if kc is not None else ""))
+    # prefill workloads: the whole compress, then random query rows, scaled to the whole chunk
     xs = {k: x[k].cpu().contiguous() for k in ("q", "k", "v")}
+    t_cmp = 0.0
+    kc = None
+    if w.block > 1:
+        t = clock()
+        kc = oracle.compress(w, xs["k"])
+        t_cmp = clock() - t
     rng = np.random.default_rng(0)
-    n_rows = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
+    n_rows, t_sel, t_att = 0, 0.0, 0.0
+    while t_sel + t_att < seconds:
         rows = rng.integers(0, w.rows, size=8)
+        t = clock()
         sel = oracle.select(w, xs["q"], kc, xs["k"], rows=np.repeat(rows, w.h_kv),
                             heads=np.tile(np.arange(w.h_kv), 8))
         idx = np.full((w.h_kv, w.rows, sel["idx"].shape[1]), -1, dtype=np.int32)
         n = np.zeros((w.h_kv, w.rows), dtype=np.int32)
         idx[sel["heads"], sel["rows"]] = sel["idx"]
         n[sel["heads"], sel["rows"]] = sel["n"]
+        t2 = clock()
         reqs = np.repeat(rows, w.h_q)
         oracle.attend(w, xs["q"], xs["k"], xs["v"], idx, n, reqs=reqs, heads=np.tile(np.arange(w.h_q), 8))
+        t_sel += t2 - t
+        t_att += clock() - t2
         n_rows += 8
-    el = time.perf_counter() - t0
-    tok_s = n_rows / el
-    return dict(value=tok_s, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"select + attend of {n_rows} random query rows (all heads), pooled keys precomputed")
+    scale = w.total_q / n_rows
+    total_s = t_cmp + (t_sel + t_att) * scale
+    return dict(value=w.total_q / total_s, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                cpu_model=cpu_model(),
+                stages_s={"compress": round(t_cmp, 3), "select": round(t_sel * scale, 3),
+                          "attend": round(t_att * scale, 3)},
+                sample=f"the whole compress once, then select + attend of {n_rows} random query rows "
+                       f"(all heads), scaled x{scale:.1f} to the chunk")
 
 
 def main():
@@ -336,6 +481,16 @@ def main():
     attn_ms = tev.mean_ms()
     tev.close()
 
+    # per-stage times, from events recorded between the three calls, in a pass of its own
+    n_st = min(args.steps, 20)
+    sev = TimingEvents(n_st, width=4)
+    for i in range(n_st):
+        step(stages=(sev, sev.pairs[i]))
+    torch.cuda.synchronize()
+    stage_ms = [sev.mean_ms(0, 1), sev.mean_ms(1, 2), sev.mean_ms(2, 3)]
+    sev.close()
+    peaks = measured_peaks(device, prefill=w.name not in DECODE)
+
     idx_h, n_h = step.idx.cpu().numpy(), step.n_idx.cpu().numpy()
     a_tot = attended_total_exact(w, idx_h, n_h)
     d = w.head_dim
@@ -347,13 +502,19 @@ def main():
         roof = dict(bound="hbm", achieved=round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s")
         roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
+        roof["measured_peak"] = peaks["copy_gbs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / peaks["copy_gbs"], 4)
         value, unit, hib = ms_step * 1e3, "µs/step", False
+        flops = None
     else:
         G = w.group
         flops = 4.0 * d * a_tot * G
         roof = dict(bound="mfma", achieved=round(flops / (attn_ms * 1e-3) / 1e12, 2), peak=BF16_PEAK_TFLOPS,
                     unit="TFLOP/s")
         roof["frac"] = round(roof["achieved"] / BF16_PEAK_TFLOPS, 4)
+        if w.dtype == DTYPE_BF16:
+            roof["measured_peak"] = peaks["bf16_gemm_tflops"]
+            roof["frac_of_measured"] = round(roof["achieved"] / peaks["bf16_gemm_tflops"], 4)
         value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
         attn_bytes = None
     roof["traffic"] = measured_traffic(w.name)
@@ -368,6 +529,12 @@ def main():
                 hits += sum(1 for j in hb if j in sel)
                 tot += len(hb)
         extra["hot_block_recall"] = round(hits / max(tot, 1), 4)
+    if w.structure == "needles":
+        extra["needle_recall"] = needle_recall(w, idx_h, n_h)
+    if w.name == "bf16_draft_decode":
+        extra["us_per_draft_token"] = round(ms_step * 1e3 / w.seqlens_q[0], 3)
+    extra["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks)
+    extra["measured_peaks"] = peaks
 
     res = {
         "metric": METRIC,

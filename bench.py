@@ -2,12 +2,14 @@
 
 Default workload: bf16 decode, 32 sequences x 32768 cached tokens, Hq 32 / Hkv 8,
 d 128, g 64, top-32 blocks + 1 init block + 128-token window.  One step is the
-whole path for one decode token per sequence: re-pool the newest block of every
-sequence (sparse_attn_compress_tail), select (sparse_attn_select) and attend
-(sparse_attn_fwd).  Inputs are synthetic and already resident in HBM.
+whole path for one decode token per sequence: append its key and value to the
+cache and re-pool the block it falls in (sparse_attn_append_kv), select
+(sparse_attn_select) and attend (sparse_attn_fwd).  Inputs are synthetic and
+already resident in HBM.
 
 Prints one JSON line.  ``--workload`` runs one of the other synthetic workloads
-instead (prefill workloads report tok/s).
+instead (prefill workloads report tok/s); ``--page-size`` keeps K and V in a
+paged cache.
 """
 from __future__ import annotations
 
@@ -24,7 +26,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 import top_block_sparse_mean_amd as sa  # noqa: E402
-from workloads import DTYPE_BF16, FULL, generate, hot_blocks, needle_groups  # noqa: E402
+from workloads import (DTYPE_BF16, FULL, from_pages, generate, hot_blocks, needle_groups,  # noqa: E402
+                       page_layout, to_pages)
 
 METRIC = "sparse-attn prefill tok/s + decode µs/step; % HBM GB/s / % MFMA peak"
 HBM_PEAK_GBS = 8000.0
@@ -33,12 +36,14 @@ FP32_PEAK_TFLOPS = 157.3
 DECODE = ("bf16_decode_32k", "bf16_draft_decode")
 
 
-def make_params(w, device):
+def make_params(w, device, layout=None):
     dt = torch.bfloat16 if w.dtype == DTYPE_BF16 else torch.float32
     return sa.Params.from_lengths(w.seqlens_q, w.seqlens_k, device=device, h_q=w.h_q, h_kv=w.h_kv,
                                   head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk,
                                   n_init=w.n_init, window=w.window, shared_selection=w.shared_selection,
-                                  topk_per_seq=w.topk_per_seq, dtype=dt)
+                                  topk_per_seq=w.topk_per_seq, dtype=dt,
+                                  block_table=None if layout is None else layout.block_table.to(device),
+                                  page_size=0 if layout is None else layout.page_size)
 
 
 class TimingEvents:
@@ -92,11 +97,20 @@ class TimingEvents:
 
 
 class Step:
-    """Preallocated buffers and the three ABI calls of one pass."""
+    """Preallocated buffers and the ABI calls of one pass.  Prefill: compress, select,
+    fwd.  Decode (one token per sequence) and draft rounds (the drafts of every
+    sequence): append the new tokens' keys and values to the cache, which re-pools
+    the blocks they fall in, then select and fwd.  The cache already holds those
+    tokens, so every step rewrites the same values.  page_size > 0 keeps K and V in
+    a paged cache read through a block table."""
 
-    def __init__(self, w, x, device):
-        self.w, self.x = w, x
-        self.p = make_params(w, device)
+    def __init__(self, w, x, device, page_size=0):
+        self.w = w
+        self.layout = page_layout(w.seqlens_k, page_size, w.seed) if page_size else None
+        if self.layout is not None:
+            x = dict(x, k=to_pages(x["k"], self.layout), v=to_pages(x["v"], self.layout))
+        self.x = x
+        self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
         sel_b, fwd_b = sa.workspace_size(self.p)
         self.ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
@@ -106,8 +120,19 @@ class Step:
         self.idx = torch.empty((w.h_kv, self.p.rows, max(w.topk, 1)), dtype=torch.int32, device=device)
         self.n_idx = torch.empty((w.h_kv, self.p.rows), dtype=torch.int32, device=device)
         self.out = torch.empty_like(x["q"])
-        if self.k_cmp is not None and self.decode:
-            sa.compress(self.p, x["k"], self.k_cmp)       # the cache's pooled keys, built before decoding
+        if self.decode:
+            # the new tokens: the last M_b of every sequence (packed rows of the generated K/V)
+            new, o = [], 0
+            for nk, nq in zip(w.seqlens_k, w.seqlens_q):
+                new.extend(range(o + nk - nq, o + nk))
+                o += nk
+            rows = torch.tensor(new, device=device)
+            src_k = x["k"] if self.layout is None else from_pages(x["k"], self.layout)
+            src_v = x["v"] if self.layout is None else from_pages(x["v"], self.layout)
+            self.k_new = src_k[rows].contiguous()
+            self.v_new = src_v[rows].contiguous()
+            if self.k_cmp is not None:
+                sa.compress(self.p, x["k"], self.k_cmp)   # the cache's pooled keys, built before decoding
 
     def __call__(self, events=None, stages=None):
         """stages: (TimingEvents, four events) recorded before compress, after compress,
@@ -115,11 +140,10 @@ class Step:
         x = self.x
         mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
         mark(0)
-        if self.k_cmp is not None:
-            if self.decode:
-                sa.compress_tail(self.p, 1, x["k"], self.k_cmp)
-            else:
-                sa.compress(self.p, x["k"], self.k_cmp)
+        if self.decode:
+            sa.append_kv(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp)
+        elif self.k_cmp is not None:
+            sa.compress(self.p, x["k"], self.k_cmp)
         mark(1)
         sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
         mark(2)
@@ -222,9 +246,9 @@ def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks):
                     r["frac_of_measured"] = round(ach / peaks[mkey], 4)
         rep[name] = r
 
-    if g > 1 and decode:
-        # newest block of every sequence re-pooled: launch-bound, no roofline figure
-        add("compress", stage_ms[0], None, "launch")
+    if decode:
+        # the new tokens' K/V rows written and their blocks re-pooled: launch-bound
+        add("append", stage_ms[0], None, "launch")
     elif g > 1:
         add("compress", stage_ms[0], w.total_k * w.h_kv * d * elt + w.h_kv * sum(nb) * d * 4, "hbm")
     if decode:
@@ -426,6 +450,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_decode_32k", choices=sorted(FULL))
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="keep K and V in a paged cache of this many tokens per page (0: packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -460,7 +486,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    step = Step(w, x, device)
+    step = Step(w, x, device, page_size=args.page_size)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -553,7 +579,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": d,
                    "max_k": w.max_k, "queries": w.total_q, "block": w.block, "topk": w.topk,
-                   "n_init": w.n_init, "window": w.window, "parallelism": "single-gpu"},
+                   "n_init": w.n_init, "window": w.window, "kv_layout": (f"paged{args.page_size}" if args.page_size
+                                                                          else "packed"),
+                   "parallelism": "single-gpu"},
         "roofline": roof,
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_algorithmic_bytes": attn_bytes,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 1
+#define SPARSE_ATTN_ABI_VERSION 2
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -75,7 +75,10 @@ typedef struct sa_params {
     int32_t batch;             /* B >= 1 sequences                                      */
     int32_t h_q, h_kv;         /* query / KV heads; h_q % h_kv == 0, G = h_q / h_kv <= 64 */
     int32_t head_dim;          /* d: 64 or 128                                          */
-    int32_t max_q, max_k;      /* max over b of M_b and N_b (grid sizing)               */
+    int32_t max_q, max_k;      /* upper bounds on every M_b and N_b (grid sizing; the
+                                  pooled-key rows nbmax = ceil(max_k / block) per
+                                  sequence, so a decode loop keeps one k_cmp, sized
+                                  for its capacity, as its sequences grow)           */
     int64_t total_q, total_k;  /* sum M_b and sum N_b: rows of Q/O and of K/V           */
     const int32_t *cu_seqlens_q; /* device [batch+1], packed query offsets, [0] = 0     */
     const int32_t *cu_seqlens_k; /* device [batch+1], packed key offsets, [0] = 0       */
@@ -92,6 +95,17 @@ typedef struct sa_params {
     void *timing_events[2];    /* optional hipEvent_t pair: when both are set,
                                   sparse_attn_fwd records [0] right before and [1]
                                   right after its main attention kernel on `stream`  */
+    /* Paged K/V cache (optional; NULL block_table = the packed layout above).
+     * With a block table every K and V argument of every call is a page pool
+     * [pool_rows, h_kv, d] and token t of sequence b is pool row
+     *   block_table[b * max_pages + t / page_size] * page_size + t % page_size;
+     * cu_seqlens_k then only gives the lengths N_b, and total_k is still sum N_b.
+     * The pool must hold fewer than 2^31 rows; page ids are the caller's
+     * contract (not checked).  Pooled keys, Q/O and the selection table keep
+     * their layouts. */
+    const int32_t *block_table; /* device [batch, max_pages] int32 page ids, or NULL  */
+    int32_t max_pages;         /* row stride of block_table; >= ceil(max_k / page_size) */
+    int32_t page_size;         /* tokens per page: a power of two, 1 .. 2^20           */
 } sa_params;
 
 /* SPARSE_ATTN_ABI_VERSION of the built library. */
@@ -125,6 +139,25 @@ sa_status sparse_attn_compress(const sa_params *p, const void *k, float *k_cmp, 
  * sparse_attn_compress for those rows.  n_tail_blocks >= 1. */
 sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, const void *k,
                                     float *k_cmp, void *stream);
+
+/* Append the newest keys and values of every sequence to its cache and re-pool
+ * the blocks they fall in (the decode-time update of the pooled keys: a block
+ * that is still filling is pooled over the tokens it has and pooled again as
+ * tokens arrive, which keeps K~ equal to a fresh sparse_attn_compress of the
+ * grown cache; SparDA summary, Method; LSA deep-read, §2.2).  The parameters
+ * describe the cache AFTER the append: the M_b rows of sequence b in
+ * cu_seqlens_q are its new tokens, at positions q0_b .. q0_b + M_b - 1
+ * (q0_b = q_pos0[b] or N_b - M_b, as for queries).
+ *   k_new, v_new  [total_q, h_kv, d] of dtype: the new keys and values
+ *   k, v          the cache, packed [total_k, h_kv, d] or paged (block_table);
+ *                 the new rows are written, no other row is
+ *   k_cmp         pooled keys as from sparse_attn_compress; the blocks holding a
+ *                 new token are recomputed from the cache, or NULL to skip
+ *                 pooling (always skipped when block == 1)
+ * Two kernels on `stream`: the row scatter, then the pooling of the touched
+ * blocks (which reads the rows the first wrote). */
+sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
+                                float *k_cmp, void *stream);
 
 /* Top-k block selection (SparDA summary, Method; LSA deep-read, §2.3; S3R
  * review, sparse drafting: recent window + top-K by score).

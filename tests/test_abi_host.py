@@ -40,7 +40,22 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 1
+    assert sa.abi_version() == 2
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes view of sa_params has the C struct's size and field offsets."""
+    fields = [f for f, _ in _lib.SaParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(sa_params));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(sa_params, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(_lib.SaParams)
+    assert got[1:] == [getattr(_lib.SaParams, f).offset for f in fields]
 
 
 def test_every_declared_symbol_is_exported():
@@ -63,7 +78,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, INVALID), ("h_q", 7, INVALID), ("h_kv", 0, INVALID), ("head_dim", 96, UNSUPPORTED),
-    ("max_q", 0, INVALID), ("max_k", 0, INVALID), ("total_k", 10, INVALID), ("cu_seqlens_q", None, INVALID),
+    ("max_q", 0, INVALID), ("max_k", 0, INVALID), ("total_k", 0, INVALID), ("total_q", 0, INVALID), ("cu_seqlens_q", None, INVALID),
     ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID),
     ("n_init", -2, INVALID), ("window", 0, INVALID), ("shared_selection", 2, INVALID), ("dtype", 5, INVALID),
     ("softmax_scale", -1.0, INVALID), ("softmax_scale", float("inf"), INVALID),
@@ -75,6 +90,21 @@ def test_validate_rejects(field, value, code):
     assert status("sparse_attn_validate", ctypes.byref(p)) == code
     msg = _lib.lib().sparse_attn_last_error().decode()
     assert msg
+
+
+@pytest.mark.parametrize("page_size,max_pages", [(0, 64), (3, 64), (1 << 21, 64), (64, 63), (-64, 64)])
+def test_validate_rejects_bad_paging(page_size, max_pages):
+    p = params(block_table=FAKE, page_size=page_size, max_pages=max_pages)   # max_k 4096
+    assert status("sparse_attn_validate", ctypes.byref(p)) == INVALID
+    assert "page" in _lib.lib().sparse_attn_last_error().decode()
+
+
+def test_validate_accepts_paging():
+    for ps, mp in [(1, 4096), (16, 256), (64, 64), (4096, 1), (1 << 20, 1)]:
+        assert status("sparse_attn_validate", ctypes.byref(params(block_table=FAKE, page_size=ps,
+                                                                  max_pages=mp))) == 0
+    # without a block table the paging fields are ignored
+    assert status("sparse_attn_validate", ctypes.byref(params(page_size=3, max_pages=0))) == 0
 
 
 def test_validate_accepts_and_clears_error():
@@ -121,6 +151,14 @@ def test_calls_reject_null_and_misaligned_pointers():
                   None) == INVALID
     assert status("sparse_attn_fwd", p, vp(FAKE + 8), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
                   None, 0, None) == INVALID
+    # append: k_new, v_new, k and v are required; k_cmp is optional but must be aligned
+    assert status("sparse_attn_append_kv", p, None, vp(FAKE), vp(FAKE), vp(FAKE), None, None) == INVALID
+    assert status("sparse_attn_append_kv", p, vp(FAKE), vp(FAKE), vp(FAKE), None, None, None) == INVALID
+    assert status("sparse_attn_append_kv", p, vp(FAKE), vp(FAKE + 2), vp(FAKE), vp(FAKE), None, None) == INVALID
+    assert status("sparse_attn_append_kv", p, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE + 4),
+                  None) == INVALID
+    bad = ctypes.byref(params(block_table=FAKE, page_size=5, max_pages=1000))
+    assert status("sparse_attn_append_kv", bad, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None) == INVALID
 
 
 def test_calls_reject_small_workspace():

@@ -12,6 +12,10 @@ call raises.
     k_cmp = compress(p, k)
     idx, n_idx = select(p, q, k_cmp, k)
     out = fwd(p, q, k, v, idx, n_idx)
+
+A decode loop appends each step's keys and values first (``append_kv``), which also
+re-pools the block the new token falls in; ``block_table=`` / ``page_size=`` switch
+K and V to a paged cache read through the block table.
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ import torch
 from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
                    SA_POOL_MEAN, SaParams, SparseAttnError, check, lib)
 
-__all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "select", "fwd",
+__all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select", "fwd",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "LIB_PATH", "EXPORTS"]
 
 _DT = {torch.float32: SA_DTYPE_F32, torch.bfloat16: SA_DTYPE_BF16}
@@ -47,8 +51,10 @@ class Params:
                  block: int, topk: int, n_init: int, window: int, dtype=torch.bfloat16,
                  pool: int = SA_POOL_MEAN, shared_selection: int = 0,
                  topk_per_seq: Optional[torch.Tensor] = None, q_pos0: Optional[torch.Tensor] = None,
-                 softmax_scale: float = 0.0):
-        self._keep = (cu_seqlens_q, cu_seqlens_k, topk_per_seq, q_pos0)
+                 softmax_scale: float = 0.0, block_table: Optional[torch.Tensor] = None, page_size: int = 0):
+        """block_table: int32 [batch, max_pages] page ids of a paged K/V cache (K and V
+        arguments are then page pools [pages * page_size, h_kv, d]); None = packed K/V."""
+        self._keep = (cu_seqlens_q, cu_seqlens_k, topk_per_seq, q_pos0, block_table)
         self.dtype = dtype
         s = SaParams()
         s.batch, s.h_q, s.h_kv, s.head_dim = batch, h_q, h_kv, head_dim
@@ -61,12 +67,18 @@ class Params:
         s.n_init, s.window, s.shared_selection = n_init, window, shared_selection
         s.softmax_scale = softmax_scale
         s.dtype = _DT[dtype]
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+                raise ValueError("block_table must be a contiguous int32 [batch, max_pages] tensor")
+            s.block_table = block_table.data_ptr()
+            s.max_pages = block_table.shape[1]
+            s.page_size = page_size
         self.s = s
 
     @classmethod
     def from_lengths(cls, seqlens_q: Sequence[int], seqlens_k: Sequence[int], device="cuda",
                      topk_per_seq: Optional[Sequence[int]] = None, q_pos0: Optional[Sequence[int]] = None,
-                     **kw) -> "Params":
+                     block_table=None, **kw) -> "Params":
         def cu(lens):
             out = [0]
             for x in lens:
@@ -76,9 +88,11 @@ class Params:
         tps = None if topk_per_seq is None else torch.tensor(list(topk_per_seq), dtype=torch.int32,
                                                              device=device)
         qp = None if q_pos0 is None else torch.tensor(list(q_pos0), dtype=torch.int32, device=device)
+        if block_table is not None and not isinstance(block_table, torch.Tensor):
+            block_table = torch.tensor(block_table, dtype=torch.int32, device=device)
         return cls(batch=len(seqlens_k), cu_seqlens_q=cu(seqlens_q), cu_seqlens_k=cu(seqlens_k),
                    max_q=max(seqlens_q), max_k=max(seqlens_k), total_q=sum(seqlens_q),
-                   total_k=sum(seqlens_k), topk_per_seq=tps, q_pos0=qp, **kw)
+                   total_k=sum(seqlens_k), topk_per_seq=tps, q_pos0=qp, block_table=block_table, **kw)
 
     @property
     def rows(self) -> int:
@@ -127,6 +141,14 @@ def compress_tail(p: Params, n_tail_blocks: int, k: torch.Tensor, k_cmp: torch.T
     check("sparse_attn_compress_tail", lib().sparse_attn_compress_tail(p.ref(), int(n_tail_blocks), _ptr(k),
                                                                        _ptr(k_cmp), _stream(stream)))
     return k_cmp
+
+
+def append_kv(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+              k_cmp: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write the new tokens' keys and values (one row per query row of ``p``) into the
+    cache and re-pool the blocks they fall in (k_cmp, when given)."""
+    check("sparse_attn_append_kv", lib().sparse_attn_append_kv(p.ref(), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v),
+                                                               _ptr(k_cmp), _stream(stream)))
 
 
 def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Optional[torch.Tensor],

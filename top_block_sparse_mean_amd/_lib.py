@@ -17,7 +17,7 @@ SA_POOL_MEAN, SA_POOL_L2SUM = 0, 1
 # Every symbol include/sparse_attn.h declares.
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
-           "sparse_attn_compress_tail", "sparse_attn_select", "sparse_attn_fwd")
+           "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_fwd")
 
 
 class SaParams(ctypes.Structure):
@@ -43,6 +43,9 @@ class SaParams(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("timing_events", ctypes.c_void_p * 2),
+        ("block_table", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
     ]
 
 

@@ -52,9 +52,9 @@ sa_status check_params(const sa_params *p)
         return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
     if (p->max_q < 1 || p->max_k < 1)
         return fail(SA_ERR_INVALID_ARG, "max_q (%d) and max_k (%d) must be >= 1", p->max_q, p->max_k);
-    if (p->total_q < p->max_q || p->total_k < p->max_k)
-        return fail(SA_ERR_INVALID_ARG, "total_q/total_k (%lld/%lld) below max_q/max_k (%d/%d)",
-                    (long long)p->total_q, (long long)p->total_k, p->max_q, p->max_k);
+    if (p->total_q < 1 || p->total_k < 1)
+        return fail(SA_ERR_INVALID_ARG, "total_q (%lld) and total_k (%lld) must be >= 1", (long long)p->total_q,
+                    (long long)p->total_k);
     if (p->total_q > (1LL << 40) || p->total_k > (1LL << 40) || p->max_k > (1 << 30))
         return fail(SA_ERR_UNSUPPORTED, "sizes beyond the supported range");
     if ((long long)p->batch * p->h_kv > 65535 || (p->max_q + 63) / 64 > 65535)
@@ -78,6 +78,15 @@ sa_status check_params(const sa_params *p)
         return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
     if (!(p->softmax_scale >= 0.f) || std::isinf(p->softmax_scale))
         return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (p->block_table) {
+        const int ps = p->page_size;
+        if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)) != 0)
+            return fail(SA_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20] (got %d)", ps);
+        const long long need = ((long long)p->max_k + ps - 1) / ps;
+        if (p->max_pages < need)
+            return fail(SA_ERR_INVALID_ARG, "max_pages (%d) below ceil(max_k / page_size) = %lld", p->max_pages,
+                        need);
+    }
     return SA_OK;
 }
 
@@ -108,6 +117,12 @@ sa::KP make_kp(const sa_params *p)
     k.nb_max = (p->max_k + p->block - 1) / p->block;
     k.rows = p->shared_selection ? p->batch : p->total_q;
     k.dtype = p->dtype;
+    k.block_table = p->block_table;
+    k.max_pages = p->block_table ? p->max_pages : 0;
+    k.page_shift = 0;
+    if (p->block_table)
+        while ((1 << k.page_shift) < p->page_size)
+            k.page_shift++;
     return k;
 }
 
@@ -182,6 +197,21 @@ sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, c
     if (n_tail_blocks < 1)
         return fail(SA_ERR_INVALID_ARG, "n_tail_blocks must be >= 1 (got %d)", n_tail_blocks);
     return compress_common(p, n_tail_blocks, k, k_cmp, stream);
+}
+
+sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
+                                float *k_cmp, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!k_new || !v_new || !k || !v)
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k and v are required");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(v) || (k_cmp && !aligned16(k_cmp)))
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k, v and k_cmp must be 16-byte aligned");
+    sa::KP kp = make_kp(p);
+    return device_status(sa::launch_append(kp, p->dtype, k_new, v_new, k, v, k_cmp, (hipStream_t)stream),
+                         "append launch");
 }
 
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,

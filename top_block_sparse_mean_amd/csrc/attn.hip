@@ -48,6 +48,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(KP P, const T *__restric
     int nsel = n_idx[(long long)c * P.rows + row];
     nsel = nsel < 0 ? 0 : (nsel > P.topk ? P.topk : nsel);
     const ASet a = aset_make(P, s.n_k, p, p_sel, sel, nsel);
+    const long long k_base = kv_base(P, s);
+    const KvMap kmap = kv_map(P, b);
 
     const int chunk = (a.total + n_split - 1) / n_split;
     const int s0 = split * chunk;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(KP P, const T *__restric
             ok[u] = pos < s1;
             if (ok[u]) {
                 int t = aset_token(a, sel, pos);
-                long long off = ((s.k_off + t) * P.h_kv + c) * D + sub * 8;
+                long long off = ((k_base + kmap.row(t)) * P.h_kv + c) * D + sub * 8;
                 load8(k + off, kx[u]);
                 load8(v + off, vx[u]);
             } else {

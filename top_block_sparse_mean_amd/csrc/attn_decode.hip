@@ -3,9 +3,9 @@
 // (per-query selection), or every head of every draft of a sequence (shared
 // selection; drafts differ only by their causal limit).  The next chunk's K/V
 // loads are issued before the current chunk is computed.  The attended
-// positions of the workgroup's split are first mapped to tokens into LDS (the
-// selection row is read like a page table).  Splits write (max, sum,
-// unnormalised output) partials that attn_combine merges.
+// positions of the workgroup's split are first mapped to K/V rows into LDS (the
+// selection row, and for a paged cache the block table, read like page tables).
+// Splits write (max, sum, unnormalised output) partials that attn_combine merges.
 #include "mfma_common.hpp"
 
 namespace sa {
@@ -69,12 +69,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
     const int chunk = (a.total + n_split - 1) / n_split;
     const int s0 = split * chunk;
     const int n = max(0, min(a.total, s0 + chunk) - s0);
+    const KvMap kmap = kv_map(P, b);
     for (int x = tid; x < n; x += 256)
-        sh_tok[x] = aset_token(a, sel, s0 + x);
+        sh_tok[x] = kmap.row(aset_token(a, sel, s0 + x));
 
     // B operand of S^T = K Q^T: lane l holds Q[row l%16][32 ks + 8 (l/16) .. +8]
     bf16x8 qop[KS];
-    int p_row = -1;
+    int lim = 0;                              // live list entries of this lane's row (split-local)
     if (rr < R) {
         const long long qi = q_first + rr / P.G;
         const int h = c * P.G + rr % P.G;
@@ -82,7 +83,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
             qop[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
-        p_row = s.q0 + (int)(q_first - s.q_off) + rr / P.G;
+        const int p_row = s.q0 + (int)(q_first - s.q_off) + rr / P.G;
+        lim = a.total - s0 - (p_max - p_row);
     } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
@@ -91,8 +93,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
     __syncthreads();
 
     const long long tstride = (long long)P.h_kv * D;
-    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
-    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
+    const uint16_t *kb = k + (kv_base(P, s) * P.h_kv + c) * D;
+    const uint16_t *vb = v + (kv_base(P, s) * P.h_kv + c) * D;
     float m_run = -INFINITY, l_part = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -101,17 +103,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
 
     ChunkRegs<D> ra, rb;
     if (32 * w < n)
-        load_chunk<D>(ra, sh_tok, 32 * w, n, kb, vb, tstride, rr, g4, p_row);
+        load_chunk<D>(ra, sh_tok, 32 * w, n, kb, vb, tstride, rr, g4, lim);
     for (int ch = w; 32 * ch < n; ch += 8) {
         const int c1 = ch + 4;
         if (32 * c1 < n)
-            load_chunk<D>(rb, sh_tok, 32 * c1, n, kb, vb, tstride, rr, g4, p_row);
+            load_chunk<D>(rb, sh_tok, 32 * c1, n, kb, vb, tstride, rr, g4, lim);
         compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
         if (32 * c1 >= n)
             break;
         const int c2 = c1 + 4;
         if (32 * c2 < n)
-            load_chunk<D>(ra, sh_tok, 32 * c2, n, kb, vb, tstride, rr, g4, p_row);
+            load_chunk<D>(ra, sh_tok, 32 * c2, n, kb, vb, tstride, rr, g4, lim);
         compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
     }
     float l_row = l_part + __shfl_xor(l_part, 16, kWave);

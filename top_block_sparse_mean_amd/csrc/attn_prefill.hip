@@ -13,13 +13,13 @@ namespace sa {
 // 8-bit live mask taken from the 32-bit token mask of its row.
 template <int D>
 __device__ __forceinline__ void load_tile(ChunkRegs<D> &r, int t0, int n_k, uint32_t m32, const uint16_t *kb,
-                                          const uint16_t *vb, long long tstride, int rr, int g4)
+                                          const uint16_t *vb, long long tstride, const KvMap &map, int rr, int g4)
 {
     constexpr int KS = D / 32;
 #pragma unroll
     for (int s = 0; s < 2; s++) {
         int t = min(t0 + 16 * s + rr, n_k - 1);
-        long long off = (long long)t * tstride + 8 * g4;
+        long long off = (long long)map.row(t) * tstride + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
             r.k[s][ks] = ld16(kb + off + 32 * ks);
@@ -31,7 +31,7 @@ __device__ __forceinline__ void load_tile(ChunkRegs<D> &r, int t0, int n_k, uint
         int t = min(t0 + off, n_k - 1);
         r.live |= ((m32 >> off) & 1u) << i;
         if (D == 128 || rr < D / 8)
-            r.v[i] = ld16(vb + (long long)t * tstride + 8 * rr);
+            r.v[i] = ld16(vb + (long long)map.row(t) * tstride + 8 * rr);
         else
             r.v[i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -166,8 +166,9 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
         return tile_mask(tile * 32, p_row, P.n_init, lo_w, sb);
     };
     const long long tstride = (long long)P.h_kv * D;
-    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
-    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
+    const uint16_t *kb = k + (kv_base(P, s) * P.h_kv + c) * D;
+    const uint16_t *vb = v + (kv_base(P, s) * P.h_kv + c) * D;
+    const KvMap kmap = kv_map(P, b);
     float m_run = -INFINITY, l_part = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -176,19 +177,19 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
     ChunkRegs<D> ra, rb;
     if (n_list > 0) {
         int t = sh_list[w][0];
-        load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+        load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, kmap, rr, g4);
     }
     for (int it = 0; it < n_list; it += 2) {
         if (it + 1 < n_list) {
             int t = sh_list[w][it + 1];
-            load_tile<D>(rb, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+            load_tile<D>(rb, t * 32, s.n_k, row_mask(t), kb, vb, tstride, kmap, rr, g4);
         }
         compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
         if (it + 1 >= n_list)
             break;
         if (it + 2 < n_list) {
             int t = sh_list[w][it + 2];
-            load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, rr, g4);
+            load_tile<D>(ra, t * 32, s.n_k, row_mask(t), kb, vb, tstride, kmap, rr, g4);
         }
         compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
     }
@@ -240,7 +241,7 @@ struct WgStage {
 };
 
 __device__ __forceinline__ void wg_issue(WgStage &st, const uint16_t *kb, const uint16_t *vb, long long tstride,
-                                         int t0, int n_k, int tid)
+                                         const KvMap &map, int t0, int n_k, int tid)
 {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
@@ -248,7 +249,7 @@ __device__ __forceinline__ void wg_issue(WgStage &st, const uint16_t *kb, const 
         const int row = chunk >> 4, col = chunk & 15;
         const int t = min(max(t0 + (row & 63), 0), n_k - 1);
         const uint16_t *base = row < 64 ? kb : vb;
-        st.c[u] = ld16(base + (long long)t * tstride + 8 * col);
+        st.c[u] = ld16(base + (long long)map.row(t) * tstride + 8 * col);
     }
 }
 
@@ -479,8 +480,9 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
 
     // this wavefront's rows: a = 0, 1 -> rows 16a + rr of its 32
     const long long tstride = (long long)P.h_kv * D;
-    const uint16_t *kb = k + (s.k_off * P.h_kv + c) * D;
-    const uint16_t *vb = v + (s.k_off * P.h_kv + c) * D;
+    const uint16_t *kb = k + (kv_base(P, s) * P.h_kv + c) * D;
+    const uint16_t *vb = v + (kv_base(P, s) * P.h_kv + c) * D;
+    const KvMap kmap = kv_map(P, b);
     bf16x8 qop[2][KS];
     int p_row[2], lo_w[2], qbit[2];
     bool row_ok[2];
@@ -534,11 +536,11 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
     if (n_list > 0) {
 #pragma unroll
         for (int x = 0; x < kWgStep; x++)
-            wg_issue(stage[x], kb, vb, tstride, sh_list[min(x, last)] * 64, s.n_k, tid);
+            wg_issue(stage[x], kb, vb, tstride, kmap, sh_list[min(x, last)] * 64, s.n_k, tid);
 #pragma unroll
         for (int x = 0; x < kWgStep; x++) {
             wg_write(stage[x], sh_kv[0] + x * kTileBytes, tid);
-            wg_issue(stage[x], kb, vb, tstride, sh_list[min(kWgStep + x, last)] * 64, s.n_k, tid);
+            wg_issue(stage[x], kb, vb, tstride, kmap, sh_list[min(kWgStep + x, last)] * 64, s.n_k, tid);
         }
         const int n_step = (n_list + kWgStep - 1) / kWgStep;
         for (int i = 0; i < n_step; i++) {
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void attn_wg_kernel(KP P, const uint16_t *_
 #pragma unroll
             for (int x = 0; x < kWgStep; x++) {
                 wg_write(stage[x], sh_kv[(i + 1) & 1] + x * kTileBytes, tid);
-                wg_issue(stage[x], kb, vb, tstride, sh_list[min(kWgStep * (i + 2) + x, last)] * 64, s.n_k, tid);
+                wg_issue(stage[x], kb, vb, tstride, kmap, sh_list[min(kWgStep * (i + 2) + x, last)] * 64, s.n_k, tid);
             }
         }
     }

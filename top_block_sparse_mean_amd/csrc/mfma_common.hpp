@@ -35,9 +35,14 @@ struct ChunkRegs {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Loads the K and V rows of list entries base .. base+31 (tok[] holds each entry's
+// row relative to kb / vb).  An entry is live for the lane's row when it lies in
+// the split (pos < n) and below the row's causal limit lim: the attended list is
+// ascending in position, so a row that stops d positions before the unit's last
+// query drops exactly the list's last d entries.
 template <int D>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D> &r, const int *tok, int base, int n, const uint16_t *kb,
-                                           const uint16_t *vb, long long tstride, int rr, int g4, int p_row)
+                                           const uint16_t *vb, long long tstride, int rr, int g4, int lim)
 {
     constexpr int KS = D / 32;
 #pragma unroll
@@ -53,7 +58,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D> &r, const int *tok, int 
     for (int i = 0; i < 8; i++) {
         int pos = base + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + (i - 4));
         int t = tok[min(pos, n - 1)];
-        r.live |= (pos < n && t <= p_row) ? (1u << i) : 0u;
+        r.live |= (pos < n && pos < lim) ? (1u << i) : 0u;
         if (D == 128 || rr < D / 8)
             r.v[i] = ld16(vb + (long long)t * tstride + 8 * rr);
         else

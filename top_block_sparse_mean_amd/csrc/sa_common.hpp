@@ -24,6 +24,8 @@ struct KP {
     int nb_max;         // ceil(max_k / g)
     long long rows;     // selection rows per KV head
     int dtype;          // 0 fp32, 1 bf16
+    const int32_t *block_table;   // paged K/V: [batch, max_pages] page ids, or nullptr (packed)
+    int max_pages, page_shift;    // block-table row stride; log2(page_size)
 };
 
 struct Seq {
@@ -41,6 +43,28 @@ __device__ __forceinline__ Seq seq_info(const KP &P, int b)
     s.q0 = P.q_pos0 ? P.q_pos0[b] : s.n_k - s.n_q;
     return s;
 }
+
+// Where token t of one sequence's K/V lives: row() is the token's row relative
+// to kv_base() (the sequence's first row when packed, the pool's first row when
+// paged: the block table read as a page table).
+struct KvMap {
+    const int32_t *pt;  // the sequence's block-table row, or nullptr (packed)
+    int shift;
+    __device__ __forceinline__ int row(int t) const
+    {
+        return pt ? (pt[t >> shift] << shift) | (t & ((1 << shift) - 1)) : t;
+    }
+};
+
+__device__ __forceinline__ KvMap kv_map(const KP &P, int b)
+{
+    KvMap m;
+    m.pt = P.block_table ? P.block_table + (long long)b * P.max_pages : nullptr;
+    m.shift = P.page_shift;
+    return m;
+}
+
+__device__ __forceinline__ long long kv_base(const KP &P, const Seq &s) { return P.block_table ? 0 : s.k_off; }
 
 // Sequence holding packed query index i: the number of b in [1, batch) with
 // cu_seqlens_q[b] <= i, counted with one load per lane and a ballot (no chain

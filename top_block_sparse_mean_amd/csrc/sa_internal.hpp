@@ -8,6 +8,8 @@ namespace sa {
 enum { kSelectEmpty = 0, kSelectRow = 1, kSelectSplit = 2, kSelectTile = 3 };
 
 hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, int n_tail, hipStream_t st);
+hipError_t launch_append(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
+                         float *k_cmp, hipStream_t st);
 
 int select_plan(const KP &P);
 size_t select_workspace_bytes(const KP &P, int plan);

@@ -368,8 +368,10 @@ struct RowDot {
 template <typename KT, int D>
 __device__ __forceinline__ const KT *key_row(const KP &P, const KT *base, const RowGeo &r, int c, int j)
 {
-    if (P.g == 1)
-        return base + ((r.k_off + j) * P.h_kv + c) * D;
+    if (P.g == 1) {
+        const long long row = P.block_table ? (long long)kv_map(P, r.b).row(j) : r.k_off + j;
+        return base + (row * P.h_kv + c) * D;
+    }
     return base + (((long long)c * P.batch + r.b) * P.nb_max + j) * D;
 }
 
@@ -649,15 +651,16 @@ struct KeyStage {
     kv4u c[N];
 };
 
+// Candidate row j lives at base + map.row(j) * row_stride (raw keys may be paged).
 template <int N, int kRowBytes>
-__device__ __forceinline__ void key_issue(KeyStage<N> &st, const unsigned char *base, long long row_stride, int jt,
-                                          int j_end, int tid)
+__device__ __forceinline__ void key_issue(KeyStage<N> &st, const unsigned char *base, long long row_stride,
+                                          const KvMap &map, int jt, int j_end, int tid)
 {
 #pragma unroll
     for (int u = 0; u < N; u++) {
         const int piece = tid + 256 * u, row = piece / (kRowBytes / 16), col = piece % (kRowBytes / 16);
         const int j = min(jt + row, j_end - 1);          // rows past the end re-read the last one
-        st.c[u] = *reinterpret_cast<const kv4u *>(base + (long long)j * row_stride + 16 * col);
+        st.c[u] = *reinterpret_cast<const kv4u *>(base + (long long)map.row(j) * row_stride + 16 * col);
     }
 }
 
@@ -739,9 +742,10 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
     // staging: thread tid holds pieces tid + 256 u of the tile (row = piece / pieces per row)
     const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(kbase);
     const long long row_stride = P.g == 1 ? (long long)P.h_kv * kRowBytes : kRowBytes;
-    const long long base_off = P.g == 1 ? ((long long)s.k_off * P.h_kv + c) * kRowBytes
+    const long long base_off = P.g == 1 ? (kv_base(P, s) * P.h_kv + c) * kRowBytes
                                         : (((long long)c * P.batch + b) * P.nb_max) * kRowBytes;
     const unsigned char *kb0 = kbytes + base_off;
+    const KvMap kmap = P.g == 1 ? kv_map(P, b) : KvMap{nullptr, 0};
     auto tile = [&](const unsigned char *buf, int jt) {
         floatx4 acc[2][2];
 #pragma unroll
@@ -788,14 +792,14 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
     };
     const int n_t = (jc1 - jc0 + 63) / 64;
     KeyStage<kChunks> stage;
-    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0, jhi_last, tid);
+    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, kmap, jc0, jhi_last, tid);
     key_write<kChunks, kRowBytes, kPitch>(stage, sh_k[0], tid);
-    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0 + 64, jhi_last, tid);   // past the end: reloads
+    key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, kmap, jc0 + 64, jhi_last, tid);   // past the end: reloads
     for (int t = 0; t < n_t; t++) {
         __syncthreads();                                  // buffer t&1 holds tile t
         tile(sh_k[t & 1], jc0 + 64 * t);
         key_write<kChunks, kRowBytes, kPitch>(stage, sh_k[(t + 1) & 1], tid);
-        key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, jc0 + 64 * (t + 2), jhi_last, tid);
+        key_issue<kChunks, kRowBytes>(stage, kb0, row_stride, kmap, jc0 + 64 * (t + 2), jhi_last, tid);
     }
 }
 

@@ -92,14 +92,20 @@ def _geom(w, cu_q, cu_k, q_pos0):
 
 
 def compress(w, k, cu_k=None) -> np.ndarray:
-    """Pooled keys K~ [Hkv, batch, nb_max, d] in fp64 (block mean, or L2-normalised sum)."""
+    """Pooled keys K~ [Hkv, batch, nb_max, d] in fp64 (mean, or L2-normalised sum, over each
+    block's window: its tokens and the w.pool_overlap tokens before them)."""
     _, cu_k, _ = _geom(w, None, cu_k, None)
     nb_max = -(-max(w.seqlens_k) // w.block)
     out = np.zeros((w.h_kv, w.batch, nb_max, w.head_dim), dtype=np.float64)
     rc = lib().or_compress(w.batch, w.h_kv, w.head_dim, _ptr(cu_k, _i32p), w.block, w.pool,
-                           w.dtype, _ptr(k), ctypes.c_int64(nb_max), _ptr(out, _f64p))
+                           int(w.pool_overlap), w.dtype, _ptr(k), ctypes.c_int64(nb_max), _ptr(out, _f64p))
     assert rc == 0
     return out
+
+
+def select_tau(w) -> float:
+    """Softmax temperature of the SOFTMAX group score: the workload's, or sqrt(d)."""
+    return float(w.select_tau) if w.select_tau > 0 else float(np.sqrt(w.head_dim))
 
 
 def select(w, q_sel, k_cmp, k, rows=None, heads=None, q_pos0=None, cu_q=None, cu_k=None,
@@ -134,7 +140,8 @@ def select(w, q_sel, k_cmp, k, rows=None, heads=None, q_pos0=None, cu_q=None, cu
     rc = lib().or_select(
         w.batch, w.h_q, w.h_kv, w.head_dim, _ptr(cu_q, _i32p), _ptr(cu_k, _i32p),
         _ptr(qp, _i32p), w.block, int(w.topk), _ptr(tps, _i32p), w.n_init, w.window,
-        int(w.shared_selection), w.dtype, _ptr(q_sel), _ptr(k_cmp, _f64p),
+        int(w.shared_selection), int(w.select_mode), ctypes.c_double(select_tau(w)), w.dtype, _ptr(q_sel),
+        _ptr(k_cmp, _f64p),
         ctypes.c_int64(nb_max), _ptr(k), ctypes.c_int64(n), _ptr(rows, _i64p),
         _ptr(heads, _i32p), kcap, _ptr(idx, _i32p), _ptr(nn, _i32p), _ptr(sk, _f64p),
         _ptr(sk1, _f64p), _ptr(fl, _f64p), _ptr(ncand, _i32p), _ptr(scores, _f64p),

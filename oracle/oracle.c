@@ -11,14 +11,24 @@
  *   compress  K~_j = mean of the keys of block j (g consecutive tokens, one KV
  *             head): the parameter-free mean pooling of keys that InfLLM-V2
  *             uses (SparDA summary, Method).  L2SUM: each key divided by its
- *             L2 norm, then the g keys summed (LSA deep-read, §2.2).  Blocks do
- *             not overlap (stride = kernel = g).  A last partial block is the
- *             mean over the tokens it has.  A zero key contributes zero to L2SUM.
+ *             L2 norm, then the keys summed (LSA deep-read, §2.2).  The pooling
+ *             window of block j is its own tokens [jg, e_j] reaching `overlap`
+ *             tokens further back (clipped at token 0): kernel g + overlap,
+ *             stride g, the overlapping compressed keys of InfLLM-V2 (SparDA
+ *             summary, Method); overlap 0 gives disjoint blocks.  A last
+ *             partial block pools the tokens it has.  A zero key contributes
+ *             zero to L2SUM.
  *
- *   select    one score per candidate block and GQA group: the group's query
- *             heads summed, dotted with K~_j, over sqrt(d) (SparDA summary,
- *             Method: one selector head per GQA group; LSA deep-read, §2.4:
- *             the heads summed into one index query).  Candidates are the blocks
+ *   select    one score per candidate block and GQA group (SparDA summary,
+ *             Method: one selector head per GQA group).  Mode SUM: the group's
+ *             query heads summed, dotted with K~_j, over sqrt(d) (LSA
+ *             deep-read, §2.4: the heads summed into one index query).  Mode
+ *             SOFTMAX: for every head h, the softmax over the row's candidates
+ *             of q_h.K~_j / tau, summed over the group's heads (the SparDA
+ *             training target, SparDA summary, Method).  Mode MAX: the largest
+ *             over the group's heads of q_h.K~_j / sqrt(d) (N-LSA scores a
+ *             bucket by its best head, LSA deep-read, §2.5).  With several
+ *             queries in a row, q_h sums head h over them.  Candidates are the blocks
  *             that lie wholly at or before the selection position p_sel and
  *             hold at least one token outside the init/window set F(p_sel).
  *             The k best by (score descending, block index ascending) are kept
@@ -52,6 +62,9 @@
 #define OR_BF16 1
 #define OR_MEAN 0
 #define OR_L2SUM 1
+#define OR_SEL_SUM 0
+#define OR_SEL_SOFTMAX 1
+#define OR_SEL_MAX 2
 
 static double elem(const void *base, int dtype, int64_t i)
 {
@@ -100,10 +113,10 @@ static int seq_of_query(int64_t i, int batch, const int32_t *cu_q)
 
 /* ---------------------------------------------------------------- compress */
 
-int or_compress(int batch, int h_kv, int d, const int32_t *cu_k, int g, int pool, int dtype,
+int or_compress(int batch, int h_kv, int d, const int32_t *cu_k, int g, int pool, int overlap, int dtype,
                 const void *k, int64_t nb_max, double *k_cmp)
 {
-    if (g < 1 || d < 1)
+    if (g < 1 || d < 1 || overlap < 0)
         return 1;
     int64_t n_items = (int64_t)h_kv * batch * nb_max;
 #pragma omp parallel for schedule(dynamic, 64)
@@ -112,13 +125,15 @@ int or_compress(int batch, int h_kv, int d, const int32_t *cu_k, int g, int pool
         int b = (int)((it / nb_max) % batch);
         int c = (int)(it / (nb_max * batch));
         int64_t n_b = cu_k[b + 1] - cu_k[b];
-        int64_t t0 = j * g, t1 = (j + 1) * (int64_t)g;
+        int64_t t0 = j * g - overlap, t1 = (j + 1) * (int64_t)g;
         double *out = k_cmp + it * d;
+        if (t0 < 0)
+            t0 = 0;
         if (t1 > n_b)
             t1 = n_b;
         for (int e = 0; e < d; e++)
             out[e] = 0.0;
-        if (t0 >= n_b)
+        if (j * g >= n_b)
             continue;
         for (int64_t t = t0; t < t1; t++) {
             int64_t row = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;
@@ -175,7 +190,7 @@ static int in_fixed_set(int64_t t, int64_t p_sel, int n_init, int window)
 
 int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
               const int32_t *q_pos0, int g, int topk, const int32_t *topk_per_seq, int n_init,
-              int window, int shared, int dtype, const void *q_sel, const double *k_cmp,
+              int window, int shared, int mode, double tau, int dtype, const void *q_sel, const double *k_cmp,
               int64_t nb_max, const void *k, int64_t n_req, const int64_t *req_row,
               const int32_t *req_kvh, int kcap, int32_t *out_idx, int32_t *out_n, double *out_sk,
               double *out_sk1, double *out_floor, int32_t *out_ncand, double *out_scores,
@@ -203,18 +218,32 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
         int64_t n_b = cu_k[b + 1] - cu_k[b];
         int64_t nb_b = (n_b + g - 1) / g;
 
-        /* score query: every row query, every head of group c, summed */
+        /* per-head queries q_h (summed over the row's queries) and their sum */
+        double *qh = (double *)calloc((size_t)G * d, sizeof(double));
         double *qs = (double *)calloc((size_t)d, sizeof(double));
         for (int64_t i = qa; i < qb; i++)
-            for (int h = c * G; h < (c + 1) * G; h++)
+            for (int hh = 0; hh < G; hh++)
                 for (int e = 0; e < d; e++)
-                    qs[e] += elem(q_sel, dtype, (i * h_q + h) * (int64_t)d + e);
-        double qnorm = 0.0;
+                    qh[hh * d + e] += elem(q_sel, dtype, (i * h_q + c * G + hh) * (int64_t)d + e);
+        for (int hh = 0; hh < G; hh++)
+            for (int e = 0; e < d; e++)
+                qs[e] += qh[hh * d + e];
+        double qnorm = 0.0, qhmax = 0.0;
         for (int e = 0; e < d; e++)
             qnorm += qs[e] * qs[e];
         qnorm = sqrt(qnorm);
+        for (int hh = 0; hh < G; hh++) {
+            double n2 = 0.0;
+            for (int e = 0; e < d; e++)
+                n2 += qh[hh * d + e] * qh[hh * d + e];
+            if (sqrt(n2) > qhmax)
+                qhmax = sqrt(n2);
+        }
 
         cand *cs = (cand *)malloc(sizeof(cand) * (size_t)(nb_b > 0 ? nb_b : 1));
+        /* SOFTMAX: every head's logit of every candidate, [candidate][head] */
+        double *lg = mode == OR_SEL_SOFTMAX ? (double *)malloc(sizeof(double) * (size_t)G *
+                                                               (size_t)(nb_b > 0 ? nb_b : 1)) : NULL;
         int64_t nc = 0;
         double kmax = 0.0;
         for (int64_t j = 0; j < nb_b; j++) {
@@ -229,24 +258,51 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
                     outside_f = 1;
             if (!outside_f)
                 continue; /* wholly inside init/window */
-            double dot = 0.0, kn = 0.0;
+            double dot = 0.0, kn = 0.0, best = -INFINITY;
+            double *kv = (double *)malloc(sizeof(double) * (size_t)d);
             for (int e = 0; e < d; e++) {
-                double kv;
                 if (g == 1)
-                    kv = elem(k, dtype, ((cu_k[b] + j) * h_kv + c) * (int64_t)d + e);
+                    kv[e] = elem(k, dtype, ((cu_k[b] + j) * h_kv + c) * (int64_t)d + e);
                 else
-                    kv = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];
-                dot += qs[e] * kv;
-                kn += kv * kv;
+                    kv[e] = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];
+                dot += qs[e] * kv[e];
+                kn += kv[e] * kv[e];
             }
+            for (int hh = 0; hh < G && mode != OR_SEL_SUM; hh++) {
+                double dh = 0.0;
+                for (int e = 0; e < d; e++)
+                    dh += qh[hh * d + e] * kv[e];
+                if (mode == OR_SEL_SOFTMAX)
+                    lg[nc * G + hh] = dh / tau;
+                else if (dh > best)
+                    best = dh;
+            }
+            free(kv);
             if (sqrt(kn) > kmax)
                 kmax = sqrt(kn);
-            cs[nc].s = dot / sqrt((double)d);
+            cs[nc].s = mode == OR_SEL_MAX ? best / sqrt((double)d) : dot / sqrt((double)d);
             cs[nc].j = (int32_t)j;
-            if (out_scores && j < score_stride)
-                out_scores[r * score_stride + j] = cs[nc].s;
             nc++;
         }
+        if (mode == OR_SEL_SOFTMAX) {
+            /* S_j = sum over heads of exp(l_hj - m_h) / Z_h over the row's candidates */
+            for (int64_t x = 0; x < nc; x++)
+                cs[x].s = 0.0;
+            for (int hh = 0; hh < G; hh++) {
+                double m = -INFINITY, z = 0.0;
+                for (int64_t x = 0; x < nc; x++)
+                    if (lg[x * G + hh] > m)
+                        m = lg[x * G + hh];
+                for (int64_t x = 0; x < nc; x++)
+                    z += exp(lg[x * G + hh] - m);
+                for (int64_t x = 0; x < nc; x++)
+                    cs[x].s += exp(lg[x * G + hh] - m) / z;
+            }
+        }
+        if (out_scores)
+            for (int64_t x = 0; x < nc; x++)
+                if (cs[x].j < score_stride)
+                    out_scores[r * score_stride + cs[x].j] = cs[x].s;
         qsort(cs, (size_t)nc, sizeof(cand), cand_order);
         int64_t kr = topk_per_seq ? topk_per_seq[b] : topk;
         int64_t ns = kr < nc ? kr : nc;
@@ -267,10 +323,20 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
             out_sk[r] = ns >= 1 ? cs[ns - 1].s : NAN;
         if (out_sk1)
             out_sk1[r] = nc > ns ? cs[ns].s : NAN;
-        if (out_floor)
-            out_floor[r] = 1e-6 * qnorm * kmax / sqrt((double)d);
+        if (out_floor) {
+            /* the size of fp32 rounding in a score: dot products of these norms, and for
+               SOFTMAX the logit error carried into the largest selected probability sum */
+            if (mode == OR_SEL_SUM)
+                out_floor[r] = 1e-6 * qnorm * kmax / sqrt((double)d);
+            else if (mode == OR_SEL_MAX)
+                out_floor[r] = 1e-6 * qhmax * kmax / sqrt((double)d);
+            else
+                out_floor[r] = 4e-6 * qhmax * kmax / tau * (ns >= 1 ? cs[0].s : 0.0);
+        }
+        free(lg);
         free(cs);
         free(qs);
+        free(qh);
     }
     return bad;
 }

@@ -17,7 +17,13 @@ disagrees with what the mathematics or the pages fix:
   * Q = 0 (uniform weights: the output is the plain mean of V over the set,
     which fixes the set's size and forbids double counting) and V constant;
   * the S3R draft count |A| = keep + t + 1 for draft t;
-  * hand-derived worked examples under tests/golden/.
+  * hand-derived worked examples under tests/golden/;
+  * overlapping pooling windows: ramp mid-points and token counts in closed
+    form, and disjoint pooling again at overlap 0;
+  * the group-score variants: a hand-worked two-head example whose three
+    modes pick different blocks, one head (every mode ranks like the sum),
+    the softmax scores summing to the group size, and a very large softmax
+    temperature ranking like the sum.
 
 ``tests/test_oracle_mutants.py`` plants mistakes in copies of oracle.c and
 checks that at least one of these pins fails for each.
@@ -33,7 +39,8 @@ import numpy as np
 import torch
 
 import oracle
-from workloads import DTYPE_BF16, DTYPE_F32, POOL_L2SUM, POOL_MEAN, Workload, generate, small
+from workloads import (DTYPE_BF16, DTYPE_F32, POOL_L2SUM, POOL_MEAN, SELECT_MAX, SELECT_SOFTMAX, SELECT_SUM,
+                       Workload, generate, small)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -161,6 +168,90 @@ def pin_compress_l2sum():
         n_j = min(g, w.total_k - j * g)
         assert np.linalg.norm(out[0, 0, j]) <= n_j + 1e-12
     assert abs(np.linalg.norm(out[0, 0, 0]) - g) < 1e-12          # equality for parallel keys
+
+
+def pin_compress_overlap_closed_forms():
+    """Windows [max(0, jg - o), e_j]: a ramp pools to the window's mid-point (MEAN), and
+    positive multiples of one direction sum to the window's token count (L2SUM)."""
+    g, n, o = 4, 23, 3
+    a = np.array([1.0, -2.0, 0.5])
+    bb = np.array([0.25, 1.0, -0.125])
+    t = np.arange(n)[:, None]
+    k = (a + t * bb).astype(np.float32)[:, None, :]
+    w = wl(h_q=1, h_kv=1, head_dim=3, seqlens_k=[n], seqlens_q=[1], block=g, pool_overlap=o)
+    out = oracle.compress(w, k)
+    for j in range(-(-n // g)):
+        t0, t1 = max(0, j * g - o), min((j + 1) * g, n) - 1
+        np.testing.assert_allclose(out[0, 0, j], a + 0.5 * (t0 + t1) * bb, rtol=1e-13, atol=1e-13)
+    kp = ((t + 1) * np.array([0.0, 2.0, 0.0])).astype(np.float32)[:, None, :]
+    w2 = w.scaled(pool=POOL_L2SUM)
+    out2 = oracle.compress(w2, kp)
+    for j in range(-(-n // g)):
+        cnt = min((j + 1) * g, n) - max(0, j * g - o)
+        np.testing.assert_allclose(out2[0, 0, j], [0.0, cnt, 0.0], rtol=1e-14, atol=0)
+    # overlap 0 is the disjoint pooling
+    x = generate(wl(dtype=DTYPE_BF16, h_q=2, h_kv=1, head_dim=8, seqlens_k=[50], seqlens_q=[1], block=8))
+    w3 = wl(dtype=DTYPE_BF16, h_q=2, h_kv=1, head_dim=8, seqlens_k=[50], seqlens_q=[1], block=8)
+    np.testing.assert_array_equal(oracle.compress(w3, x["k"]), oracle.compress(w3.scaled(pool_overlap=0), x["k"]))
+
+
+def _two_head_example(mode, tau=0.0, topk=1):
+    """Token-level selection (g = 1) of one query at position 3 with heads q_0 = (1, 0),
+    q_1 = (0, 1) over candidate keys (3, 0), (2, 2), (0, 2.5); token 3 is the window."""
+    w = wl(h_q=2, h_kv=1, head_dim=2, seqlens_k=[4], seqlens_q=[1], block=1, topk=topk, n_init=0,
+           window=1, select_mode=mode, select_tau=tau)
+    q = np.array([[[1.0, 0.0], [0.0, 1.0]]], dtype=np.float32)
+    k = np.array([[[3.0, 0.0]], [[2.0, 2.0]], [[0.0, 2.5]], [[9.0, 9.0]]], dtype=np.float32)
+    return oracle.select(w, q, None, k, want_scores=True)
+
+
+def pin_select_modes_worked_example():
+    """Per-head scores (3, 0), (2, 2), (0, 2.5): the sum ranks (4, 3, 2.5), the max (3, 2.5, 2);
+    the softmax sum at tau = 1 is sum_h e^{l_hj} / sum_i e^{l_hi}."""
+    r = _two_head_example(SELECT_SUM, topk=2)
+    np.testing.assert_allclose(r["scores"][0, :3], np.array([3.0, 4.0, 2.5]) / math.sqrt(2), rtol=1e-14)
+    assert list(r["idx"][0]) == [0, 1]
+    r = _two_head_example(SELECT_MAX, topk=1)
+    np.testing.assert_allclose(r["scores"][0, :3], np.array([3.0, 2.0, 2.5]) / math.sqrt(2), rtol=1e-14)
+    assert list(r["idx"][0]) == [0]
+    r = _two_head_example(SELECT_MAX, topk=2)
+    assert list(r["idx"][0]) == [0, 2]
+    l0, l1 = [3.0, 2.0, 0.0], [0.0, 2.0, 2.5]
+    z0, z1 = sum(math.exp(x) for x in l0), sum(math.exp(x) for x in l1)
+    want = [math.exp(l0[j]) / z0 + math.exp(l1[j]) / z1 for j in range(3)]
+    r = _two_head_example(SELECT_SOFTMAX, tau=1.0, topk=2)
+    np.testing.assert_allclose(r["scores"][0, :3], want, rtol=1e-13)
+    assert list(r["idx"][0]) == [0, 2]
+    r = _two_head_example(SELECT_SOFTMAX, tau=50.0, topk=1)     # nearly uniform: ranks like the sum
+    assert list(r["idx"][0]) == [1]
+
+
+def pin_select_modes_one_head():
+    """One head per group: max over one head is that head, and a softmax is increasing in
+    its logit, so every mode selects what the sum selects."""
+    w = small("bf16_decode_32k").scaled(h_q=8, h_kv=8, topk=9)
+    x = generate(w)
+    kc = oracle.compress(w, x["k"])
+    ref = oracle.select(w, x["q"], kc, x["k"])
+    for mode, tau in ((SELECT_MAX, 0.0), (SELECT_SOFTMAX, 0.0), (SELECT_SOFTMAX, 0.3)):
+        got = oracle.select(w.scaled(select_mode=mode, select_tau=tau), x["q"], kc, x["k"])
+        np.testing.assert_array_equal(got["n"], ref["n"])
+        np.testing.assert_array_equal(got["idx"], ref["idx"])
+
+
+def pin_select_softmax_invariants():
+    """Every head's softmax over the candidates sums to one, so the scores of a row sum to
+    the group size; a very large temperature ranks like the sum of logits."""
+    w = small("bf16_decode_32k").scaled(topk=6, select_mode=SELECT_SOFTMAX)
+    x = generate(w)
+    kc = oracle.compress(w, x["k"])
+    r = oracle.select(w, x["q"], kc, x["k"], want_scores=True)
+    tot = np.nansum(r["scores"], axis=1)
+    ok = r["ncand"] > 0
+    np.testing.assert_allclose(tot[ok], w.group, rtol=1e-12)
+    big = oracle.select(w.scaled(select_tau=1e7), x["q"], kc, x["k"])
+    ref = oracle.select(w.scaled(select_mode=SELECT_SUM), x["q"], kc, x["k"])
+    np.testing.assert_array_equal(big["idx"], ref["idx"])
 
 
 # ------------------------------------------------------------------ select

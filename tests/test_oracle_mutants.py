@@ -19,10 +19,21 @@ MUTANTS = {
     "l2_no_normalise": ("scale = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;", "scale = 1.0;"),
     "compress_head0": ("int64_t row = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;",
                        "int64_t row = ((cu_k[b] + t) * h_kv) * (int64_t)d;"),
-    "score_drops_head": ("for (int h = c * G; h < (c + 1) * G; h++)",
-                         "for (int h = c * G; h < (c + 1) * G - 1; h++)"),
-    "score_wrong_block": ("kv = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];",
-                          "kv = k_cmp[(((int64_t)c * batch + b) * nb_max + (j > 0 ? j - 1 : j)) * d + e];"),
+    "score_drops_head": ("for (int hh = 0; hh < G; hh++)\n            for (int e = 0; e < d; e++)\n"
+                         "                qs[e] += qh[hh * d + e];",
+                         "for (int hh = 0; hh < G - 1; hh++)\n            for (int e = 0; e < d; e++)\n"
+                         "                qs[e] += qh[hh * d + e];"),
+    "score_wrong_block": ("kv[e] = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];",
+                          "kv[e] = k_cmp[(((int64_t)c * batch + b) * nb_max + (j > 0 ? j - 1 : j)) * d + e];"),
+    "overlap_ignored": ("int64_t t0 = j * g - overlap,", "int64_t t0 = j * g,"),
+    "overlap_forward": ("t1 = (j + 1) * (int64_t)g;\n        double *out", "t1 = (j + 1) * (int64_t)g + overlap;\n        double *out"),
+    "max_is_sum": ("cs[nc].s = mode == OR_SEL_MAX ? best / sqrt((double)d) : dot / sqrt((double)d);",
+                   "cs[nc].s = dot / sqrt((double)d);"),
+    "max_takes_min": ("else if (dh > best)", "else if (dh < best || best == -INFINITY)"),
+    "softmax_no_tau": ("lg[nc * G + hh] = dh / tau;", "lg[nc * G + hh] = dh;"),
+    "softmax_unshifted_sum": ("z += exp(lg[x * G + hh] - m);", "z += exp(lg[x * G + hh]);"),
+    "softmax_one_head": ("for (int hh = 0; hh < G; hh++) {\n                double m = -INFINITY, z = 0.0;",
+                         "for (int hh = 0; hh < 1; hh++) {\n                double m = -INFINITY, z = 0.0;"),
     "ties_to_higher": ("return (x->j > y->j) - (x->j < y->j);", "return (x->j < y->j) - (x->j > y->j);"),
     "ascending_scores": ("if (x->s > y->s)\n        return -1;", "if (x->s < y->s)\n        return -1;"),
     "visibility_off_by_one": ("if (t1 > p_sel)\n                continue;", "if (t1 > p_sel + 1)\n                continue;"),

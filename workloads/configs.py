@@ -26,6 +26,11 @@ from typing import List, Optional
 POOL_MEAN = 0
 POOL_L2SUM = 1
 
+# how a GQA group's heads combine into one block score
+SELECT_SUM = 0        # the heads' queries summed into one selector query
+SELECT_SOFTMAX = 1    # sum over heads of each head's softmax over the candidates (temperature tau)
+SELECT_MAX = 2        # max over heads of the per-head score
+
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
@@ -46,6 +51,9 @@ class Workload:
     window: int
     shared_selection: int = 0  # 1: one selection per sequence, shared by its queries
     topk_per_seq: Optional[List[int]] = None
+    pool_overlap: int = 0      # o: each block's pooling window reaches o tokens back (kernel g + o, stride g)
+    select_mode: int = SELECT_SUM
+    select_tau: float = 0.0    # softmax temperature of SELECT_SOFTMAX; 0 = sqrt(d)
     structure: str = "iid"     # iid | hot_blocks | lowrank | needles
     seed: int = 0
     # structure knobs

@@ -41,7 +41,8 @@ def make_params(w, device, layout=None):
     return sa.Params.from_lengths(w.seqlens_q, w.seqlens_k, device=device, h_q=w.h_q, h_kv=w.h_kv,
                                   head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk,
                                   n_init=w.n_init, window=w.window, shared_selection=w.shared_selection,
-                                  topk_per_seq=w.topk_per_seq, dtype=dt,
+                                  topk_per_seq=w.topk_per_seq, dtype=dt, pool_overlap=w.pool_overlap,
+                                  select_mode=w.select_mode, select_tau=w.select_tau,
                                   block_table=None if layout is None else layout.block_table.to(device),
                                   page_size=0 if layout is None else layout.page_size)
 
@@ -452,6 +453,11 @@ def main():
     ap.add_argument("--workload", default="bf16_decode_32k", choices=sorted(FULL))
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep K and V in a paged cache of this many tokens per page (0: packed)")
+    ap.add_argument("--select-mode", choices=["sum", "softmax", "max"], default="sum",
+                    help="group score of the selector: heads summed (default), sum of per-head softmaxes, "
+                         "max over heads")
+    ap.add_argument("--pool-overlap", type=int, default=0,
+                    help="pooling windows reach this many tokens before their block (0: disjoint)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -476,7 +482,8 @@ def main():
 
     device = "cuda"
     torch.cuda.set_device(0)
-    w = FULL[args.workload]()
+    w = FULL[args.workload]().scaled(select_mode={"sum": 0, "softmax": 1, "max": 2}[args.select_mode],
+                                     pool_overlap=args.pool_overlap)
     x = generate(w, device=device)
     torch.cuda.synchronize()
     if args.copy_probe_mib:
@@ -581,6 +588,7 @@ def main():
                    "max_k": w.max_k, "queries": w.total_q, "block": w.block, "topk": w.topk,
                    "n_init": w.n_init, "window": w.window, "kv_layout": (f"paged{args.page_size}" if args.page_size
                                                                           else "packed"),
+                   "select_mode": args.select_mode, "pool_overlap": w.pool_overlap,
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "attn_kernel_ms": round(attn_ms, 5),

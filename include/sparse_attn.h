@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 2
+#define SPARSE_ATTN_ABI_VERSION 3
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -70,6 +70,15 @@ typedef enum sa_status {
 
 typedef enum sa_dtype { SA_DTYPE_F32 = 0, SA_DTYPE_BF16 = 1 } sa_dtype;
 typedef enum sa_pool { SA_POOL_MEAN = 0, SA_POOL_L2SUM = 1 } sa_pool;
+
+/* How the query heads of a GQA group combine into one block score. */
+typedef enum sa_select_mode {
+    SA_SELECT_SUM = 0,     /* (sum_h q_h) . K~_j / sqrt(d): the heads summed into one selector query */
+    SA_SELECT_SOFTMAX = 1, /* sum_h softmax_j(q_h . K~_j / tau) over the row's candidates (SparDA
+                              summary, Method: the target score of its indexer)                  */
+    SA_SELECT_MAX = 2      /* max_h q_h . K~_j / sqrt(d) (LSA deep-read, §2.5: a bucket scored by
+                              its best head)                                                       */
+} sa_select_mode;
 
 typedef struct sa_params {
     int32_t batch;             /* B >= 1 sequences                                      */
@@ -106,6 +115,13 @@ typedef struct sa_params {
     const int32_t *block_table; /* device [batch, max_pages] int32 page ids, or NULL  */
     int32_t max_pages;         /* row stride of block_table; >= ceil(max_k / page_size) */
     int32_t page_size;         /* tokens per page: a power of two, 1 .. 2^20           */
+    /* Selector variants (zero = the definitions above). */
+    int32_t pool_overlap;      /* o >= 0: block j pools tokens [max(0, j*g - o), e_j], a window of
+                                  g + o tokens at stride g (InfLLM-V2's overlapping compressed keys,
+                                  SparDA summary, Method); block j is still tokens [j*g, e_j]      */
+    int32_t select_mode;       /* sa_select_mode; with several queries in a row, q_h sums head h
+                                  over them                                                       */
+    float select_temperature;  /* tau of SA_SELECT_SOFTMAX; 0 => sqrt(head_dim)                    */
 } sa_params;
 
 /* SPARSE_ATTN_ABI_VERSION of the built library. */
@@ -129,7 +145,8 @@ sa_status sparse_attn_workspace_size(const sa_params *p, size_t *select_bytes, s
  *   k      [total_k, h_kv, d] of dtype
  *   k_cmp  [h_kv, batch, nbmax, d] fp32, nbmax = ceil(max_k / block); block j of
  *          sequence b holds the mean (SA_POOL_MEAN) or the sum of k/|k|_2
- *          (SA_POOL_L2SUM, a zero key adds zero) over the block's tokens, the
+ *          (SA_POOL_L2SUM, a zero key adds zero) over the block's pooling
+ *          window (its tokens and the pool_overlap tokens before them), the
  *          last block of a sequence over the tokens it has.  Rows
  *          j >= ceil(N_b / block) are not written. */
 sa_status sparse_attn_compress(const sa_params *p, const void *k, float *k_cmp, void *stream);

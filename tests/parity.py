@@ -43,7 +43,8 @@ def params_for(w, device="cuda"):
     return sa.Params.from_lengths(w.seqlens_q, w.seqlens_k, device=device, h_q=w.h_q, h_kv=w.h_kv,
                                   head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk,
                                   n_init=w.n_init, window=w.window, shared_selection=w.shared_selection,
-                                  topk_per_seq=w.topk_per_seq, dtype=dt)
+                                  topk_per_seq=w.topk_per_seq, dtype=dt, pool_overlap=w.pool_overlap,
+                                  select_mode=w.select_mode, select_tau=w.select_tau)
 
 
 def run_gpu(w, xg, p=None):

@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 2
+    assert sa.abi_version() == 3
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -82,6 +82,9 @@ def test_status_strings():
     ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID),
     ("n_init", -2, INVALID), ("window", 0, INVALID), ("shared_selection", 2, INVALID), ("dtype", 5, INVALID),
     ("softmax_scale", -1.0, INVALID), ("softmax_scale", float("inf"), INVALID),
+    ("pool_overlap", -1, INVALID), ("pool_overlap", (1 << 20) + 1, INVALID), ("select_mode", 3, INVALID),
+    ("select_mode", -1, INVALID), ("select_temperature", -0.5, INVALID),
+    ("select_temperature", float("inf"), INVALID),
     ("h_q", 2 * 65, UNSUPPORTED)])
 def test_validate_rejects(field, value, code):
     p = params(**{field: value})
@@ -137,6 +140,9 @@ def test_workspace_sizes():
     assert sel == 2 * 2 * 20000 * 4
     # k = 0: nothing to score
     assert _ws(params(topk=0))[0] == 0
+    # per-head group scores: order keys of every (row, block); SOFTMAX also keeps every head's logit
+    assert _ws(params(select_mode=2))[0] == 2 * 2 * 64 * 4
+    assert _ws(params(select_mode=1))[0] == 2 * 2 * 64 * 4 * (1 + 4)
 
 
 def test_calls_reject_null_and_misaligned_pointers():

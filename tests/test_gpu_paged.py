@@ -39,7 +39,8 @@ def paged_params(w, layout, seqlens_k=None, seqlens_q=None, max_k=None):
     p = sa.Params.from_lengths(seqlens_q or w.seqlens_q, seqlens_k or w.seqlens_k, device="cuda", h_q=w.h_q,
                                h_kv=w.h_kv, head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk,
                                n_init=w.n_init, window=w.window, shared_selection=w.shared_selection,
-                               topk_per_seq=w.topk_per_seq, dtype=_dt(w),
+                               topk_per_seq=w.topk_per_seq, dtype=_dt(w), pool_overlap=w.pool_overlap,
+                               select_mode=w.select_mode, select_tau=w.select_tau,
                                block_table=None if layout is None else layout.block_table.cuda(),
                                page_size=0 if layout is None else layout.page_size)
     if max_k is not None:

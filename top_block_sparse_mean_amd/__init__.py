@@ -25,10 +25,12 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
-                   SA_POOL_MEAN, SaParams, SparseAttnError, check, lib)
+                   SA_POOL_MEAN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaParams, SparseAttnError,
+                   check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select", "fwd",
-           "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "LIB_PATH", "EXPORTS"]
+           "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
+           "SA_SELECT_MAX", "LIB_PATH", "EXPORTS"]
 
 _DT = {torch.float32: SA_DTYPE_F32, torch.bfloat16: SA_DTYPE_BF16}
 
@@ -51,9 +53,13 @@ class Params:
                  block: int, topk: int, n_init: int, window: int, dtype=torch.bfloat16,
                  pool: int = SA_POOL_MEAN, shared_selection: int = 0,
                  topk_per_seq: Optional[torch.Tensor] = None, q_pos0: Optional[torch.Tensor] = None,
-                 softmax_scale: float = 0.0, block_table: Optional[torch.Tensor] = None, page_size: int = 0):
+                 softmax_scale: float = 0.0, block_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                 pool_overlap: int = 0, select_mode: int = SA_SELECT_SUM, select_tau: float = 0.0):
         """block_table: int32 [batch, max_pages] page ids of a paged K/V cache (K and V
-        arguments are then page pools [pages * page_size, h_kv, d]); None = packed K/V."""
+        arguments are then page pools [pages * page_size, h_kv, d]); None = packed K/V.
+        pool_overlap / select_mode / select_tau: the selector variants (overlapping pooling
+        windows; the group score as a sum of per-head softmaxes at temperature tau, or as
+        the max over heads)."""
         self._keep = (cu_seqlens_q, cu_seqlens_k, topk_per_seq, q_pos0, block_table)
         self.dtype = dtype
         s = SaParams()
@@ -67,6 +73,7 @@ class Params:
         s.n_init, s.window, s.shared_selection = n_init, window, shared_selection
         s.softmax_scale = softmax_scale
         s.dtype = _DT[dtype]
+        s.pool_overlap, s.select_mode, s.select_temperature = pool_overlap, select_mode, select_tau
         if block_table is not None:
             if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
                 raise ValueError("block_table must be a contiguous int32 [batch, max_pages] tensor")

@@ -78,6 +78,12 @@ sa_status check_params(const sa_params *p)
         return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
     if (!(p->softmax_scale >= 0.f) || std::isinf(p->softmax_scale))
         return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (p->pool_overlap < 0 || p->pool_overlap > (1 << 20))
+        return fail(SA_ERR_INVALID_ARG, "pool_overlap must be in [0, 2^20] (got %d)", p->pool_overlap);
+    if (p->select_mode != SA_SELECT_SUM && p->select_mode != SA_SELECT_SOFTMAX && p->select_mode != SA_SELECT_MAX)
+        return fail(SA_ERR_INVALID_ARG, "unknown select_mode %d", p->select_mode);
+    if (!(p->select_temperature >= 0.f) || std::isinf(p->select_temperature))
+        return fail(SA_ERR_INVALID_ARG, "select_temperature must be finite and >= 0");
     if (p->block_table) {
         const int ps = p->page_size;
         if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)) != 0)
@@ -117,6 +123,12 @@ sa::KP make_kp(const sa_params *p)
     k.nb_max = (p->max_k + p->block - 1) / p->block;
     k.rows = p->shared_selection ? p->batch : p->total_q;
     k.dtype = p->dtype;
+    k.pool_overlap = p->pool_overlap;
+    k.select_mode = p->select_mode;
+    // per-head score scale: 1/tau for the softmax sum, 1/sqrt(d) otherwise
+    k.head_score_scale = p->select_mode == SA_SELECT_SOFTMAX && p->select_temperature > 0.f
+                             ? 1.0f / p->select_temperature
+                             : 1.0f / std::sqrt((float)p->head_dim);
     k.block_table = p->block_table;
     k.max_pages = p->block_table ? p->max_pages : 0;
     k.page_shift = 0;

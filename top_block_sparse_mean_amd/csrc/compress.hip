@@ -1,8 +1,10 @@
 // compress.hip -- pooled keys, one streaming pass over K.
 //
-// K~_j = mean of the keys of block j (SparDA summary, Method: InfLLM-V2 pools
-// keys by a parameter-free mean), or the sum of the L2-normalised keys (LSA
-// deep-read, §2.2).  Blocks are g consecutive tokens of one KV head, stride g.
+// K~_j = mean of the keys of block j's pooling window (SparDA summary, Method:
+// InfLLM-V2 pools keys by a parameter-free mean into overlapping compressed
+// keys), or the sum of the L2-normalised keys (LSA deep-read, §2.2).  Block j
+// is g consecutive tokens of one KV head, stride g; its window reaches
+// pool_overlap tokens further back (clipped at token 0).
 //
 // Mapping: one thread owns 8 consecutive head-dim elements of one pooled
 // vector.  Threads are numbered chunk-fastest, then KV head, then block, then
@@ -31,8 +33,8 @@ __device__ __forceinline__ bool pooled_block(const KP &P, const Seq &s, int mode
     } else if (mode == kPoolTail) {
         j = nb - n_blk_iter + jj;
     } else {
-        j = s.q0 / P.g + jj;
-        last = s.n_q > 0 ? min(last, (s.q0 + s.n_q - 1) / P.g) : -1;
+        j = s.q0 / P.g + jj;          // a token also lies in the windows of the blocks up to o tokens after it
+        last = s.n_q > 0 ? min(last, (s.q0 + s.n_q - 1 + P.pool_overlap) / P.g) : -1;
     }
     return j >= 0 && j <= last && j < P.nb_max;
 }
@@ -61,10 +63,10 @@ __global__ __launch_bounds__(256) void compress_kernel(KP P, const T *__restrict
         map = kv_map(P, b);
         live = pooled_block(P, s, mode, n_blk_iter, jj, j);
     }
-    int t0 = j * P.g;
-    int t1 = min(t0 + P.g, n_k);
+    int t0 = max(0, j * P.g - P.pool_overlap);          // the block's pooling window [t0, t1)
+    int t1 = min(j * P.g + P.g, n_k);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int it = 0; it < P.g; it++) {
+    for (int it = 0; it < P.g + P.pool_overlap; it++) {
         int t = t0 + it;
         bool ok = live && t < t1;
         float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -114,9 +116,9 @@ __global__ __launch_bounds__(256) void compress_few_kernel(KP P, const T *__rest
     int j;
     if (!pooled_block(P, s, mode, n_blk_iter, jj, j))
         return;
-    const int t0 = j * P.g, t1 = min(t0 + P.g, n_k);
+    const int t0 = max(0, j * P.g - P.pool_overlap), t1 = min(j * P.g + P.g, n_k);   // pooling window
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int it = 0; it < P.g; it += TG) {
+    for (int it = 0; it < P.g + P.pool_overlap; it += TG) {
         int t = t0 + it + tg;
         bool ok = t < t1;
         float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -217,9 +219,10 @@ __global__ __launch_bounds__(256) void append_rows_kernel(KP P, const T *__restr
     }
 }
 
-// With pooling: one workgroup per (sequence, KV head, block holding a new token).
-// The block's new tokens are taken from k_new / v_new and written to the cache;
-// its other tokens are read from the cache; the block is pooled exactly as
+// With pooling: one workgroup per (sequence, KV head, block whose pooling window
+// holds a new token).  New tokens in the window are taken from k_new / v_new
+// (and written to the cache when they belong to the block itself); its other
+// tokens are read from the cache; the window is pooled exactly as
 // compress_few_kernel pools it.  Each new (token, head) belongs to one block, so
 // every cache row is written by one workgroup, and no workgroup reads a row
 // another writes.
@@ -240,9 +243,9 @@ __global__ __launch_bounds__(256) void append_pool_kernel(KP P, const T *__restr
     int j;
     if (!pooled_block(P, s, kPoolAppended, n_blk_iter, jj, j))
         return;
-    const int t0 = j * P.g, t1 = min(t0 + P.g, s.n_k);
+    const int t0 = max(0, j * P.g - P.pool_overlap), t1 = min(j * P.g + P.g, s.n_k);   // pooling window
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int it = 0; it < P.g; it += TG) {
+    for (int it = 0; it < P.g + P.pool_overlap; it += TG) {
         const int t = t0 + it + tg;
         const bool ok = t < t1;
         float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -252,11 +255,12 @@ __global__ __launch_bounds__(256) void append_pool_kernel(KP P, const T *__restr
                 const long long nrow = (s.q_off + (t - s.q0)) * P.h_kv + c;
                 load8(k_new + nrow * D + chunk * 8, x);
                 constexpr int PPC = 8 * (int)sizeof(T) / 16;        // 16-byte pieces per 8 elements
+                if (t >= j * P.g)                                    // the block's own tokens only
 #pragma unroll
-                for (int u = 0; u < PPC; u++) {
-                    copy_piece(k_new, k, nrow, crow, D, chunk * PPC + u);
-                    copy_piece(v_new, v, nrow, crow, D, chunk * PPC + u);
-                }
+                    for (int u = 0; u < PPC; u++) {
+                        copy_piece(k_new, k, nrow, crow, D, chunk * PPC + u);
+                        copy_piece(v_new, v, nrow, crow, D, chunk * PPC + u);
+                    }
             } else {
                 load8(k + crow * D + chunk * 8, x);
             }
@@ -297,8 +301,8 @@ static hipError_t launch_append_t(const KP &P, const void *k_new, const void *v_
                                                                              (const T *)v_new, (T *)k, (T *)v);
         return hipGetLastError();
     }
-    // M consecutive tokens meet at most ceil(M / g) + 1 blocks
-    long long n_blk = (P.max_q + P.g - 1) / P.g + 1;
+    // M consecutive tokens lie in the windows of at most ceil((M + o) / g) + 1 blocks
+    long long n_blk = ((long long)P.max_q + P.pool_overlap + P.g - 1) / P.g + 1;
     if (n_blk > P.nb_max)
         n_blk = P.nb_max;
     const dim3 grid((unsigned)(P.batch * n_blk * P.h_kv));

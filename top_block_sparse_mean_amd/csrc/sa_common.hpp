@@ -26,6 +26,9 @@ struct KP {
     int dtype;          // 0 fp32, 1 bf16
     const int32_t *block_table;   // paged K/V: [batch, max_pages] page ids, or nullptr (packed)
     int max_pages, page_shift;    // block-table row stride; log2(page_size)
+    int pool_overlap;             // pooling window of block j starts at max(0, j*g - pool_overlap)
+    int select_mode;              // 0 sum of heads, 1 sum of per-head softmaxes, 2 max over heads
+    float head_score_scale;       // per-head score scale (1/tau or 1/sqrt(d))
 };
 
 struct Seq {

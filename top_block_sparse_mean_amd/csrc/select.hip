@@ -475,6 +475,161 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     }
 }
 
+// ---------------------------------------------------------------- per-head group scores
+
+// The SOFTMAX and MAX group scores need every head's own score of a block.
+// score_heads: grid (rows * n_chunk, h_kv), CH candidates per workgroup.  The
+// group's per-head selector queries (head h summed over the row's queries) sit
+// in LDS; a key row is read once and dotted with every head, each dot reduced
+// over the row's lanes.  MAX writes the order key of the best head's score
+// (scaled by 1/sqrt(d)); SOFTMAX writes every head's logit (scaled by 1/tau) to
+// ws_l[row][head][j].
+constexpr int kMaxG = 64;
+
+template <typename T, typename KT, int D, int CH>
+__global__ __launch_bounds__(256) void score_heads_kernel(KP P, const T *__restrict__ q,
+                                                          const KT *__restrict__ kbase, uint32_t *__restrict__ ws,
+                                                          float *__restrict__ ws_l, long long stride, int n_chunk)
+{
+    using RD = RowDot<KT, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L, NG = 4 * GPW;
+    constexpr int U = 64 / NG < 1 ? 1 : 64 / NG;          // 64 rows per round
+    constexpr int RW = U * NG;
+    __shared__ __attribute__((aligned(16))) float sh_q[kMaxG * D];
+    const long long row = blockIdx.x / n_chunk;
+    const int chunk = (int)(blockIdx.x % n_chunk);
+    const int c = blockIdx.y;
+    const RowGeo r = row_geo(P, row);
+    if (r.need == r.n_cand)                              // every candidate kept: no scores needed
+        return;
+    const int j0 = r.j_lo + chunk * CH;
+    const int j1 = min(j0 + CH, r.j_hi);
+    if (j0 >= j1)
+        return;
+    const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    const int rounds = (j1 - j0 + RW - 1) / RW;
+    uint4 ra[U], rb[U];
+    auto load = [&](uint4 (&raw)[U], int rd) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int j = min(j0 + rd * RW + u * NG + grp, j1 - 1);
+            raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, j))[sub];
+        }
+    };
+    load(ra, 0);
+    for (int x = tid; x < P.G * D; x += 256) {
+        const long long h = c * P.G + x / D;
+        float acc = 0.f;
+        for (long long i = r.q_first; i < r.q_last; i++) {
+            if constexpr (sizeof(T) == 2)
+                acc += bf16_to_f32(q[(i * P.h_q + h) * D + x % D]);
+            else
+                acc += q[(i * P.h_q + h) * D + x % D];
+        }
+        sh_q[x] = acc;
+    }
+    __syncthreads();
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    float *logits = ws_l + ((long long)c * P.rows + row) * P.G * stride;
+    // heads outer, rows inner: one read of a head's query slice per round
+    auto reduce = [&](const uint4 (&raw)[U], int rd) {
+        float best[U];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            best[u] = -INFINITY;
+        for (int h = 0; h < P.G; h++) {
+            float qv[VPL];
+#pragma unroll
+            for (int e = 0; e < VPL; e++)
+                qv[e] = sh_q[h * D + sub * VPL + e];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv)) * P.head_score_scale;
+                const int j = j0 + rd * RW + u * NG + grp;
+                if (P.select_mode == 2)
+                    best[u] = fmaxf(best[u], sc);
+                else if (sub == 0 && j < j1)
+                    logits[(long long)h * stride + j] = sc;
+            }
+        }
+        if (P.select_mode == 2) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = j0 + rd * RW + u * NG + grp;
+                if (sub == 0 && j < j1)
+                    keys[j] = order_key(best[u]);
+            }
+        }
+    };
+    for (int rd = 0; rd < rounds; rd += 2) {
+        if (rd + 1 < rounds)
+            load(rb, rd + 1);
+        reduce(ra, rd);
+        if (rd + 1 >= rounds)
+            break;
+        if (rd + 2 < rounds)
+            load(ra, rd + 2);
+        reduce(rb, rd + 1);
+    }
+}
+
+// Sum over a 256-thread workgroup (or max), in a fixed order: the result does not
+// depend on timing.  Every thread gets the result.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce_256(float v, float *sh)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float u = __shfl_xor(v, o, kWave);
+        v = MAX ? fmaxf(v, u) : v + u;
+    }
+    __syncthreads();                                     // sh is free
+    if (lane_id() == 0)
+        sh[threadIdx.x / kWave] = v;
+    __syncthreads();
+    return MAX ? fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3])) : (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// SOFTMAX: grid (rows, h_kv).  Per head h, m_h = max and Z_h = sum of exp(l - m_h)
+// over the row's candidates; then S_j = sum_h exp(l_hj - m_h) / Z_h, written as
+// order keys for the top-k.
+__global__ __launch_bounds__(256) void softmax_rows_kernel(KP P, const float *__restrict__ ws_l,
+                                                           uint32_t *__restrict__ ws, long long stride)
+{
+    __shared__ float sh_red[4];
+    __shared__ float sh_m[kMaxG], sh_zi[kMaxG];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y, tid = threadIdx.x;
+    const RowGeo r = row_geo(P, row);
+    if (r.need == r.n_cand)
+        return;
+    const float *lrow = ws_l + ((long long)c * P.rows + row) * P.G * stride;
+    for (int h = 0; h < P.G; h++) {
+        const float *l = lrow + (long long)h * stride;
+        float m = -INFINITY;
+        for (int j = r.j_lo + tid; j < r.j_hi; j += 256)
+            m = fmaxf(m, l[j]);
+        m = block_reduce_256<true>(m, sh_red);
+        float z = 0.f;
+        for (int j = r.j_lo + tid; j < r.j_hi; j += 256)
+            z += expf(l[j] - m);
+        z = block_reduce_256<false>(z, sh_red);
+        if (tid == 0) {
+            sh_m[h] = m;
+            sh_zi[h] = 1.0f / z;
+        }
+    }
+    __syncthreads();
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    for (int j = r.j_lo + tid; j < r.j_hi; j += 256) {
+        float sc = 0.f;
+        for (int h = 0; h < P.G; h++)
+            sc += expf(lrow[(long long)h * stride + j] - sh_m[h]) * sh_zi[h];
+        keys[j] = order_key(sc);
+    }
+}
+
 // ---------------------------------------------------------------- select_part + select_merge
 
 // Rows with at most 64*KPL candidates and few rows (decode).  select_part: the
@@ -1163,6 +1318,10 @@ size_t select_workspace_bytes(const KP &P, int plan)
 {
     if (plan == kSelectEmpty)
         return 0;
+    if (plan == kSelectHeads) {                           // order keys, and every head's logits for SOFTMAX
+        const size_t per = (size_t)P.h_kv * (size_t)P.rows * (size_t)key_stride(P) * sizeof(uint32_t);
+        return per * (P.select_mode == 1 ? 1 + (size_t)P.G : 1);
+    }
     const long long stride = plan == kSelectRow ? cand_cap(P) : key_stride(P);
     if (plan == kSelectRow) {                             // (key, position) survivors of every part
         const long long n_part = (stride + kPartCand - 1) / kPartCand;
@@ -1175,6 +1334,8 @@ int select_plan(const KP &P)
 {
     if (P.topk == 0)
         return kSelectEmpty;
+    if (P.select_mode != 0)
+        return kSelectHeads;
     bool few_rows = P.shared || P.max_q <= 8;
     long long max_cand = P.g == 1 ? P.max_k : P.nb_max;
     int plan = !few_rows ? kSelectTile : (max_cand <= kRowMaxCand ? kSelectRow : kSelectSplit);
@@ -1226,7 +1387,35 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             select_merge_kernel<16><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
         return hipGetLastError();
     }
-    if (plan == kSelectSplit) {
+    if (plan == kSelectHeads) {
+        // 128-candidate chunks while the grid would hold fewer than 1024 workgroups (decode)
+        float *ws_l = reinterpret_cast<float *>(wsk + (size_t)P.h_kv * (size_t)P.rows * (size_t)stride);
+        const bool small = P.rows * P.h_kv * ((stride + kSplitChunk - 1) / kSplitChunk) < 1024;
+        const int ch = small ? 128 : kSplitChunk;
+        const int n_chunk = (int)((stride + ch - 1) / ch);
+        dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
+        if (P.g == 1) {
+            if (small)
+                score_heads_kernel<T, T, D, 128><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, ws_l, stride,
+                                                                           n_chunk);
+            else
+                score_heads_kernel<T, T, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, ws_l,
+                                                                                   stride, n_chunk);
+        } else {
+            if (small)
+                score_heads_kernel<T, float, D, 128><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, ws_l, stride,
+                                                                               n_chunk);
+            else
+                score_heads_kernel<T, float, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, ws_l,
+                                                                                       stride, n_chunk);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        if (P.select_mode == 1)
+            softmax_rows_kernel<<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(256), 0, st>>>(P, ws_l, wsk,
+                                                                                              stride);
+    } else if (plan == kSelectSplit) {
         int n_chunk = (int)((stride + kSplitChunk - 1) / kSplitChunk);
         dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
         if (P.g == 1)

@@ -27,8 +27,14 @@
  *             of q_h.K~_j / tau, summed over the group's heads (the SparDA
  *             training target, SparDA summary, Method).  Mode MAX: the largest
  *             over the group's heads of q_h.K~_j / sqrt(d) (N-LSA scores a
- *             bucket by its best head, LSA deep-read, §2.5).  With several
- *             queries in a row, q_h sums head h over them.  Candidates are the blocks
+ *             bucket by its best head, LSA deep-read, §2.5).  Mode ATTN: the
+ *             attention mass a dense verify pass puts on the block, summed over
+ *             the row's queries i and the group's heads h: the sum over the
+ *             block's tokens t of exp(q_ih.k_t / sqrt(d) - lse_ih), lse_ih the
+ *             log-sum-exp of query i, head h over every key up to its position
+ *             (S3R review: the verifier's attention weights refresh the subset
+ *             the next drafts read).  With several queries in a row, q_h sums
+ *             head h over them (modes SUM, SOFTMAX, MAX).  Candidates are the blocks
  *             that lie wholly at or before the selection position p_sel and
  *             hold at least one token outside the init/window set F(p_sel).
  *             The k best by (score descending, block index ascending) are kept
@@ -65,6 +71,7 @@
 #define OR_SEL_SUM 0
 #define OR_SEL_SOFTMAX 1
 #define OR_SEL_MAX 2
+#define OR_SEL_ATTN 3
 
 static double elem(const void *base, int dtype, int64_t i)
 {
@@ -263,12 +270,14 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
             for (int e = 0; e < d; e++) {
                 if (g == 1)
                     kv[e] = elem(k, dtype, ((cu_k[b] + j) * h_kv + c) * (int64_t)d + e);
+                else if (mode == OR_SEL_ATTN)
+                    kv[e] = 0.0;                    /* scored from the raw keys below */
                 else
                     kv[e] = k_cmp[(((int64_t)c * batch + b) * nb_max + j) * d + e];
                 dot += qs[e] * kv[e];
                 kn += kv[e] * kv[e];
             }
-            for (int hh = 0; hh < G && mode != OR_SEL_SUM; hh++) {
+            for (int hh = 0; hh < G && (mode == OR_SEL_SOFTMAX || mode == OR_SEL_MAX); hh++) {
                 double dh = 0.0;
                 for (int e = 0; e < d; e++)
                     dh += qh[hh * d + e] * kv[e];
@@ -283,6 +292,43 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
             cs[nc].s = mode == OR_SEL_MAX ? best / sqrt((double)d) : dot / sqrt((double)d);
             cs[nc].j = (int32_t)j;
             nc++;
+        }
+        if (mode == OR_SEL_ATTN) {
+            /* every (query, head) of the row: its dense causal log-sum-exp, then the
+               attention mass it puts on each candidate block's tokens */
+            for (int64_t x = 0; x < nc; x++)
+                cs[x].s = 0.0;
+            double q0b = (double)first_query_pos(b, cu_q, cu_k, q_pos0);
+            for (int64_t i = qa; i < qb; i++) {
+                int64_t p_i = (int64_t)q0b + (i - cu_q[b]);
+                if (p_i > n_b - 1)
+                    p_i = n_b - 1;
+                for (int hh = 0; hh < G; hh++) {
+                    int64_t qoff = (i * h_q + c * G + hh) * (int64_t)d;
+                    double *lgt = (double *)malloc(sizeof(double) * (size_t)(p_i + 1 > 0 ? p_i + 1 : 1));
+                    double m = -INFINITY, z = 0.0;
+                    for (int64_t t = 0; t <= p_i; t++) {
+                        int64_t koff = ((cu_k[b] + t) * h_kv + c) * (int64_t)d;
+                        double dot = 0.0;
+                        for (int e = 0; e < d; e++)
+                            dot += elem(q_sel, dtype, qoff + e) * elem(k, dtype, koff + e);
+                        lgt[t] = dot / sqrt((double)d);
+                        if (lgt[t] > m)
+                            m = lgt[t];
+                    }
+                    for (int64_t t = 0; t <= p_i; t++)
+                        z += exp(lgt[t] - m);
+                    double lse_ih = m + log(z);
+                    for (int64_t x = 0; x < nc; x++) {
+                        int64_t t0 = (int64_t)cs[x].j * g, t1 = t0 + g - 1;
+                        if (t1 > p_i)
+                            t1 = p_i;
+                        for (int64_t t = t0; t <= t1; t++)
+                            cs[x].s += exp(lgt[t] - lse_ih);
+                    }
+                    free(lgt);
+                }
+            }
         }
         if (mode == OR_SEL_SOFTMAX) {
             /* S_j = sum over heads of exp(l_hj - m_h) / Z_h over the row's candidates */
@@ -330,8 +376,10 @@ int or_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
                 out_floor[r] = 1e-6 * qnorm * kmax / sqrt((double)d);
             else if (mode == OR_SEL_MAX)
                 out_floor[r] = 1e-6 * qhmax * kmax / sqrt((double)d);
-            else
+            else if (mode == OR_SEL_SOFTMAX)
                 out_floor[r] = 4e-6 * qhmax * kmax / tau * (ns >= 1 ? cs[0].s : 0.0);
+            else
+                out_floor[r] = 1e-5 * (ns >= 1 ? cs[0].s : 0.0);
         }
         free(lg);
         free(cs);

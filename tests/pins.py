@@ -39,8 +39,8 @@ import numpy as np
 import torch
 
 import oracle
-from workloads import (DTYPE_BF16, DTYPE_F32, POOL_L2SUM, POOL_MEAN, SELECT_MAX, SELECT_SOFTMAX, SELECT_SUM,
-                       Workload, generate, small)
+from workloads import (DTYPE_BF16, DTYPE_F32, POOL_L2SUM, POOL_MEAN, SELECT_ATTN, SELECT_MAX, SELECT_SOFTMAX,
+                       SELECT_SUM, Workload, generate, small)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -252,6 +252,70 @@ def pin_select_softmax_invariants():
     big = oracle.select(w.scaled(select_tau=1e7), x["q"], kc, x["k"])
     ref = oracle.select(w.scaled(select_mode=SELECT_SUM), x["q"], kc, x["k"])
     np.testing.assert_array_equal(big["idx"], ref["idx"])
+
+
+def pin_select_attn_uniform_queries():
+    """Q = 0: every query spreads its mass evenly over its p_i + 1 visible tokens, so
+    block j scores sum_i G |block j| / (p_i + 1) (shared rows: 6 drafts)."""
+    g, n_hist, m = 3, 40, 6
+    w = wl(h_q=4, h_kv=2, head_dim=8, seqlens_k=[n_hist + m, 29 + m], seqlens_q=[m, m], block=g, topk=5,
+           n_init=2, window=4, shared_selection=1, select_mode=SELECT_ATTN)
+    x = generate(w.scaled(dtype=DTYPE_F32))
+    q = torch.zeros_like(x["q"])
+    r = oracle.select(w, q, None, x["k"], want_scores=True)
+    for rr, b in enumerate(r["rows"]):
+        nk = w.seqlens_k[b]
+        q0 = nk - m
+        for j in range(-(-nk // g)):
+            s = r["scores"][rr, j]
+            if np.isnan(s):
+                continue
+            size = min((j + 1) * g, nk) - j * g
+            want = sum(w.group * size / (q0 + t + 1) for t in range(m))
+            assert abs(s - want) < 1e-12 * want, (b, j, s, want)
+
+
+def pin_select_attn_worked_example():
+    """One query at position 2, one head, keys with logits (ln 4, 0, ln 3) over sqrt(d) = 1
+    (d = 1): masses 4/8, 1/8, 3/8 of which tokens 0 and 1 are candidates (window 1)."""
+    w = wl(h_q=1, h_kv=1, head_dim=1, seqlens_k=[3], seqlens_q=[1], block=1, topk=1, n_init=0, window=1,
+           select_mode=SELECT_ATTN)
+    q = torch.tensor([[[1.0]]], dtype=torch.float32)
+    k = torch.tensor([[[math.log(4.0)]], [[0.0]], [[math.log(3.0)]]], dtype=torch.float32)
+    r = oracle.select(w, q, None, k, want_scores=True)
+    kf = k.double().numpy().reshape(-1)
+    z = np.exp(kf).sum()
+    np.testing.assert_allclose(r["scores"][0, :2], np.exp(kf[:2]) / z, rtol=1e-14)
+    assert list(r["idx"][0]) == [0]
+    np.testing.assert_allclose(np.exp(kf) / z, [0.5, 0.125, 0.375], rtol=1e-6)
+
+
+def pin_select_attn_shift_invariance():
+    """Adding to every key a vector orthogonal to every query leaves every softmax, hence
+    every mass and the selection, unchanged."""
+    w = wl(dtype=DTYPE_F32, h_q=2, h_kv=1, head_dim=8, seqlens_k=[70], seqlens_q=[3], block=2, topk=6,
+           n_init=1, window=5, shared_selection=1, select_mode=SELECT_ATTN)
+    x = generate(w)
+    q = x["q"].clone()
+    q[..., 7] = 0.0                            # every query lies in the first 7 dimensions
+    k2 = x["k"].clone()
+    k2[..., 7] += 3.0                          # so this shift is orthogonal to all of them
+    a = oracle.select(w, q, None, x["k"], want_scores=True)
+    b = oracle.select(w, q, None, k2, want_scores=True)
+    np.testing.assert_allclose(b["scores"], a["scores"], rtol=1e-12, atol=0)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+
+
+def pin_select_attn_one_query_ranks_by_dot():
+    """One query and one head per row: exp(l_t - lse) is increasing in the logit, so the
+    selection is the dot-product selection (g = 1)."""
+    w = wl(dtype=DTYPE_BF16, h_q=3, h_kv=3, head_dim=16, seqlens_k=[300, 123], seqlens_q=[1, 1], block=1,
+           topk=17, n_init=4, window=8)
+    x = generate(w)
+    ref = oracle.select(w, x["q"], None, x["k"])
+    got = oracle.select(w.scaled(select_mode=SELECT_ATTN), x["q"], None, x["k"])
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    np.testing.assert_array_equal(got["n"], ref["n"])
 
 
 # ------------------------------------------------------------------ select

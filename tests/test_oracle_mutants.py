@@ -32,6 +32,13 @@ MUTANTS = {
     "max_takes_min": ("else if (dh > best)", "else if (dh < best || best == -INFINITY)"),
     "softmax_no_tau": ("lg[nc * G + hh] = dh / tau;", "lg[nc * G + hh] = dh;"),
     "softmax_unshifted_sum": ("z += exp(lg[x * G + hh] - m);", "z += exp(lg[x * G + hh]);"),
+    "attn_no_lse": ("cs[x].s += exp(lgt[t] - lse_ih);", "cs[x].s += exp(lgt[t] - m);"),
+    "attn_causal_short": ("for (int64_t t = 0; t <= p_i; t++)\n                        z += exp(lgt[t] - m);",
+                          "for (int64_t t = 0; t < p_i; t++)\n                        z += exp(lgt[t] - m);"),
+    "attn_block_first_token": ("int64_t t0 = (int64_t)cs[x].j * g, t1 = t0 + g - 1;",
+                               "int64_t t0 = (int64_t)cs[x].j * g, t1 = t0;"),
+    "attn_last_query_only": ("for (int64_t i = qa; i < qb; i++) {\n                int64_t p_i",
+                             "for (int64_t i = qb - 1; i < qb; i++) {\n                int64_t p_i"),
     "softmax_one_head": ("for (int hh = 0; hh < G; hh++) {\n                double m = -INFINITY, z = 0.0;",
                          "for (int hh = 0; hh < 1; hh++) {\n                double m = -INFINITY, z = 0.0;"),
     "ties_to_higher": ("return (x->j > y->j) - (x->j < y->j);", "return (x->j < y->j) - (x->j > y->j);"),

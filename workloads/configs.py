@@ -30,6 +30,7 @@ POOL_L2SUM = 1
 SELECT_SUM = 0        # the heads' queries summed into one selector query
 SELECT_SOFTMAX = 1    # sum over heads of each head's softmax over the candidates (temperature tau)
 SELECT_MAX = 2        # max over heads of the per-head score
+SELECT_ATTN = 3       # attention mass of a dense verify pass (every query and head of the row)
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 3
+#define SPARSE_ATTN_ABI_VERSION 4
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -76,8 +76,13 @@ typedef enum sa_select_mode {
     SA_SELECT_SUM = 0,     /* (sum_h q_h) . K~_j / sqrt(d): the heads summed into one selector query */
     SA_SELECT_SOFTMAX = 1, /* sum_h softmax_j(q_h . K~_j / tau) over the row's candidates (SparDA
                               summary, Method: the target score of its indexer)                  */
-    SA_SELECT_MAX = 2      /* max_h q_h . K~_j / sqrt(d) (LSA deep-read, §2.5: a bucket scored by
+    SA_SELECT_MAX = 2,     /* max_h q_h . K~_j / sqrt(d) (LSA deep-read, §2.5: a bucket scored by
                               its best head)                                                       */
+    SA_SELECT_ATTN = 3     /* the attention mass a dense verify pass puts on block j: the sum over
+                              the row's queries i, the group's heads h and the block's tokens t of
+                              exp(scale q_ih . k_t - lse_ih), lse from that pass (S3R review: the
+                              verifier's attention refreshes the next drafts' subset); reads the
+                              raw keys                                                            */
 } sa_select_mode;
 
 typedef struct sa_params {
@@ -122,6 +127,10 @@ typedef struct sa_params {
     int32_t select_mode;       /* sa_select_mode; with several queries in a row, q_h sums head h
                                   over them                                                       */
     float select_temperature;  /* tau of SA_SELECT_SOFTMAX; 0 => sqrt(head_dim)                    */
+    const float *attn_lse;     /* SA_SELECT_ATTN: device [h_q, total_q] natural-log log-sum-exp of
+                                  each (query, head) over every key up to its position, as
+                                  sparse_attn_fwd writes it for a table that keeps every candidate;
+                                  the row's queries times G must be <= 64                          */
 } sa_params;
 
 /* SPARSE_ATTN_ABI_VERSION of the built library. */
@@ -181,8 +190,10 @@ sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const voi
  *   q_sel  [total_q, h_q, d] of dtype: the selector queries (Q itself, or a
  *          separate selector projection of the same shape)
  *   k_cmp  pooled keys from sparse_attn_compress; ignored when block == 1 (the
- *          raw keys `k` are scored) and may then be NULL
- *   k      [total_k, h_kv, d]; read only when block == 1 (else may be NULL)
+ *          raw keys `k` are scored) or select_mode == SA_SELECT_ATTN, and may then
+ *          be NULL
+ *   k      [total_k, h_kv, d] (or the paged pool); read when block == 1 or
+ *          select_mode == SA_SELECT_ATTN (else may be NULL)
  *   idx    [h_kv, rows, topk] int32 out: selected block indices of each row in
  *          ascending order, padded with -1; rows = total_q, or batch when
  *          shared_selection = 1

@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 3
+    assert sa.abi_version() == 4
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -82,8 +82,8 @@ def test_status_strings():
     ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID),
     ("n_init", -2, INVALID), ("window", 0, INVALID), ("shared_selection", 2, INVALID), ("dtype", 5, INVALID),
     ("softmax_scale", -1.0, INVALID), ("softmax_scale", float("inf"), INVALID),
-    ("pool_overlap", -1, INVALID), ("pool_overlap", (1 << 20) + 1, INVALID), ("select_mode", 3, INVALID),
-    ("select_mode", -1, INVALID), ("select_temperature", -0.5, INVALID),
+    ("pool_overlap", -1, INVALID), ("pool_overlap", (1 << 20) + 1, INVALID),
+    ("select_mode", -1, INVALID), ("select_mode", 4, INVALID), ("select_temperature", -0.5, INVALID),
     ("select_temperature", float("inf"), INVALID),
     ("h_q", 2 * 65, UNSUPPORTED)])
 def test_validate_rejects(field, value, code):
@@ -163,6 +163,18 @@ def test_calls_reject_null_and_misaligned_pointers():
     assert status("sparse_attn_append_kv", p, vp(FAKE), vp(FAKE + 2), vp(FAKE), vp(FAKE), None, None) == INVALID
     assert status("sparse_attn_append_kv", p, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE + 4),
                   None) == INVALID
+    # attention-mass selection: raw keys and the verify pass's lse are required; rows of
+    # more than 64 (query, head) pairs are not built
+    pa = ctypes.byref(params(select_mode=3))
+    ws = vp(FAKE)
+    assert status("sparse_attn_select", pa, vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), ws, 1 << 30,
+                  None) == INVALID
+    assert "attn_lse" in _lib.lib().sparse_attn_last_error().decode()
+    assert status("sparse_attn_select", pa, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), ws, 1 << 30,
+                  None) == INVALID
+    assert "raw keys" in _lib.lib().sparse_attn_last_error().decode()
+    big = params(select_mode=3, shared_selection=1, max_q=20, total_q=40, attn_lse=FAKE)   # 20 x 4 pairs
+    assert status("sparse_attn_validate", ctypes.byref(big)) == UNSUPPORTED
     bad = ctypes.byref(params(block_table=FAKE, page_size=5, max_pages=1000))
     assert status("sparse_attn_append_kv", bad, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None) == INVALID
 

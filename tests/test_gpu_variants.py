@@ -1,7 +1,9 @@
 """Selector variants through the C ABI against the oracle (needs an MI355X):
 overlapping pooling windows (kernel g + o, stride g), the group score as the sum
-of per-head softmaxes over the candidates, and the group score as the max over
-heads.  Every stage is compared to the bars of the default path (pooled keys,
+of per-head softmaxes over the candidates, the group score as the max over
+heads, and the S3R refresh: selection by the attention mass of a dense verify
+pass (whose lse the GPU's own dense sparse_attn_fwd provides; the oracle
+computes its own).  Every stage is compared to the bars of the default path (pooled keys,
 index sets with the near-tie rule on the mode's own scores, outputs)."""
 import numpy as np
 import pytest
@@ -10,7 +12,7 @@ import torch
 import oracle
 import parity
 import top_block_sparse_mean_amd as sa
-from workloads import FULL, SELECT_MAX, SELECT_SOFTMAX, generate, small
+from workloads import FULL, SELECT_ATTN, SELECT_MAX, SELECT_SOFTMAX, SELECT_SUM, generate, page_layout, small, to_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +98,63 @@ def test_full_decode_32k_modes_sampled(mode):
 
 def test_full_draft_decode_max_sampled():
     _sampled_decode(FULL["bf16_draft_decode"]().scaled(select_mode=SELECT_MAX), n_rows=16, n_req=256)
+
+
+def _verify_lse(w, xg, k=None, v=None, layout=None):
+    """The dense verify pass on the GPU: a table keeping every candidate, attention with lse."""
+    wd = w.scaled(select_mode=SELECT_SUM, topk=max(w.seqlens_k), topk_per_seq=None)
+    p = parity.params_for(wd) if layout is None else _paged(wd, layout)
+    k = xg["k"] if k is None else k
+    v = xg["v"] if v is None else v
+    kc = sa.compress(p, k) if wd.block > 1 else None
+    idx, n_idx = sa.select(p, xg["q"], kc, k)
+    _, lse = sa.fwd(p, xg["q"], k, v, idx, n_idx, want_lse=True)
+    return lse
+
+
+def _paged(w, layout):
+    p = parity.params_for(w)
+    return sa.Params.from_lengths(w.seqlens_q, w.seqlens_k, device="cuda", h_q=w.h_q, h_kv=w.h_kv,
+                                  head_dim=w.head_dim, block=w.block, pool=w.pool, topk=w.topk, n_init=w.n_init,
+                                  window=w.window, shared_selection=w.shared_selection,
+                                  topk_per_seq=w.topk_per_seq, dtype=p.dtype, select_mode=w.select_mode,
+                                  block_table=layout.block_table.cuda(), page_size=layout.page_size)
+
+
+@pytest.mark.parametrize("name", ["bf16_draft_decode", "bf16_decode_32k", "tiny_fp32_prefill"])
+def test_attention_mass_refresh(name):
+    """Every row's selection by verify attention mass equals the oracle's (near-tie rule on
+    the masses).  The verify pass keeps every candidate, so it is dense (window >= g here)."""
+    w = small(name).scaled(select_mode=SELECT_ATTN)
+    x, xg = parity.gen_pair(w)
+    lse = _verify_lse(w, xg)
+    p = parity.params_for(w)
+    idx, n_idx = sa.select(p, xg["q"], None, xg["k"], attn_lse=lse)
+    torch.cuda.synchronize()
+    parity.check_select(w, x, None, idx.cpu().numpy(), n_idx.cpu().numpy())
+
+
+def test_attention_mass_refresh_paged():
+    w = small("bf16_draft_decode").scaled(select_mode=SELECT_ATTN)
+    x, xg = parity.gen_pair(w)
+    layout = page_layout(w.seqlens_k, 16, w.seed + 3)
+    kp, vp = to_pages(xg["k"], layout), to_pages(xg["v"], layout)
+    lse = _verify_lse(w, xg, kp, vp, layout)
+    idx, n_idx = sa.select(_paged(w, layout), xg["q"], None, kp, attn_lse=lse)
+    torch.cuda.synchronize()
+    parity.check_select(w, x, None, idx.cpu().numpy(), n_idx.cpu().numpy())
+
+
+def test_full_draft_decode_refresh_sampled():
+    """The S3R round at full size: dense verify of the 6 drafts of 64 sequences, then the
+    refreshed selection (sampled rows against the oracle)."""
+    w = FULL["bf16_draft_decode"]().scaled(select_mode=SELECT_ATTN)
+    xg = generate(w, device="cuda")
+    lse = _verify_lse(w, xg)
+    idx, n_idx = sa.select(parity.params_for(w), xg["q"], None, xg["k"], attn_lse=lse)
+    torch.cuda.synchronize()
+    x = {k: (t.cpu() if isinstance(t, torch.Tensor) else t) for k, t in xg.items()}
+    rng = np.random.default_rng(11)
+    rows = np.repeat(rng.choice(w.rows, size=12, replace=False), w.h_kv)
+    heads = np.tile(np.arange(w.h_kv), len(rows) // w.h_kv)
+    parity.check_select(w, x, None, idx.cpu().numpy(), n_idx.cpu().numpy(), rows=rows, heads=heads)

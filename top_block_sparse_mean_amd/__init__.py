@@ -25,12 +25,12 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
-                   SA_POOL_MEAN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaParams, SparseAttnError,
-                   check, lib)
+                   SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaParams,
+                   SparseAttnError, check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select", "fwd",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
-           "SA_SELECT_MAX", "LIB_PATH", "EXPORTS"]
+           "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
 
 _DT = {torch.float32: SA_DTYPE_F32, torch.bfloat16: SA_DTYPE_BF16}
 
@@ -160,15 +160,22 @@ def append_kv(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tens
 
 def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Optional[torch.Tensor],
            idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
-           ws: Optional[torch.Tensor] = None, stream=None):
+           ws: Optional[torch.Tensor] = None, stream=None, attn_lse: Optional[torch.Tensor] = None):
+    """Top-k selection.  With select_mode SA_SELECT_ATTN, q_sel are the verify queries and
+    ``attn_lse`` [h_q, total_q] the log-sum-exp their dense attention pass returned."""
     dev = q_sel.device
     if idx is None:
         idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
     if n_idx is None:
         n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
     ws, nbytes = _ws(workspace_size(p)[0], dev, ws)
-    check("sparse_attn_select", lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx),
-                                                         _ptr(n_idx), _ptr(ws), nbytes, _stream(stream)))
+    p.s.attn_lse = None if attn_lse is None else attn_lse.data_ptr()
+    try:
+        st = lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx), _ptr(n_idx), _ptr(ws),
+                                      nbytes, _stream(stream))
+    finally:
+        p.s.attn_lse = None
+    check("sparse_attn_select", st)
     return idx, n_idx
 
 

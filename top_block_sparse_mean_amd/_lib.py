@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "libsparse_attn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(5)
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_POOL_MEAN, SA_POOL_L2SUM = 0, 1
-SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX = 0, 1, 2
+SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX, SA_SELECT_ATTN = 0, 1, 2, 3
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
@@ -50,6 +50,7 @@ class SaParams(ctypes.Structure):
         ("pool_overlap", ctypes.c_int32),
         ("select_mode", ctypes.c_int32),
         ("select_temperature", ctypes.c_float),
+        ("attn_lse", ctypes.c_void_p),
     ]
 
 

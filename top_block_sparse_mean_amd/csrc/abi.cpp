@@ -80,8 +80,11 @@ sa_status check_params(const sa_params *p)
         return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     if (p->pool_overlap < 0 || p->pool_overlap > (1 << 20))
         return fail(SA_ERR_INVALID_ARG, "pool_overlap must be in [0, 2^20] (got %d)", p->pool_overlap);
-    if (p->select_mode != SA_SELECT_SUM && p->select_mode != SA_SELECT_SOFTMAX && p->select_mode != SA_SELECT_MAX)
+    if (p->select_mode != SA_SELECT_SUM && p->select_mode != SA_SELECT_SOFTMAX && p->select_mode != SA_SELECT_MAX &&
+        p->select_mode != SA_SELECT_ATTN)
         return fail(SA_ERR_INVALID_ARG, "unknown select_mode %d", p->select_mode);
+    if (p->select_mode == SA_SELECT_ATTN && (long long)(p->shared_selection ? p->max_q : 1) * (p->h_q / p->h_kv) > 64)
+        return fail(SA_ERR_UNSUPPORTED, "SA_SELECT_ATTN: a row's queries times the group size must be <= 64");
     if (!(p->select_temperature >= 0.f) || std::isinf(p->select_temperature))
         return fail(SA_ERR_INVALID_ARG, "select_temperature must be finite and >= 0");
     if (p->block_table) {
@@ -129,6 +132,7 @@ sa::KP make_kp(const sa_params *p)
     k.head_score_scale = p->select_mode == SA_SELECT_SOFTMAX && p->select_temperature > 0.f
                              ? 1.0f / p->select_temperature
                              : 1.0f / std::sqrt((float)p->head_dim);
+    k.attn_lse = p->attn_lse;
     k.block_table = p->block_table;
     k.max_pages = p->block_table ? p->max_pages : 0;
     k.page_shift = 0;
@@ -234,10 +238,13 @@ sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float 
         return s;
     if (!q_sel || !n_idx || (!idx && p->topk > 0))
         return fail(SA_ERR_INVALID_ARG, "q_sel, idx and n_idx are required");
-    if (p->block == 1 && !k)
-        return fail(SA_ERR_INVALID_ARG, "block == 1 scores the raw keys: k is required");
-    if (p->block > 1 && !k_cmp)
+    const bool attn = p->select_mode == SA_SELECT_ATTN;
+    if ((p->block == 1 || attn) && !k)
+        return fail(SA_ERR_INVALID_ARG, "block == 1 or SA_SELECT_ATTN scores the raw keys: k is required");
+    if (p->block > 1 && !attn && !k_cmp)
         return fail(SA_ERR_INVALID_ARG, "block > 1 scores pooled keys: k_cmp is required");
+    if (attn && !p->attn_lse)
+        return fail(SA_ERR_INVALID_ARG, "SA_SELECT_ATTN needs attn_lse");
     if (!aligned16(q_sel) || (k && !aligned16(k)) || (k_cmp && !aligned16(k_cmp)))
         return fail(SA_ERR_INVALID_ARG, "q_sel, k and k_cmp must be 16-byte aligned");
     sa::KP kp = make_kp(p);

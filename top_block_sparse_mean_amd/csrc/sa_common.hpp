@@ -29,6 +29,7 @@ struct KP {
     int pool_overlap;             // pooling window of block j starts at max(0, j*g - pool_overlap)
     int select_mode;              // 0 sum of heads, 1 sum of per-head softmaxes, 2 max over heads
     float head_score_scale;       // per-head score scale (1/tau or 1/sqrt(d))
+    const float *attn_lse;        // select mode 3: [h_q, total_q] log-sum-exp of a dense verify pass
 };
 
 struct Seq {

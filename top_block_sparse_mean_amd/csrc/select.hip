@@ -574,6 +574,93 @@ __global__ __launch_bounds__(256) void score_heads_kernel(KP P, const T *__restr
     }
 }
 
+// SA_SELECT_ATTN: grid (rows * n_chunk, h_kv).  The row's (query, head) pairs
+// (R = its queries x G <= 64) sit in LDS with their log-sum-exps from the verify
+// pass; every token of a candidate block is dotted with every pair and
+// exp(scale dot - lse) is summed, in a fixed order (the block's tokens, then the
+// pairs), into the block's score: the attention mass the verify pass put on it.
+template <typename T, int D, int CH>
+__global__ __launch_bounds__(256) void score_attn_kernel(KP P, const T *__restrict__ q, const T *__restrict__ k,
+                                                         uint32_t *__restrict__ ws, long long stride, int n_chunk)
+{
+    using RD = RowDot<T, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L, NG = 4 * GPW;
+    constexpr int U = 64 / NG < 1 ? 1 : 64 / NG;          // 64 candidates per round
+    constexpr int RW = U * NG;
+    __shared__ __attribute__((aligned(16))) float sh_q[kMaxG * D];
+    __shared__ float sh_lse[kMaxG];
+    const long long row = blockIdx.x / n_chunk;
+    const int chunk = (int)(blockIdx.x % n_chunk);
+    const int c = blockIdx.y;
+    const RowGeo r = row_geo(P, row);
+    if (r.need == r.n_cand)
+        return;
+    const int j0 = r.j_lo + chunk * CH;
+    const int j1 = min(j0 + CH, r.j_hi);
+    if (j0 >= j1)
+        return;
+    const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    const int R = (int)(r.q_last - r.q_first) * P.G;
+    for (int x = tid; x < R * D; x += 256) {
+        const int pr = x / D;
+        const long long i = r.q_first + pr / P.G;
+        const long long h = (long long)c * P.G + pr % P.G;
+        if constexpr (sizeof(T) == 2)
+            sh_q[x] = bf16_to_f32(q[(i * P.h_q + h) * D + x % D]);
+        else
+            sh_q[x] = q[(i * P.h_q + h) * D + x % D];
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int x = tid; x < R; x += 256) {
+        const long long i = r.q_first + x / P.G;
+        const long long h = (long long)c * P.G + x % P.G;
+        sh_lse[x] = P.attn_lse[h * P.total_q + i] * kLog2e;
+    }
+    __syncthreads();
+    const KvMap kmap = kv_map(P, r.b);
+    const T *kb = k + (P.block_table ? 0 : r.k_off * P.h_kv) * D + (long long)c * D;
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    const int rounds = (j1 - j0 + RW - 1) / RW;
+    for (int rd = 0; rd < rounds; rd++) {
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            acc[u] = 0.f;
+        for (int s = 0; s < P.g; s++) {
+            uint4 raw[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int jr = j0 + rd * RW + u * NG + grp;
+                const int j = min(jr, j1 - 1);
+                const int t = j * P.g + s;
+                ok[u] = jr < j1 && t < r.n_k;
+                const long long tr = kmap.row(min(t, r.n_k - 1));
+                raw[u] = reinterpret_cast<const uint4 *>(kb + tr * P.h_kv * D)[sub];
+            }
+            for (int pr = 0; pr < R; pr++) {
+                float qv[VPL];
+#pragma unroll
+                for (int e = 0; e < VPL; e++)
+                    qv[e] = sh_q[pr * D + sub * VPL + e];
+                const float lb = sh_lse[pr];
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const float dot = group_sum<L>(slice_dot<VPL>(raw[u], qv));
+                    acc[u] += ok[u] ? exp2f(dot * (P.scale * kLog2e) - lb) : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int j = j0 + rd * RW + u * NG + grp;
+            if (sub == 0 && j < j1)
+                keys[j] = order_key(acc[u]);
+        }
+    }
+}
+
 // Sum over a 256-thread workgroup (or max), in a fixed order: the result does not
 // depend on timing.  Every thread gets the result.
 template <bool MAX>
@@ -1394,7 +1481,13 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         const int ch = small ? 128 : kSplitChunk;
         const int n_chunk = (int)((stride + ch - 1) / ch);
         dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
-        if (P.g == 1) {
+        if (P.select_mode == 3) {
+            if (small)
+                score_attn_kernel<T, D, 128><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, n_chunk);
+            else
+                score_attn_kernel<T, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,
+                                                                               n_chunk);
+        } else if (P.g == 1) {
             if (small)
                 score_heads_kernel<T, T, D, 128><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, ws_l, stride,
                                                                            n_chunk);

@@ -361,6 +361,53 @@ def record_counters(workload, fetch_dir, write_dir, commands):
     print(path)
 
 
+def s3r_refresh(w, step, steps, device):
+    """The rest of an S3R round after the drafts (S3R review): the dense verify pass over
+    the history and the drafts (a table keeping every candidate; attention with lse),
+    then the next round's selection by the attention mass that pass put on each history
+    token (select_mode SA_SELECT_ATTN).  Each leg is timed with events over `steps`
+    repetitions; bytes are the keys and values read once per (sequence, KV head)."""
+    from workloads import SELECT_ATTN
+    x = step.x
+    wd = w.scaled(topk=max(w.seqlens_k), topk_per_seq=None)
+    pd = make_params(wd, device, step.layout)
+    pa = make_params(w.scaled(select_mode=SELECT_ATTN), device, step.layout)
+    sel_b, fwd_b = sa.workspace_size(pd)
+    ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
+    ws_fwd = torch.empty(max(fwd_b, 16), dtype=torch.uint8, device=device)
+    idx_d, n_d = sa.select(pd, x["q"], None, x["k"], ws=ws_sel)          # every candidate: dense
+    ws_a = torch.empty(max(sa.workspace_size(pa)[0], 16), dtype=torch.uint8, device=device)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((w.h_q, w.total_q), dtype=torch.float32, device=device)
+    idx = torch.empty((w.h_kv, pa.rows, max(w.topk, 1)), dtype=torch.int32, device=device)
+    n_idx = torch.empty((w.h_kv, pa.rows), dtype=torch.int32, device=device)
+    ev = TimingEvents(steps, width=3)
+
+    def leg(evs=None):
+        if evs:
+            ev.record(evs[0])
+        sa.fwd(pd, x["q"], x["k"], x["v"], idx_d, n_d, out=out, lse=lse, want_lse=True, ws=ws_fwd)
+        if evs:
+            ev.record(evs[1])
+        sa.select(pa, x["q"], None, x["k"], idx, n_idx, ws=ws_a, attn_lse=lse)
+        if evs:
+            ev.record(evs[2])
+    for _ in range(3):
+        leg()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        leg(ev.pairs[i])
+    torch.cuda.synchronize()
+    v_ms, r_ms = ev.mean_ms(0, 1), ev.mean_ms(1, 2)
+    ev.close()
+    elt = 2 if w.dtype == DTYPE_BF16 else 4
+    kv_bytes = w.total_k * w.h_kv * w.head_dim * elt
+    return {"verify_ms": round(v_ms, 5), "refresh_ms": round(r_ms, 5),
+            "verify_gbs": round(2 * kv_bytes / (v_ms * 1e-3) / 1e9, 1),
+            "refresh_gbs": round(kv_bytes / (r_ms * 1e-3) / 1e9, 1),
+            "round_us": None}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -458,6 +505,8 @@ def main():
                          "max over heads")
     ap.add_argument("--pool-overlap", type=int, default=0,
                     help="pooling windows reach this many tokens before their block (0: disjoint)")
+    ap.add_argument("--s3r-refresh", action="store_true",
+                    help="draft workload: also time the dense verify pass and the refreshed selection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -569,6 +618,10 @@ def main():
     if w.name == "bf16_draft_decode":
         extra["us_per_draft_token"] = round(ms_step * 1e3 / w.seqlens_q[0], 3)
     extra["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks)
+    if args.s3r_refresh and w.shared_selection:
+        r = s3r_refresh(w, step, min(args.steps, 20), device)
+        r["round_us"] = round(ms_step * 1e3 + (r["verify_ms"] + r["refresh_ms"]) * 1e3, 2)
+        extra["s3r"] = r
     extra["measured_peaks"] = peaks
 
     res = {

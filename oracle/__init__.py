@@ -50,6 +50,8 @@ def lib():
         L.or_select.restype = ctypes.c_int
         L.or_attend.restype = ctypes.c_int
         L.or_num_threads.restype = ctypes.c_int
+        L.or_bucket_build.restype = ctypes.c_int
+        L.or_bucket_select.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -202,3 +204,50 @@ def run(w, x, rows=None, reqs=None, heads=None):
     idx, n = table(w, sel)
     att = attend(w, x["q"], x["k"], x["v"], idx, n, reqs=reqs, heads=heads)
     return dict(k_cmp=kc, sel=sel, idx=idx, n_idx=n, **att)
+
+
+def bucket_build(w, k_cmp, cu_k=None) -> dict:
+    """The LSA flat bucket index of every complete cluster block, from pooled keys
+    ``k_cmp`` [Hkv, batch, nb_max, d] (fp64, from ``compress``): members [Hkv, batch,
+    n_cb, C/g] grouped by bucket, offsets [.., NB + 1], centroids [.., NB, d] and the
+    smallest relative decision margin of each block (inf when no decision was close)."""
+    _, cu_k, _ = _geom(w, None, cu_k, None)
+    g, C, NB = w.block, w.bucket_block, w.bucket_count
+    M = C // g
+    ncb = max(w.seqlens_k) // C
+    nb_max = -(-max(w.seqlens_k) // g)
+    k_cmp = np.ascontiguousarray(k_cmp, dtype=np.float64)
+    member = np.empty((w.h_kv, w.batch, ncb, M), dtype=np.int32)
+    offset = np.empty((w.h_kv, w.batch, ncb, NB + 1), dtype=np.int32)
+    cent = np.empty((w.h_kv, w.batch, ncb, NB, w.head_dim), dtype=np.float64)
+    margin = np.empty((w.h_kv, w.batch, ncb), dtype=np.float64)
+    rc = lib().or_bucket_build(w.batch, w.h_kv, w.head_dim, _ptr(cu_k, _i32p), g, C, NB, w.bucket_cap,
+                               _ptr(k_cmp, _f64p), ctypes.c_int64(nb_max), ctypes.c_int64(ncb),
+                               _ptr(member, _i32p), _ptr(offset, _i32p), _ptr(cent, _f64p), _ptr(margin, _f64p))
+    assert rc == 0
+    return dict(member=member, offset=offset, centroid=cent, margin=margin)
+
+
+def bucket_select(w, q_sel, index, rows=None, heads=None, q_pos0=None, cu_q=None, cu_k=None) -> dict:
+    """Flat bucket retrieval for (row, KV head) requests: the w.bucket_topk best buckets
+    expanded to their member groups (ascending, -1 padded to kb * cap / g).  Returns
+    dict(idx, n, nbk (buckets taken), sk / sk1 / floor (bucket-score near-tie data))."""
+    cu_q, cu_k, qp = _geom(w, cu_q, cu_k, q_pos0)
+    if rows is None:
+        rr, hh = np.meshgrid(np.arange(w.rows), np.arange(w.h_kv), indexing="xy")
+        heads, rows = hh.reshape(-1), rr.reshape(-1)
+    rows, heads = _i64(rows), _i32(heads)
+    n = len(rows)
+    kcap = max(w.bucket_topk * (w.bucket_cap // w.block), 1)
+    idx = np.empty((n, kcap), dtype=np.int32)
+    nn, nbk = np.empty(n, dtype=np.int32), np.empty(n, dtype=np.int32)
+    sk, sk1, fl = (np.empty(n, dtype=np.float64) for _ in range(3))
+    ncb = index["member"].shape[2]
+    rc = lib().or_bucket_select(
+        w.batch, w.h_q, w.h_kv, w.head_dim, _ptr(cu_q, _i32p), _ptr(cu_k, _i32p), _ptr(qp, _i32p), w.block,
+        w.bucket_block, w.bucket_count, w.bucket_topk, int(w.shared_selection), w.dtype, _ptr(q_sel),
+        _ptr(index["member"], _i32p), _ptr(index["offset"], _i32p), _ptr(index["centroid"], _f64p),
+        ctypes.c_int64(ncb), ctypes.c_int64(n), _ptr(rows, _i64p), _ptr(heads, _i32p), kcap, _ptr(idx, _i32p),
+        _ptr(nn, _i32p), _ptr(sk, _f64p), _ptr(sk1, _f64p), _ptr(fl, _f64p), _ptr(nbk, _i32p))
+    assert rc == 0, "expansion exceeded the table width"
+    return dict(idx=idx, n=nn, nbk=nbk, sk=sk, sk1=sk1, floor=fl, rows=rows, heads=heads)

@@ -473,3 +473,266 @@ int or_attend(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
     }
     return 0;
 }
+
+/* ------------------------------------------------------------- LSA buckets */
+
+/*
+ * bucket_build: the LSA flat index (LSA deep-read, §2.2).  The pooled keys of every
+ * complete cluster block (C consecutive tokens = C/g pooled groups of one sequence
+ * and KV head) start as one bucket each; every round, each bucket finds its
+ * cheapest partner under Ward's criterion among the buckets it may join (merged
+ * size <= cap groups), and the pairs that are each other's cheapest merge together
+ * (if that would leave fewer than NB buckets, only the cheapest pairs do, enough to
+ * reach NB); rounds repeat until NB buckets remain or no pair may merge.  Ward's
+ * criterion for buckets A, B with member sums S and sizes n is
+ * n_A n_B / (n_A + n_B) |S_A/n_A - S_B/n_B|^2, evaluated here as
+ * |n_B S_A - n_A S_B|^2 / (n_A n_B (n_A + n_B)) in fp32 with fused multiply-adds
+ * over the head dimension in order (the precision the kernel decides in).  Ties:
+ * the lower bucket (a bucket is named by its smallest member).  A bucket's centroid
+ * is the normalised sum of its members.  Output per block: members grouped by
+ * bucket (buckets in name order, members ascending), NB + 1 offsets, NB centroids
+ * (fp64), and the smallest relative margin of any decision taken (second best vs
+ * best partner; first excluded vs last merged pair), so tests can tell a
+ * near-tied block from a wrong one.
+ */
+static float ward_cost(const float *sa, int na, const float *sb, int nb, int d)
+{
+    float acc = 0.0f;
+    const float fa = (float)na, fb = (float)nb;
+    for (int e = 0; e < d; e++) {
+        const float t = fa * sb[e];
+        const float diff = fmaf(fb, sa[e], -t);
+        acc = fmaf(diff, diff, acc);
+    }
+    return acc * (1.0f / (float)(na * nb * (na + nb)));
+}
+
+int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int C, int NB, int cap_tok,
+                    const double *k_cmp, int64_t nb_max, int64_t ncb_max, int32_t *member, int32_t *offset,
+                    double *centroid, double *margin)
+{
+    const int M = C / g, capg = cap_tok / g;
+    if (C % g || cap_tok % g || NB < 1 || NB > M || capg < 1)
+        return 1;
+    int64_t n_items = (int64_t)h_kv * batch * ncb_max;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t it = 0; it < n_items; it++) {
+        int64_t cb = it % ncb_max;
+        int b = (int)((it / ncb_max) % batch);
+        int c = (int)(it / (ncb_max * batch));
+        int64_t n_b = cu_k[b + 1] - cu_k[b];
+        int32_t *mem = member + it * M;
+        int32_t *off = offset + it * (NB + 1);
+        double *cen = centroid + it * (int64_t)NB * d;
+        margin[it] = INFINITY;
+        if ((cb + 1) * C > n_b) {                      /* incomplete: no buckets */
+            for (int x = 0; x < M; x++)
+                mem[x] = -1;
+            for (int x = 0; x <= NB; x++)
+                off[x] = 0;
+            continue;
+        }
+        float *S = (float *)malloc(sizeof(float) * (size_t)M * d);
+        int *size = (int *)malloc(sizeof(int) * M), *alive = (int *)malloc(sizeof(int) * M);
+        int *root = (int *)malloc(sizeof(int) * M), *nn = (int *)malloc(sizeof(int) * M);
+        float *nnc = (float *)malloc(sizeof(float) * M);
+        for (int x = 0; x < M; x++) {
+            const double *src = k_cmp + (((int64_t)c * batch + b) * nb_max + cb * M + x) * d;
+            for (int e = 0; e < d; e++)
+                S[x * d + e] = (float)src[e];
+            size[x] = 1;
+            alive[x] = 1;
+            root[x] = x;
+        }
+        int count = M;
+        double mg = INFINITY;
+        while (count > NB) {
+            int any = 0;
+            for (int a = 0; a < M; a++) {
+                nn[a] = -1;
+                if (!alive[a])
+                    continue;
+                float best = INFINITY, second = INFINITY;
+                for (int o = 0; o < M; o++) {
+                    if (o == a || !alive[o] || size[a] + size[o] > capg)
+                        continue;
+                    const int lo = a < o ? a : o, hi = a < o ? o : a;      /* symmetric: lower name first */
+                    float w = ward_cost(S + lo * d, size[lo], S + hi * d, size[hi], d);
+                    if (w < best) {
+                        second = best;
+                        best = w;
+                        nn[a] = o;
+                    } else if (w < second) {
+                        second = w;
+                    }
+                }
+                nnc[a] = best;
+                if (nn[a] >= 0) {
+                    any = 1;
+                    if (second < INFINITY) {
+                        double r = best > 0.0f ? ((double)second - best) / best : (second > 0.0f ? INFINITY : 0.0);
+                        if (r < mg)
+                            mg = r;
+                    }
+                }
+            }
+            if (!any)
+                break;
+            /* mutual pairs (a < o), cheapest first, ties by a */
+            int np = 0;
+            int *pa = (int *)malloc(sizeof(int) * M);
+            for (int a = 0; a < M; a++)
+                if (alive[a] && nn[a] > a && nn[nn[a]] == a)
+                    pa[np++] = a;
+            for (int x = 1; x < np; x++)               /* insertion sort by (cost, a) */
+                for (int y = x; y > 0 && (nnc[pa[y]] < nnc[pa[y - 1]] ||
+                                          (nnc[pa[y]] == nnc[pa[y - 1]] && pa[y] < pa[y - 1])); y--) {
+                    int t = pa[y];
+                    pa[y] = pa[y - 1];
+                    pa[y - 1] = t;
+                }
+            int take = np < count - NB ? np : count - NB;
+            if (take < np && take > 0) {
+                float lo = nnc[pa[take - 1]], hi = nnc[pa[take]];
+                double r = lo > 0.0f ? ((double)hi - lo) / lo : (hi > 0.0f ? INFINITY : 0.0);
+                if (r < mg)
+                    mg = r;
+            }
+            for (int x = 0; x < take; x++) {
+                int a = pa[x], o = nn[a];
+                for (int e = 0; e < d; e++)
+                    S[a * d + e] += S[o * d + e];
+                size[a] += size[o];
+                alive[o] = 0;
+                for (int y = 0; y < M; y++)
+                    if (root[y] == o)
+                        root[y] = a;
+                count--;
+            }
+            free(pa);
+            if (take == 0)
+                break;
+        }
+        /* buckets in name order (a bucket is named by its smallest member = its root) */
+        int nbk = 0, pos = 0;
+        for (int a = 0; a < M && nbk < NB; a++) {
+            if (!alive[a])
+                continue;
+            off[nbk] = pos;
+            double nrm = 0.0;
+            for (int e = 0; e < d; e++)
+                nrm += (double)S[a * d + e] * S[a * d + e];
+            nrm = sqrt(nrm);
+            for (int e = 0; e < d; e++)
+                cen[(int64_t)nbk * d + e] = nrm > 0.0 ? S[a * d + e] / nrm : 0.0;
+            for (int y = 0; y < M; y++)
+                if (root[y] == a)
+                    mem[pos++] = y;
+            nbk++;
+        }
+        for (; nbk <= NB; nbk++)
+            off[nbk] = pos;
+        margin[it] = mg;
+        free(S);
+        free(size);
+        free(alive);
+        free(root);
+        free(nn);
+        free(nnc);
+    }
+    return 0;
+}
+
+/*
+ * bucket_select: flat retrieval (LSA deep-read, §2.3).  The row's selector query
+ * (the group's heads summed, over the row's queries) scores every bucket of the
+ * complete cluster blocks that end at or before p_sel, s = qs . centroid / sqrt(d);
+ * the kb best (score descending, bucket index ascending) are expanded to all their
+ * member groups, written in ascending group order (width kcap, -1 padded).  The
+ * near-tie data (sk, sk1, floor) refer to the bucket scores.
+ */
+int or_bucket_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
+                     const int32_t *q_pos0, int g, int C, int NB, int kb, int shared, int dtype, const void *q_sel,
+                     const int32_t *member, const int32_t *offset, const double *centroid, int64_t ncb_max,
+                     int64_t n_req, const int64_t *req_row, const int32_t *req_kvh, int kcap, int32_t *out_idx,
+                     int32_t *out_n, double *out_sk, double *out_sk1, double *out_floor, int32_t *out_nbk)
+{
+    const int G = h_q / h_kv, M = C / g;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_req; r++) {
+        int64_t row = req_row[r];
+        int c = req_kvh[r];
+        int b;
+        int64_t qa, qb, p_sel;
+        if (shared) {
+            b = (int)row;
+            qa = cu_q[b];
+            qb = cu_q[b + 1];
+            p_sel = first_query_pos(b, cu_q, cu_k, q_pos0);
+            p_sel -= 1;                                /* the boundary before the row's queries */
+        } else {
+            b = seq_of_query(row, batch, cu_q);
+            qa = row;
+            qb = row + 1;
+            p_sel = first_query_pos(b, cu_q, cu_k, q_pos0) + (row - cu_q[b]);
+        }
+        int64_t n_b = cu_k[b + 1] - cu_k[b];
+        int64_t ncb = (p_sel + 1) / C;                 /* complete blocks wholly at or before p_sel */
+        if (ncb > n_b / C)
+            ncb = n_b / C;
+        if (ncb > ncb_max)
+            ncb = ncb_max;
+        double *qs = (double *)calloc((size_t)d, sizeof(double));
+        for (int64_t i = qa; i < qb; i++)
+            for (int h = c * G; h < (c + 1) * G; h++)
+                for (int e = 0; e < d; e++)
+                    qs[e] += elem(q_sel, dtype, (i * h_q + h) * (int64_t)d + e);
+        double qnorm = 0.0;
+        for (int e = 0; e < d; e++)
+            qnorm += qs[e] * qs[e];
+        qnorm = sqrt(qnorm);
+        int64_t nc = ncb * NB;
+        cand *cs = (cand *)malloc(sizeof(cand) * (size_t)(nc > 0 ? nc : 1));
+        for (int64_t j = 0; j < nc; j++) {
+            const double *cv = centroid + ((((int64_t)c * batch + b) * ncb_max + j / NB) * NB + j % NB) * d;
+            double dot = 0.0;
+            for (int e = 0; e < d; e++)
+                dot += qs[e] * cv[e];
+            cs[j].s = dot / sqrt((double)d);
+            cs[j].j = (int32_t)j;
+        }
+        qsort(cs, (size_t)nc, sizeof(cand), cand_order);
+        int64_t ns = kb < nc ? kb : nc;
+        int32_t *dst = out_idx + r * (int64_t)kcap;
+        int64_t n_out = 0;
+        for (int64_t s = 0; s < ns; s++) {
+            int64_t j = cs[s].j, blk = j / NB, lb = j % NB;
+            const int64_t base = (((int64_t)c * batch + b) * ncb_max + blk);
+            const int32_t *mem = member + base * M;
+            const int32_t *off = offset + base * (NB + 1);
+            for (int x = off[lb]; x < off[lb + 1]; x++) {
+                if (n_out >= kcap) {
+                    bad |= 1;
+                    break;
+                }
+                dst[n_out++] = (int32_t)(blk * M + mem[x]);
+            }
+        }
+        qsort(dst, (size_t)n_out, sizeof(int32_t), int_order);
+        for (int64_t s = n_out; s < kcap; s++)
+            dst[s] = -1;
+        out_n[r] = (int32_t)n_out;
+        if (out_nbk)
+            out_nbk[r] = (int32_t)ns;
+        if (out_sk)
+            out_sk[r] = ns >= 1 ? cs[ns - 1].s : NAN;
+        if (out_sk1)
+            out_sk1[r] = nc > ns ? cs[ns].s : NAN;
+        if (out_floor)
+            out_floor[r] = 1e-6 * qnorm / sqrt((double)d);     /* centroids have unit norm */
+        free(cs);
+        free(qs);
+    }
+    return bad;
+}

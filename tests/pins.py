@@ -318,6 +318,103 @@ def pin_select_attn_one_query_ranks_by_dot():
     np.testing.assert_array_equal(got["n"], ref["n"])
 
 
+def _bucket_index(points, C, NB, cap, g=1):
+    """Bucket index of one sequence, one KV head, from given pooled keys [n, d] (fp64)."""
+    pts = np.asarray(points, dtype=np.float64)
+    w = wl(h_q=1, h_kv=1, head_dim=pts.shape[1], seqlens_k=[pts.shape[0] * g], seqlens_q=[1], block=g,
+           bucket_block=C, bucket_count=NB, bucket_cap=cap)
+    return w, oracle.bucket_build(w, pts[None, None])
+
+
+def _buckets(ix, blk=0):
+    mem, off = ix["member"][0, 0, blk], ix["offset"][0, 0, blk]
+    return [sorted(mem[off[i]:off[i + 1]].tolist()) for i in range(len(off) - 1)]
+
+
+def pin_bucket_pairs_and_centroids():
+    """Four well separated pairs: each pair is each other's cheapest merge; centroids are
+    the normalised pair sums."""
+    pts = [(0, 5), (1, 5), (10, 0), (11, 0), (0, -10), (1, -10), (-20, 0), (-21, 0)]
+    w, ix = _bucket_index(pts, C=8, NB=4, cap=2)
+    assert _buckets(ix) == [[0, 1], [2, 3], [4, 5], [6, 7]]
+    for i, (a, b) in enumerate([(0, 1), (2, 3), (4, 5), (6, 7)]):
+        s = np.add(pts[a], pts[b]).astype(np.float64)
+        np.testing.assert_allclose(ix["centroid"][0, 0, 0, i], s / np.linalg.norm(s), rtol=1e-7)
+
+
+def pin_bucket_truncation_by_cost_then_name():
+    """Four mutual pairs but NB = 5 leaves room for three merges: the cheapest (Ward cost
+    0.125) and, of the three tied at 0.5, the two with the lower names."""
+    pts = [(0, 0), (1, 0), (20, 0), (20.5, 0), (40, 0), (41, 0), (60, 0), (61, 0)]
+    pts = [(x, 100.0) for x, _ in pts]
+    w, ix = _bucket_index(pts, C=8, NB=5, cap=4)
+    assert _buckets(ix) == [[0, 1], [2, 3], [4, 5], [6], [7]]
+    assert list(ix["offset"][0, 0, 0]) == [0, 2, 4, 6, 7, 8]
+
+
+def pin_bucket_ward_weighting():
+    """Point 2 at 0 is nearer to the centroid of the pair {0, 1} (at -2.8) than to point 3
+    (at 3), but Ward's cost n_A n_B / (n_A + n_B) d^2 is 5.23 against 4.5: it joins point 3."""
+    pts = [(-3.0, 1.0), (-2.6, 1.0), (0.0, 1.0), (3.0, 1.0)]
+    w, ix = _bucket_index(pts, C=4, NB=2, cap=3)             # {0, 1, 2} would fit
+    assert _buckets(ix) == [[0, 1], [2, 3]]
+
+
+def pin_bucket_invariants():
+    """Random keys: each complete cluster block is partitioned into exactly NB buckets of at
+    most cap/g groups, named and listed in order; centroids are normalised member sums;
+    the incomplete last block has no buckets."""
+    g, C, NB, cap = 4, 64, 8, 16
+    w = wl(dtype=DTYPE_BF16, h_q=4, h_kv=2, head_dim=16, seqlens_k=[3 * C + 37, 2 * C], seqlens_q=[1, 1],
+           block=g, pool=POOL_L2SUM, bucket_block=C, bucket_count=NB, bucket_cap=cap)
+    x = generate(w)
+    kc = oracle.compress(w, x["k"])
+    ix = oracle.bucket_build(w, kc)
+    M = C // g
+    for c in range(2):
+        for b, nk in enumerate(w.seqlens_k):
+            for blk in range(ix["member"].shape[2]):
+                mem, off = ix["member"][c, b, blk], ix["offset"][c, b, blk]
+                if (blk + 1) * C > nk:
+                    assert (mem == -1).all() and (off == 0).all()
+                    continue
+                assert sorted(mem.tolist()) == list(range(M))
+                sizes = np.diff(off)
+                assert len(sizes) == NB and (sizes >= 1).all() and (sizes <= cap // g).all()
+                names = [mem[off[i]] for i in range(NB)]
+                assert names == sorted(names)
+                for i in range(NB):
+                    grp = mem[off[i]:off[i + 1]]
+                    assert list(grp) == sorted(grp)
+                    ssum = kc[c, b, blk * M + grp].astype(np.float32).astype(np.float64).sum(0)
+                    np.testing.assert_allclose(ix["centroid"][c, b, blk, i], ssum / np.linalg.norm(ssum),
+                                               rtol=1e-5, atol=1e-6)
+
+
+def pin_bucket_select():
+    """kb >= every visible bucket selects every group of the complete cluster blocks that
+    end at or before p_sel; kb = 1 with the query along one centroid takes that bucket."""
+    g, C, NB, cap = 4, 64, 8, 16
+    w = wl(dtype=DTYPE_F32, h_q=2, h_kv=1, head_dim=16, seqlens_k=[5 * C + 10], seqlens_q=[40], block=g,
+           pool=POOL_L2SUM, bucket_block=C, bucket_count=NB, bucket_cap=cap, bucket_topk=1000)
+    x = generate(w)
+    ix = oracle.bucket_build(w, oracle.compress(w, x["k"]))
+    r = oracle.bucket_select(w, x["q"], ix)
+    for rr in range(w.rows):
+        p = w.seqlens_k[0] - w.seqlens_q[0] + rr
+        ncb = (p + 1) // C
+        assert r["idx"][rr, :r["n"][rr]].tolist() == list(range(ncb * C // g))
+    # one bucket: a query along the centroid of bucket 5 of block 2 (unit centroids: it wins)
+    w1 = w.scaled(bucket_topk=1, seqlens_q=[1], seqlens_k=[4 * C])
+    target = ix["centroid"][0, 0, 2, 5]
+    q = torch.zeros((1, 2, 16), dtype=torch.float32)
+    q[0, 0] = torch.from_numpy(target * 3.0).float()
+    r1 = oracle.bucket_select(w1, q, ix)
+    mem, off = ix["member"][0, 0, 2], ix["offset"][0, 0, 2]
+    want = sorted((2 * (C // g) + mem[off[5]:off[6]]).tolist())
+    assert r1["idx"][0, :r1["n"][0]].tolist() == want and r1["nbk"][0] == 1
+
+
 # ------------------------------------------------------------------ select
 
 def _planted_scores_case(rng, g, n, pool, n_init, window, topk, G=2, d=8, n_levels=4):

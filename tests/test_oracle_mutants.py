@@ -39,6 +39,15 @@ MUTANTS = {
                                "int64_t t0 = (int64_t)cs[x].j * g, t1 = t0;"),
     "attn_last_query_only": ("for (int64_t i = qa; i < qb; i++) {\n                int64_t p_i",
                              "for (int64_t i = qb - 1; i < qb; i++) {\n                int64_t p_i"),
+    "ward_unweighted": ("return acc * (1.0f / (float)(na * nb * (na + nb)));",
+                        "return acc * (1.0f / (float)(na * na * nb * nb));"),
+    "ward_not_mutual": ("if (alive[a] && nn[a] > a && nn[nn[a]] == a)", "if (alive[a] && nn[a] > a)"),
+    "ward_truncate_dearest": ("(nnc[pa[y]] < nnc[pa[y - 1]] ||", "(nnc[pa[y]] > nnc[pa[y - 1]] ||"),
+    "ward_ignore_cap": ("if (o == a || !alive[o] || size[a] + size[o] > capg)", "if (o == a || !alive[o])"),
+    "centroid_unnormalised": ("cen[(int64_t)nbk * d + e] = nrm > 0.0 ? S[a * d + e] / nrm : 0.0;",
+                              "cen[(int64_t)nbk * d + e] = S[a * d + e];"),
+    "bucket_blocks_off_by_one": ("int64_t ncb = (p_sel + 1) / C;", "int64_t ncb = (p_sel + 1 + C - 1) / C;"),
+    "expand_drops_member": ("for (int x = off[lb]; x < off[lb + 1]; x++) {", "for (int x = off[lb]; x < off[lb + 1] - 1; x++) {"),
     "softmax_one_head": ("for (int hh = 0; hh < G; hh++) {\n                double m = -INFINITY, z = 0.0;",
                          "for (int hh = 0; hh < 1; hh++) {\n                double m = -INFINITY, z = 0.0;"),
     "ties_to_higher": ("return (x->j > y->j) - (x->j < y->j);", "return (x->j < y->j) - (x->j > y->j);"),

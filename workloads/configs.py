@@ -55,6 +55,12 @@ class Workload:
     pool_overlap: int = 0      # o: each block's pooling window reaches o tokens back (kernel g + o, stride g)
     select_mode: int = SELECT_SUM
     select_tau: float = 0.0    # softmax temperature of SELECT_SOFTMAX; 0 = sqrt(d)
+    # LSA flat bucket index: cluster blocks of bucket_block tokens, bucket_count buckets each,
+    # at most bucket_cap tokens per bucket; retrieval takes the bucket_topk best buckets
+    bucket_block: int = 512
+    bucket_count: int = 64
+    bucket_cap: int = 16
+    bucket_topk: int = 256
     structure: str = "iid"     # iid | hot_blocks | lowrank | needles
     seed: int = 0
     # structure knobs

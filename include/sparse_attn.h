@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 4
+#define SPARSE_ATTN_ABI_VERSION 5
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -133,6 +133,27 @@ typedef struct sa_params {
                                   the row's queries times G must be <= 64                          */
 } sa_params;
 
+/* The LSA flat bucket index (LSA deep-read, §2.2-§2.3): every complete cluster block
+ * of block_tokens consecutive tokens (block_tokens / block pooled groups of one
+ * sequence and KV head) is clustered bottom-up by Ward's criterion into `count`
+ * buckets of at most cap_tokens tokens; a bucket's centroid is the normalised sum of
+ * its members' pooled keys.  The arrays are owned by the caller. */
+typedef struct sa_bucket_index {
+    int32_t block_tokens;      /* C: a multiple of block, with C / block <= 128              */
+    int32_t count;             /* NB buckets per cluster block, 1 <= NB <= C / block          */
+    int32_t cap_tokens;        /* a multiple of block; (cap_tokens / block) * NB >= 2 C / block
+                                  (merging never stalls above NB buckets)                     */
+    int32_t blocks_max;        /* cluster blocks per (sequence, KV head) in the arrays,
+                                  >= max_k / C (only complete blocks hold buckets)            */
+    float *centroid;           /* device [h_kv, batch, blocks_max, NB, d] fp32                */
+    int32_t *member;           /* device [h_kv, batch, blocks_max, C / block]: each block's
+                                  group indices, grouped by bucket (buckets ordered by their
+                                  smallest member), ascending within a bucket; -1 for a block
+                                  that is not complete                                         */
+    int32_t *offset;           /* device [h_kv, batch, blocks_max, NB + 1]: bucket i holds
+                                  member[offset[i] .. offset[i+1])                             */
+} sa_bucket_index;
+
 /* SPARSE_ATTN_ABI_VERSION of the built library. */
 int sparse_attn_abi_version(void);
 
@@ -206,6 +227,34 @@ sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const voi
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp,
                              const void *k, int32_t *idx, int32_t *n_idx, void *ws,
                              size_t ws_bytes, void *stream);
+
+/* Build the bucket index from pooled keys (LSA deep-read, §2.2: streaming Ward
+ * clustering into buckets, centroids = normalised member sums).  Every round, each
+ * bucket finds its cheapest partner by Ward's criterion among the buckets it may join
+ * (merged size within cap); pairs that are each other's cheapest merge -- the cheapest
+ * pairs (by cost, then the lower bucket) when all would leave fewer than NB buckets --
+ * until NB buckets remain.  Costs are fp32: |n_B S_A - n_A S_B|^2 / (n_A n_B (n_A + n_B))
+ * with S the member sums and n the sizes, accumulated with fused multiply-adds over the
+ * head dimension in order.  Blocks that are not complete are marked (member -1).
+ *   k_cmp  pooled keys [h_kv, batch, nbmax, d] from sparse_attn_compress */
+sa_status sparse_attn_bucket_build(const sa_params *p, const float *k_cmp, const sa_bucket_index *bx, void *stream);
+
+/* Bytes of workspace sparse_attn_bucket_select needs for n_buckets per row. */
+sa_status sparse_attn_bucket_workspace_size(const sa_params *p, const sa_bucket_index *bx, int32_t n_buckets,
+                                            size_t *bytes);
+
+/* Flat bucket retrieval (LSA deep-read, §2.3): the row's selector query (the group's
+ * heads summed, as in sparse_attn_select) scores the centroids of the complete
+ * cluster blocks that end at or before the row's selection position, the n_buckets
+ * best (ties to the lower bucket) are taken and expanded to all their member groups.
+ *   idx    [h_kv, rows, topk] out: the groups, ascending, -1 padded; topk (the table
+ *          width, which sparse_attn_fwd reads too) must be >= n_buckets * cap_tokens /
+ *          block and <= 4096
+ *   n_idx  [h_kv, rows] out: the number of groups
+ *   n_buckets in [1, 1024]; ws of sparse_attn_bucket_workspace_size bytes. */
+sa_status sparse_attn_bucket_select(const sa_params *p, const void *q_sel, const sa_bucket_index *bx,
+                                    int32_t n_buckets, int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes,
+                                    void *stream);
 
 /* Sparse attention over A(p) for every query and query head (PulseCol, §3.1
  * Eq. (2); S3R review, sparse drafting formula).

@@ -230,7 +230,8 @@ def bucket_build(w, k_cmp, cu_k=None) -> dict:
 
 def bucket_select(w, q_sel, index, rows=None, heads=None, q_pos0=None, cu_q=None, cu_k=None) -> dict:
     """Flat bucket retrieval for (row, KV head) requests: the w.bucket_topk best buckets
-    expanded to their member groups (ascending, -1 padded to kb * cap / g).  Returns
+    expanded to their member groups outside the sink and window (ascending, -1 padded
+    to kb * cap / g).  Returns
     dict(idx, n, nbk (buckets taken), sk / sk1 / floor (bucket-score near-tie data))."""
     cu_q, cu_k, qp = _geom(w, cu_q, cu_k, q_pos0)
     if rows is None:
@@ -245,7 +246,7 @@ def bucket_select(w, q_sel, index, rows=None, heads=None, q_pos0=None, cu_q=None
     ncb = index["member"].shape[2]
     rc = lib().or_bucket_select(
         w.batch, w.h_q, w.h_kv, w.head_dim, _ptr(cu_q, _i32p), _ptr(cu_k, _i32p), _ptr(qp, _i32p), w.block,
-        w.bucket_block, w.bucket_count, w.bucket_topk, int(w.shared_selection), w.dtype, _ptr(q_sel),
+        w.n_init, w.window, w.bucket_block, w.bucket_count, w.bucket_topk, int(w.shared_selection), w.dtype, _ptr(q_sel),
         _ptr(index["member"], _i32p), _ptr(index["offset"], _i32p), _ptr(index["centroid"], _f64p),
         ctypes.c_int64(ncb), ctypes.c_int64(n), _ptr(rows, _i64p), _ptr(heads, _i32p), kcap, _ptr(idx, _i32p),
         _ptr(nn, _i32p), _ptr(sk, _f64p), _ptr(sk1, _f64p), _ptr(fl, _f64p), _ptr(nbk, _i32p))

@@ -512,7 +512,9 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
                     double *centroid, double *margin)
 {
     const int M = C / g, capg = cap_tok / g;
-    if (C % g || cap_tok % g || NB < 1 || NB > M || capg < 1)
+    /* capg * NB >= 2M: merging can always continue while more than NB buckets remain
+       (a stuck partition has every bucket above capg / 2, hence fewer than 2M / capg) */
+    if (C % g || cap_tok % g || NB < 1 || NB > M || capg < 1 || (int64_t)capg * NB < 2 * (int64_t)M)
         return 1;
     int64_t n_items = (int64_t)h_kv * batch * ncb_max;
 #pragma omp parallel for schedule(dynamic, 4)
@@ -647,12 +649,15 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
  * bucket_select: flat retrieval (LSA deep-read, §2.3).  The row's selector query
  * (the group's heads summed, over the row's queries) scores every bucket of the
  * complete cluster blocks that end at or before p_sel, s = qs . centroid / sqrt(d);
- * the kb best (score descending, bucket index ascending) are expanded to all their
- * member groups, written in ascending group order (width kcap, -1 padded).  The
- * near-tie data (sk, sk1, floor) refer to the bucket scores.
+ * the kb best (score descending, bucket index ascending) are expanded to their
+ * member groups, keeping those that meet the non-fixed region [n_init, p_sel - w + 1)
+ * (the sink and window are attended anyway: a group wholly inside them is left out,
+ * as for block candidates), written in ascending group order (width kcap, -1
+ * padded).  The near-tie data (sk, sk1, floor) refer to the bucket scores.
  */
 int or_bucket_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
-                     const int32_t *q_pos0, int g, int C, int NB, int kb, int shared, int dtype, const void *q_sel,
+                     const int32_t *q_pos0, int g, int n_init, int window, int C, int NB, int kb, int shared,
+                     int dtype, const void *q_sel,
                      const int32_t *member, const int32_t *offset, const double *centroid, int64_t ncb_max,
                      int64_t n_req, const int64_t *req_row, const int32_t *req_kvh, int kcap, int32_t *out_idx,
                      int32_t *out_n, double *out_sk, double *out_sk1, double *out_floor, int32_t *out_nbk)
@@ -712,11 +717,14 @@ int or_bucket_select(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, c
             const int32_t *mem = member + base * M;
             const int32_t *off = offset + base * (NB + 1);
             for (int x = off[lb]; x < off[lb + 1]; x++) {
+                const int64_t grp = blk * M + mem[x];
+                if (!(grp * g < p_sel - window + 1 && (grp + 1) * g > n_init))
+                    continue;                          /* wholly inside the sink or the window */
                 if (n_out >= kcap) {
                     bad |= 1;
                     break;
                 }
-                dst[n_out++] = (int32_t)(blk * M + mem[x]);
+                dst[n_out++] = (int32_t)grp;
             }
         }
         qsort(dst, (size_t)n_out, sizeof(int32_t), int_order);

@@ -335,7 +335,7 @@ def pin_bucket_pairs_and_centroids():
     """Four well separated pairs: each pair is each other's cheapest merge; centroids are
     the normalised pair sums."""
     pts = [(0, 5), (1, 5), (10, 0), (11, 0), (0, -10), (1, -10), (-20, 0), (-21, 0)]
-    w, ix = _bucket_index(pts, C=8, NB=4, cap=2)
+    w, ix = _bucket_index(pts, C=8, NB=4, cap=4)
     assert _buckets(ix) == [[0, 1], [2, 3], [4, 5], [6, 7]]
     for i, (a, b) in enumerate([(0, 1), (2, 3), (4, 5), (6, 7)]):
         s = np.add(pts[a], pts[b]).astype(np.float64)
@@ -356,7 +356,7 @@ def pin_bucket_ward_weighting():
     """Point 2 at 0 is nearer to the centroid of the pair {0, 1} (at -2.8) than to point 3
     (at 3), but Ward's cost n_A n_B / (n_A + n_B) d^2 is 5.23 against 4.5: it joins point 3."""
     pts = [(-3.0, 1.0), (-2.6, 1.0), (0.0, 1.0), (3.0, 1.0)]
-    w, ix = _bucket_index(pts, C=4, NB=2, cap=3)             # {0, 1, 2} would fit
+    w, ix = _bucket_index(pts, C=4, NB=2, cap=4)             # {0, 1, 2} would fit
     assert _buckets(ix) == [[0, 1], [2, 3]]
 
 
@@ -393,17 +393,21 @@ def pin_bucket_invariants():
 
 def pin_bucket_select():
     """kb >= every visible bucket selects every group of the complete cluster blocks that
-    end at or before p_sel; kb = 1 with the query along one centroid takes that bucket."""
+    end at or before p_sel, except those wholly inside the sink or window; kb = 1 with the
+    query along one centroid takes that bucket."""
     g, C, NB, cap = 4, 64, 8, 16
     w = wl(dtype=DTYPE_F32, h_q=2, h_kv=1, head_dim=16, seqlens_k=[5 * C + 10], seqlens_q=[40], block=g,
-           pool=POOL_L2SUM, bucket_block=C, bucket_count=NB, bucket_cap=cap, bucket_topk=1000)
+           pool=POOL_L2SUM, n_init=6, window=40, bucket_block=C, bucket_count=NB, bucket_cap=cap,
+           bucket_topk=1000)
     x = generate(w)
     ix = oracle.bucket_build(w, oracle.compress(w, x["k"]))
     r = oracle.bucket_select(w, x["q"], ix)
     for rr in range(w.rows):
         p = w.seqlens_k[0] - w.seqlens_q[0] + rr
         ncb = (p + 1) // C
-        assert r["idx"][rr, :r["n"][rr]].tolist() == list(range(ncb * C // g))
+        hi = p - w.window + 1                    # groups wholly in the sink or window are left out
+        want = [j for j in range(ncb * C // g) if j * g < hi and (j + 1) * g > w.n_init]
+        assert r["idx"][rr, :r["n"][rr]].tolist() == want
     # one bucket: a query along the centroid of bucket 5 of block 2 (unit centroids: it wins)
     w1 = w.scaled(bucket_topk=1, seqlens_q=[1], seqlens_k=[4 * C])
     target = ix["centroid"][0, 0, 2, 5]

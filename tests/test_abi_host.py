@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 4
+    assert sa.abi_version() == 5
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -197,3 +197,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def _bx(**kw):
+    b = _lib.SaBucketIndex()
+    base = dict(block_tokens=512, count=64, cap_tokens=16, blocks_max=8, centroid=FAKE, member=FAKE, offset=FAKE)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(b, k, v)
+    return b
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("block_tokens", 510, INVALID), ("block_tokens", 1024, UNSUPPORTED), ("count", 0, INVALID),
+    ("count", 129, INVALID), ("cap_tokens", 8, INVALID), ("cap_tokens", 6, INVALID), ("blocks_max", 3, INVALID),
+    ("centroid", None, INVALID), ("member", None, INVALID), ("centroid", FAKE + 4, INVALID)])
+def test_bucket_build_rejects(field, value, code):
+    p = params(block=4, max_k=4096, total_k=8192)                 # 128 groups per 512-token block
+    b = _bx(**{field: value})
+    vp = ctypes.c_void_p
+    assert status("sparse_attn_bucket_build", ctypes.byref(p), vp(FAKE), ctypes.byref(b), None) == code
+    assert _lib.lib().sparse_attn_last_error().decode()
+
+
+def test_bucket_select_checks():
+    p = params(block=4, max_k=4096, total_k=8192, topk=1024)
+    b = ctypes.byref(_bx())
+    n = ctypes.c_size_t(0)
+    assert status("sparse_attn_bucket_workspace_size", ctypes.byref(p), b, 256, ctypes.byref(n)) == 0 and n.value > 0
+    for nb, code in ((0, INVALID), (1025, INVALID), (257, INVALID)):     # 257 * 4 > the 1024-wide table
+        assert status("sparse_attn_bucket_workspace_size", ctypes.byref(p), b, nb, ctypes.byref(n)) == code
+    wide = params(block=4, max_k=4096, total_k=8192, topk=8192)
+    assert status("sparse_attn_bucket_workspace_size", ctypes.byref(wide), b, 256, ctypes.byref(n)) == UNSUPPORTED
+    vp = ctypes.c_void_p
+    assert status("sparse_attn_bucket_select", ctypes.byref(p), vp(FAKE), b, 256, vp(FAKE), vp(FAKE), vp(FAKE), 16,
+                  None) == WORKSPACE

@@ -47,6 +47,8 @@ MUTANTS = {
     "centroid_unnormalised": ("cen[(int64_t)nbk * d + e] = nrm > 0.0 ? S[a * d + e] / nrm : 0.0;",
                               "cen[(int64_t)nbk * d + e] = S[a * d + e];"),
     "bucket_blocks_off_by_one": ("int64_t ncb = (p_sel + 1) / C;", "int64_t ncb = (p_sel + 1 + C - 1) / C;"),
+    "expand_keeps_window": ("if (!(grp * g < p_sel - window + 1 && (grp + 1) * g > n_init))",
+                            "if (!((grp + 1) * g > n_init))"),
     "expand_drops_member": ("for (int x = off[lb]; x < off[lb + 1]; x++) {", "for (int x = off[lb]; x < off[lb + 1] - 1; x++) {"),
     "softmax_one_head": ("for (int hh = 0; hh < G; hh++) {\n                double m = -INFINITY, z = 0.0;",
                          "for (int hh = 0; hh < 1; hh++) {\n                double m = -INFINITY, z = 0.0;"),

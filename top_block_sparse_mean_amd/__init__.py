@@ -25,10 +25,11 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
-                   SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaParams,
-                   SparseAttnError, check, lib)
+                   SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaBucketIndex,
+                   SaParams, SparseAttnError, check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select", "fwd",
+           "BucketIndex", "bucket_build", "bucket_select",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
            "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
 
@@ -201,3 +202,50 @@ def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch
         p.s.timing_events[1] = None
     check("sparse_attn_fwd", st)
     return (out, lse) if want_lse else out
+
+
+class BucketIndex:
+    """Device arrays of an LSA flat bucket index (sa_bucket_index): cluster blocks of
+    ``block_tokens`` tokens, ``count`` buckets each, at most ``cap_tokens`` per bucket."""
+
+    def __init__(self, p: Params, block_tokens: int = 512, count: int = 64, cap_tokens: int = 16, device="cuda"):
+        s = p.s
+        self.blocks_max = max(s.max_k // block_tokens, 1)
+        m = block_tokens // s.block
+        self.centroid = torch.empty((s.h_kv, s.batch, self.blocks_max, count, s.head_dim), dtype=torch.float32,
+                                    device=device)
+        self.member = torch.empty((s.h_kv, s.batch, self.blocks_max, m), dtype=torch.int32, device=device)
+        self.offset = torch.empty((s.h_kv, s.batch, self.blocks_max, count + 1), dtype=torch.int32, device=device)
+        b = SaBucketIndex()
+        b.block_tokens, b.count, b.cap_tokens, b.blocks_max = block_tokens, count, cap_tokens, self.blocks_max
+        b.centroid, b.member, b.offset = self.centroid.data_ptr(), self.member.data_ptr(), self.offset.data_ptr()
+        self.s = b
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def bucket_build(p: Params, k_cmp: torch.Tensor, index: BucketIndex, stream=None) -> BucketIndex:
+    """Cluster the pooled keys of every complete cluster block into buckets."""
+    check("sparse_attn_bucket_build", lib().sparse_attn_bucket_build(p.ref(), _ptr(k_cmp), index.ref(),
+                                                                     _stream(stream)))
+    return index
+
+
+def bucket_select(p: Params, q_sel: torch.Tensor, index: BucketIndex, n_buckets: int,
+                  idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None):
+    """Flat bucket retrieval; the table width is p's topk (>= n_buckets * cap / block)."""
+    dev = q_sel.device
+    if idx is None:
+        idx = torch.empty((p.s.h_kv, p.rows, p.s.topk), dtype=torch.int32, device=dev)
+    if n_idx is None:
+        n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
+    nb = ctypes.c_size_t(0)
+    check("sparse_attn_bucket_workspace_size",
+          lib().sparse_attn_bucket_workspace_size(p.ref(), index.ref(), int(n_buckets), ctypes.byref(nb)))
+    ws, nbytes = _ws(nb.value, dev, ws)
+    check("sparse_attn_bucket_select",
+          lib().sparse_attn_bucket_select(p.ref(), _ptr(q_sel), index.ref(), int(n_buckets), _ptr(idx), _ptr(n_idx),
+                                          _ptr(ws), nbytes, _stream(stream)))
+    return idx, n_idx

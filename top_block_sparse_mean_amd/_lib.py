@@ -18,7 +18,8 @@ SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX, SA_SELECT_ATTN = 0, 1, 2, 3
 # Every symbol include/sparse_attn.h declares.
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
-           "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_fwd")
+           "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_fwd",
+           "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select")
 
 
 class SaParams(ctypes.Structure):
@@ -51,6 +52,18 @@ class SaParams(ctypes.Structure):
         ("select_mode", ctypes.c_int32),
         ("select_temperature", ctypes.c_float),
         ("attn_lse", ctypes.c_void_p),
+    ]
+
+
+class SaBucketIndex(ctypes.Structure):
+    _fields_ = [
+        ("block_tokens", ctypes.c_int32),
+        ("count", ctypes.c_int32),
+        ("cap_tokens", ctypes.c_int32),
+        ("blocks_max", ctypes.c_int32),
+        ("centroid", ctypes.c_void_p),
+        ("member", ctypes.c_void_p),
+        ("offset", ctypes.c_void_p),
     ]
 
 

@@ -133,6 +133,7 @@ sa::KP make_kp(const sa_params *p)
                              ? 1.0f / p->select_temperature
                              : 1.0f / std::sqrt((float)p->head_dim);
     k.attn_lse = p->attn_lse;
+    k.bucket_c = k.bucket_nb = k.bucket_nblk = 0;
     k.block_table = p->block_table;
     k.max_pages = p->block_table ? p->max_pages : 0;
     k.page_shift = 0;
@@ -228,6 +229,101 @@ sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const voi
     sa::KP kp = make_kp(p);
     return device_status(sa::launch_append(kp, p->dtype, k_new, v_new, k, v, k_cmp, (hipStream_t)stream),
                          "append launch");
+}
+
+static sa_status check_buckets(const sa_params *p, const sa_bucket_index *bx, sa::BucketArgs *out)
+{
+    if (!bx)
+        return fail(SA_ERR_INVALID_ARG, "bucket index is NULL");
+    const int g = p->block;
+    if (bx->block_tokens < g || bx->block_tokens % g || bx->cap_tokens < g || bx->cap_tokens % g)
+        return fail(SA_ERR_INVALID_ARG, "block_tokens (%d) and cap_tokens (%d) must be positive multiples of block",
+                    bx->block_tokens, bx->cap_tokens);
+    const int M = bx->block_tokens / g;
+    if (M > 128)
+        return fail(SA_ERR_UNSUPPORTED, "block_tokens / block = %d groups per cluster block exceeds 128", M);
+    if (bx->count < 1 || bx->count > M)
+        return fail(SA_ERR_INVALID_ARG, "count (%d) must be in [1, block_tokens / block = %d]", bx->count, M);
+    if ((long long)(bx->cap_tokens / g) * bx->count < 2LL * M)
+        return fail(SA_ERR_INVALID_ARG, "(cap_tokens / block) * count must be >= 2 * block_tokens / block");
+    if (bx->blocks_max < p->max_k / bx->block_tokens || bx->blocks_max < 0)
+        return fail(SA_ERR_INVALID_ARG, "blocks_max (%d) below max_k / block_tokens (%d)", bx->blocks_max,
+                    p->max_k / bx->block_tokens);
+    if (!bx->centroid || !bx->member || !bx->offset || !aligned16(bx->centroid))
+        return fail(SA_ERR_INVALID_ARG, "centroid (16-byte aligned), member and offset are required");
+    out->C = bx->block_tokens;
+    out->NB = bx->count;
+    out->cap = bx->cap_tokens;
+    out->nblk = bx->blocks_max;
+    out->centroid = bx->centroid;
+    out->member = bx->member;
+    out->offset = bx->offset;
+    return SA_OK;
+}
+
+sa_status sparse_attn_bucket_build(const sa_params *p, const float *k_cmp, const sa_bucket_index *bx, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    sa::BucketArgs B;
+    if ((s = check_buckets(p, bx, &B)) != SA_OK)
+        return s;
+    if (!k_cmp || !aligned16(k_cmp))
+        return fail(SA_ERR_INVALID_ARG, "k_cmp is required (16-byte aligned)");
+    sa::KP kp = make_kp(p);
+    return device_status(sa::launch_bucket_build(kp, k_cmp, B, (hipStream_t)stream), "bucket build launch");
+}
+
+static sa_status check_bucket_select(const sa_params *p, const sa_bucket_index *bx, int32_t n_buckets,
+                                     sa::BucketArgs *B)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if ((s = check_buckets(p, bx, B)) != SA_OK)
+        return s;
+    if (n_buckets < 1 || n_buckets > 1024)
+        return fail(SA_ERR_INVALID_ARG, "n_buckets must be in [1, 1024] (got %d)", n_buckets);
+    const long long need = (long long)n_buckets * (bx->cap_tokens / p->block);
+    if (p->topk < need)
+        return fail(SA_ERR_INVALID_ARG, "topk (%d, the table width) below n_buckets * cap_tokens / block = %lld",
+                    p->topk, need);
+    if (p->topk > 4096)
+        return fail(SA_ERR_UNSUPPORTED, "bucket selection tables are at most 4096 groups wide (topk %d)", p->topk);
+    return SA_OK;
+}
+
+sa_status sparse_attn_bucket_workspace_size(const sa_params *p, const sa_bucket_index *bx, int32_t n_buckets,
+                                            size_t *bytes)
+{
+    sa::BucketArgs B;
+    sa_status s = check_bucket_select(p, bx, n_buckets, &B);
+    if (s != SA_OK)
+        return s;
+    if (bytes)
+        *bytes = sa::bucket_select_workspace_bytes(make_kp(p), B, n_buckets);
+    return ok();
+}
+
+sa_status sparse_attn_bucket_select(const sa_params *p, const void *q_sel, const sa_bucket_index *bx,
+                                    int32_t n_buckets, int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes,
+                                    void *stream)
+{
+    sa::BucketArgs B;
+    sa_status s = check_bucket_select(p, bx, n_buckets, &B);
+    if (s != SA_OK)
+        return s;
+    if (!q_sel || !idx || !n_idx || !aligned16(q_sel))
+        return fail(SA_ERR_INVALID_ARG, "q_sel (16-byte aligned), idx and n_idx are required");
+    sa::KP kp = make_kp(p);
+    const size_t need = sa::bucket_select_workspace_bytes(kp, B, n_buckets);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(SA_ERR_WORKSPACE, "bucket select needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    return device_status(sa::launch_bucket_select(kp, p->dtype, q_sel, B, n_buckets, idx, n_idx, ws,
+                                                  (hipStream_t)stream),
+                         "bucket select launch");
 }
 
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,

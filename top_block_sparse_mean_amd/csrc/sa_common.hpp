@@ -30,6 +30,9 @@ struct KP {
     int select_mode;              // 0 sum of heads, 1 sum of per-head softmaxes, 2 max over heads
     float head_score_scale;       // per-head score scale (1/tau or 1/sqrt(d))
     const float *attn_lse;        // select mode 3: [h_q, total_q] log-sum-exp of a dense verify pass
+    // bucket selection (bucket_nb > 0): candidates are the buckets of the complete cluster
+    // blocks of bucket_c tokens that end at or before p_sel, bucket_nb per block
+    int bucket_c, bucket_nb, bucket_nblk;
 };
 
 struct Seq {
@@ -104,6 +107,24 @@ __device__ __host__ __forceinline__ void cand_range(int g, int n_init, int windo
     if (j_hi < j_lo)
         j_hi = j_lo;
 }
+
+// Candidate range of a selection row: blocks (cand_range), or, for bucket selection,
+// the buckets of the complete cluster blocks ending at or before p_sel.
+__device__ __host__ __forceinline__ void row_cands(const KP &P, int n_k, int p_sel, int &j_lo, int &j_hi)
+{
+    if (P.bucket_nb > 0) {
+        int ncb = p_sel < 0 ? 0 : (p_sel + 1) / P.bucket_c;
+        ncb = ncb < n_k / P.bucket_c ? ncb : n_k / P.bucket_c;
+        ncb = ncb < P.bucket_nblk ? ncb : P.bucket_nblk;
+        j_lo = 0;
+        j_hi = ncb * P.bucket_nb;
+        return;
+    }
+    cand_range(P.g, P.n_init, P.window, n_k, p_sel, j_lo, j_hi);
+}
+
+// The first candidate index any row can have.
+__device__ __host__ __forceinline__ int first_cand(const KP &P) { return P.bucket_nb > 0 ? 0 : P.n_init / P.g; }
 
 // The attended set of one query as three disjoint ranges of positions:
 //   [0, n1) -> init tokens; [n1, n1+n2) -> tokens of the selected blocks clipped

@@ -11,6 +11,19 @@ hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, 
 hipError_t launch_append(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
                          float *k_cmp, hipStream_t st);
 
+// The LSA flat bucket index: C tokens per cluster block, NB buckets per block, at most
+// cap tokens per bucket, nblk blocks per (sequence, KV head) in the arrays.
+struct BucketArgs {
+    int C, NB, cap, nblk;
+    float *centroid;      // [h_kv, batch, nblk, NB, d]
+    int32_t *member;      // [h_kv, batch, nblk, C/g]
+    int32_t *offset;      // [h_kv, batch, nblk, NB + 1]
+};
+hipError_t launch_bucket_build(const KP &P, const float *k_cmp, const BucketArgs &B, hipStream_t st);
+size_t bucket_select_workspace_bytes(const KP &P, const BucketArgs &B, int kb);
+hipError_t launch_bucket_select(const KP &P, int dtype, const void *q_sel, const BucketArgs &B, int kb, int32_t *idx,
+                                int32_t *n_idx, void *ws, hipStream_t st);
+
 int select_plan(const KP &P);
 size_t select_workspace_bytes(const KP &P, int plan);
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,

@@ -61,7 +61,7 @@ __device__ __forceinline__ RowGeo row_geo(const KP &P, long long row)
         r.n_k = s.n_k;
         r.k_off = s.k_off;
     }
-    cand_range(P.g, P.n_init, P.window, r.n_k, r.p_sel, r.j_lo, r.j_hi);
+    row_cands(P, r.n_k, r.p_sel, r.j_lo, r.j_hi);
     const int cap = P.g == 1 ? P.max_k : P.nb_max;     // rows of the key table / workspace
     r.j_hi = min(r.j_hi, cap);
     r.j_lo = min(r.j_lo, r.j_hi);
@@ -934,7 +934,7 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
         return;
     const int r_end = min(r0 + 64, s.n_q);
     int jlo_last, jhi_last;
-    cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
+    row_cands(P, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
     jhi_last = min(jhi_last, (int)stride);
     const int jc0 = jlo_last + blockIdx.x * col_tiles * 64;
     if (jc0 >= jhi_last)
@@ -977,10 +977,10 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
             const int rl = r0 + wr + 16 * a + 4 * lk + i;
             int jl = 0, jh = 0;
             if (rl < r_end)
-                cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + rl, jl, jh);
+                row_cands(P, s.n_k, s.q0 + rl, jl, jh);
             jh_row[a][i] = jh > jl ? min(jh, (int)stride) : 0;
         }
-    const int j_first = P.n_init / P.g;
+    const int j_first = first_cand(P);
     // staging: thread tid holds pieces tid + 256 u of the tile (row = piece / pieces per row)
     const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(kbase);
     const long long row_stride = P.g == 1 ? (long long)P.h_kv * kRowBytes : kRowBytes;
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
         return;
     // the candidate range of any row with candidates starts at n_init / g: load first, then
     // resolve the row's geometry while the loads are in flight
-    const int j_first = P.n_init / P.g;
+    const int j_first = first_cand(P);
     const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
     uint32_t kr[KPL];
 #pragma unroll

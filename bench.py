@@ -105,14 +105,19 @@ class Step:
     tokens, so every step rewrites the same values.  page_size > 0 keeps K and V in
     a paged cache read through a block table."""
 
-    def __init__(self, w, x, device, page_size=0):
+    def __init__(self, w, x, device, page_size=0, buckets=False):
         self.w = w
+        self.buckets = buckets
         self.layout = page_layout(w.seqlens_k, page_size, w.seed) if page_size else None
         if self.layout is not None:
             x = dict(x, k=to_pages(x["k"], self.layout), v=to_pages(x["v"], self.layout))
         self.x = x
+        if buckets:          # the table holds the chosen buckets' groups: width = buckets x cap / g
+            w = w.scaled(topk=w.bucket_topk * (w.bucket_cap // w.block))
+            self.w = w
         self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
+        self.index = sa.BucketIndex(self.p, w.bucket_block, w.bucket_count, w.bucket_cap) if buckets else None
         sel_b, fwd_b = sa.workspace_size(self.p)
         self.ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
         self.ws_fwd = torch.empty(max(fwd_b, 16), dtype=torch.uint8, device=device)
@@ -121,6 +126,16 @@ class Step:
         self.idx = torch.empty((w.h_kv, self.p.rows, max(w.topk, 1)), dtype=torch.int32, device=device)
         self.n_idx = torch.empty((w.h_kv, self.p.rows), dtype=torch.int32, device=device)
         self.out = torch.empty_like(x["q"])
+        if buckets:
+            # the history's buckets exist before the chunk arrives: build them once, untimed
+            self.build_from = min(nk - nq for nk, nq in zip(w.seqlens_k, w.seqlens_q)) // w.bucket_block
+            if self.k_cmp is not None:
+                sa.compress(self.p, x["k"], self.k_cmp)
+                sa.bucket_build(self.p, self.k_cmp, self.index)
+            nb = ctypes.c_size_t(0)
+            sa._lib.check("sparse_attn_bucket_workspace_size", sa.lib().sparse_attn_bucket_workspace_size(
+                self.p.ref(), self.index.ref(), int(w.bucket_topk), ctypes.byref(nb)))
+            self.ws_bkt = torch.empty(max(nb.value, 16), dtype=torch.uint8, device=device)
         if self.decode:
             # the new tokens: the last M_b of every sequence (packed rows of the generated K/V)
             new, o = [], 0
@@ -145,8 +160,13 @@ class Step:
             sa.append_kv(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp)
         elif self.k_cmp is not None:
             sa.compress(self.p, x["k"], self.k_cmp)
+            if self.index is not None:      # the chunk's new cluster blocks; earlier ones are frozen
+                sa.bucket_build(self.p, self.k_cmp, self.index, build_from=self.build_from)
         mark(1)
-        sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
+        if self.index is not None:
+            sa.bucket_select(self.p, x["q"], self.index, self.w.bucket_topk, self.idx, self.n_idx, ws=self.ws_bkt)
+        else:
+            sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
         mark(2)
         sa.fwd(self.p, x["q"], x["k"], x["v"], self.idx, self.n_idx, out=self.out, ws=self.ws_fwd,
                events=events)
@@ -219,7 +239,7 @@ def measured_peaks(device, prefill):
     return out
 
 
-def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks):
+def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks, buckets=False):
     """Each stage of one step against its own bound, on algorithmic work.
     compress: keys read once + pooled keys written (HBM).  select: decode reads the
     pooled keys (or, with g = 1, the raw keys) once per step (HBM); prefill scores every
@@ -247,7 +267,10 @@ def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks):
                     r["frac_of_measured"] = round(ach / peaks[mkey], 4)
         rep[name] = r
 
-    if decode:
+    if buckets:
+        # pooling, then Ward clustering of every cluster block (pair costs in LDS): no single bound
+        add("index", stage_ms[0], None, "mixed")
+    elif decode:
         # the new tokens' K/V rows written and their blocks re-pooled: launch-bound
         add("append", stage_ms[0], None, "launch")
     elif g > 1:
@@ -260,7 +283,10 @@ def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks):
         cand = 0
         for nk, nq in zip(w.seqlens_k, w.seqlens_q):
             p = range(nk - nq, nk)
-            cand += sum(q // g + 1 for q in p)
+            if buckets:        # the centroids of the complete cluster blocks before each row
+                cand += sum((q + 1) // w.bucket_block * w.bucket_count for q in p)
+            else:
+                cand += sum(q // g + 1 for q in p)
         add("select", stage_ms[1], 2.0 * d * w.h_kv * cand, "mfma_fp32")
         add("fwd", stage_ms[2], attn_flops, "mfma_bf16" if w.dtype == DTYPE_BF16 else "alu_fp32")
     return rep
@@ -505,6 +531,10 @@ def main():
                          "max over heads")
     ap.add_argument("--pool-overlap", type=int, default=0,
                     help="pooling windows reach this many tokens before their block (0: disjoint)")
+    ap.add_argument("--lsa-buckets", action="store_true",
+                    help="prefill workloads: select through the LSA flat bucket index (cluster blocks of 512 "
+                         "tokens, 64 buckets of at most 16 tokens; 256 buckets per query); a step clusters the "
+                         "blocks its chunk completes, the history's buckets are built beforehand")
     ap.add_argument("--s3r-refresh", action="store_true",
                     help="draft workload: also time the dense verify pass and the refreshed selection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -542,7 +572,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    step = Step(w, x, device, page_size=args.page_size)
+    step = Step(w, x, device, page_size=args.page_size, buckets=args.lsa_buckets)
+    w = step.w
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -617,7 +648,7 @@ def main():
         extra["needle_recall"] = needle_recall(w, idx_h, n_h)
     if w.name == "bf16_draft_decode":
         extra["us_per_draft_token"] = round(ms_step * 1e3 / w.seqlens_q[0], 3)
-    extra["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks)
+    extra["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks, buckets=args.lsa_buckets)
     if args.s3r_refresh and w.shared_selection:
         r = s3r_refresh(w, step, min(args.steps, 20), device)
         r["round_us"] = round(ms_step * 1e3 + (r["verify_ms"] + r["refresh_ms"]) * 1e3, 2)
@@ -642,6 +673,7 @@ def main():
                    "n_init": w.n_init, "window": w.window, "kv_layout": (f"paged{args.page_size}" if args.page_size
                                                                           else "packed"),
                    "select_mode": args.select_mode, "pool_overlap": w.pool_overlap,
+                   "selector": "lsa_buckets" if args.lsa_buckets else "blocks",
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "attn_kernel_ms": round(attn_ms, 5),

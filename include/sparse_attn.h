@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 5
+#define SPARSE_ATTN_ABI_VERSION 6
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -152,6 +152,9 @@ typedef struct sa_bucket_index {
                                   that is not complete                                         */
     int32_t *offset;           /* device [h_kv, batch, blocks_max, NB + 1]: bucket i holds
                                   member[offset[i] .. offset[i+1])                             */
+    int32_t build_from;        /* sparse_attn_bucket_build leaves cluster blocks before this
+                                  one untouched (a stream of chunks clusters each block once,
+                                  as it completes; buckets are frozen once built)             */
 } sa_bucket_index;
 
 /* SPARSE_ATTN_ABI_VERSION of the built library. */

@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 5
+    assert sa.abi_version() == 6
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -211,7 +211,8 @@ def _bx(**kw):
 @pytest.mark.parametrize("field,value,code", [
     ("block_tokens", 510, INVALID), ("block_tokens", 1024, UNSUPPORTED), ("count", 0, INVALID),
     ("count", 129, INVALID), ("cap_tokens", 8, INVALID), ("cap_tokens", 6, INVALID), ("blocks_max", 3, INVALID),
-    ("centroid", None, INVALID), ("member", None, INVALID), ("centroid", FAKE + 4, INVALID)])
+    ("centroid", None, INVALID), ("member", None, INVALID), ("centroid", FAKE + 4, INVALID),
+    ("build_from", -1, INVALID)])
 def test_bucket_build_rejects(field, value, code):
     p = params(block=4, max_k=4096, total_k=8192)                 # 128 groups per 512-token block
     b = _bx(**{field: value})

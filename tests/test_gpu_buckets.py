@@ -138,3 +138,26 @@ def test_full_chunked_prefill_1m_buckets_sampled():
     att = oracle.attend(w, x["q"], x["k"], x["v"], idx, n_idx, reqs=reqs, heads=hs)
     gout = out.float().cpu().reshape(w.total_q, w.h_q, w.head_dim)[reqs, hs].double().numpy()
     parity.check_output(w, gout, att["out"])
+
+
+def test_incremental_build():
+    """Building from block f rewrites blocks f.. exactly as a full build and leaves the
+    earlier blocks untouched (a chunk stream clusters each block once)."""
+    w = SHAPES["lsa_chunk"]()
+    w = w.scaled(topk=_width(w))
+    x, xg = parity.gen_pair(w)
+    p = parity.params_for(w)
+    kc = sa.compress(p, xg["k"])
+    full = sa.bucket_build(p, kc, sa.BucketIndex(p, w.bucket_block, w.bucket_count, w.bucket_cap))
+    part = sa.BucketIndex(p, w.bucket_block, w.bucket_count, w.bucket_cap)
+    part.member.fill_(-7)
+    part.offset.fill_(-7)
+    part.centroid.fill_(7.0)
+    f = 20
+    sa.bucket_build(p, kc, part, build_from=f)
+    torch.cuda.synchronize()
+    assert (part.member[:, :, :f] == -7).all() and (part.offset[:, :, :f] == -7).all()
+    assert (part.centroid[:, :, :f] == 7.0).all()
+    assert torch.equal(part.member[:, :, f:], full.member[:, :, f:])
+    assert torch.equal(part.offset[:, :, f:], full.offset[:, :, f:])
+    assert torch.equal(part.centroid[:, :, f:], full.centroid[:, :, f:])

@@ -225,8 +225,10 @@ class BucketIndex:
         return ctypes.byref(self.s)
 
 
-def bucket_build(p: Params, k_cmp: torch.Tensor, index: BucketIndex, stream=None) -> BucketIndex:
-    """Cluster the pooled keys of every complete cluster block into buckets."""
+def bucket_build(p: Params, k_cmp: torch.Tensor, index: BucketIndex, stream=None, build_from: int = 0) -> BucketIndex:
+    """Cluster the pooled keys of every complete cluster block from ``build_from`` on into buckets
+    (earlier blocks are left as they are)."""
+    index.s.build_from = int(build_from)
     check("sparse_attn_bucket_build", lib().sparse_attn_bucket_build(p.ref(), _ptr(k_cmp), index.ref(),
                                                                      _stream(stream)))
     return index

@@ -64,6 +64,7 @@ class SaBucketIndex(ctypes.Structure):
         ("centroid", ctypes.c_void_p),
         ("member", ctypes.c_void_p),
         ("offset", ctypes.c_void_p),
+        ("build_from", ctypes.c_int32),
     ]
 
 

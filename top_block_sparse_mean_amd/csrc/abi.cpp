@@ -255,6 +255,9 @@ static sa_status check_buckets(const sa_params *p, const sa_bucket_index *bx, sa
     out->NB = bx->count;
     out->cap = bx->cap_tokens;
     out->nblk = bx->blocks_max;
+    if (bx->build_from < 0)
+        return fail(SA_ERR_INVALID_ARG, "build_from must be >= 0 (got %d)", bx->build_from);
+    out->from = bx->build_from;
     out->centroid = bx->centroid;
     out->member = bx->member;
     out->offset = bx->offset;

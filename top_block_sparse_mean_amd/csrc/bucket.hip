@@ -47,10 +47,11 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
     __shared__ int sh_into[kBucketMaxM], sh_pair[kBucketMaxM], sh_bk[kBucketMaxM], sh_off[kBucketMaxM + 1];
     __shared__ float sh_nnc[kBucketMaxM];
     const int M = B.C / P.g, capg = B.cap / P.g, NB = B.NB;
-    const long long item = blockIdx.x;
-    const int blk = (int)(item % B.nblk);
-    const int b = (int)((item / B.nblk) % P.batch);
-    const int c = (int)(item / ((long long)B.nblk * P.batch));
+    const int span = B.nblk - B.from;                            // blocks from B.from on
+    const int blk = B.from + (int)(blockIdx.x % span);
+    const int b = (int)((blockIdx.x / span) % P.batch);
+    const int c = (int)(blockIdx.x / ((long long)span * P.batch));
+    const long long item = ((long long)c * P.batch + b) * B.nblk + blk;
     const int tid = threadIdx.x;
     const Seq s = seq_info(P, b);
     int32_t *mem = B.member + item * M;
@@ -287,9 +288,9 @@ __global__ __launch_bounds__(256) void bucket_expand_kernel(KP P, BucketArgs B, 
 
 hipError_t launch_bucket_build(const KP &P, const float *k_cmp, const BucketArgs &B, hipStream_t st)
 {
-    const long long items = (long long)P.h_kv * P.batch * B.nblk;
-    if (items == 0)
+    if (B.from >= B.nblk)
         return hipSuccess;
+    const long long items = (long long)P.h_kv * P.batch * (B.nblk - B.from);
     if (P.d == 128)
         bucket_build_kernel<128><<<dim3((unsigned)items), dim3(256), 0, st>>>(P, k_cmp, B);
     else

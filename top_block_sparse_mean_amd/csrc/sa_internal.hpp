@@ -14,7 +14,7 @@ hipError_t launch_append(const KP &P, int dtype, const void *k_new, const void *
 // The LSA flat bucket index: C tokens per cluster block, NB buckets per block, at most
 // cap tokens per bucket, nblk blocks per (sequence, KV head) in the arrays.
 struct BucketArgs {
-    int C, NB, cap, nblk;
+    int C, NB, cap, nblk, from;
     float *centroid;      // [h_kv, batch, nblk, NB, d]
     int32_t *member;      // [h_kv, batch, nblk, C/g]
     int32_t *offset;      // [h_kv, batch, nblk, NB + 1]

@@ -1164,6 +1164,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
     __shared__ int cand_idx[kCompactCap];
     __shared__ int sh_scan[NW];
     __shared__ int sh_digit, sh_above, sh_ncand;
+    __shared__ int sh_cnt3[3];
     const long long row = blockIdx.x;
     const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id();
     RowGeo r = row_geo(P, row);
@@ -1283,36 +1284,49 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         __syncthreads();
     }
     if (gather) {
-        // exact pick of rem among the gathered keys: tau = rem-th largest key
+        // exact pick of rem among the gathered keys: tau = rem-th largest key.  Each count
+        // is one barrier: wavefront ballots summed by LDS atomics into one of three
+        // rotating counters (the one two rounds ahead is cleared once every thread has
+        // read the last round's).
         const int nc = sh_ncand;
+        if (tid < 3)
+            sh_cnt3[tid] = 0;
+        __syncthreads();
+        int rnd = 0;
+        auto block_count = [&](auto pred) -> int {
+            int cnt = 0;
+            for (int base = 0; base < nc; base += NT) {
+                const int x = base + tid;
+                cnt += __popcll(__ballot(x < nc && pred(x)));
+            }
+            if (lane == 0 && cnt)
+                atomicAdd(&sh_cnt3[rnd % 3], cnt);
+            __syncthreads();
+            const int tot = sh_cnt3[rnd % 3];
+            if (tid == 0)
+                sh_cnt3[(rnd + 2) % 3] = 0;
+            rnd++;
+            return tot;
+        };
         uint32_t tau = prefix;
         for (int bit = 31; bit >= 0; --bit) {
             if (pmask & (1u << bit))
                 continue;                                    // fixed by the prefix
             const uint32_t cand = tau | (1u << bit);
-            int cnt = 0;
-            for (int x = tid; x < nc; x += NT)
-                cnt += cand_key[x] >= cand ? 1 : 0;
-            cnt = block_scan_int<NT>(cnt, sh_scan).y;
-            if (cnt >= rem)
+            if (block_count([&](int x) { return cand_key[x] >= cand; }) >= rem)
                 tau = cand;
         }
-        int gt = 0;
-        for (int x = tid; x < nc; x += NT)
-            gt += cand_key[x] > tau ? 1 : 0;
-        const int n_gt = block_scan_int<NT>(gt, sh_scan).y;
+        const int n_gt = block_count([&](int x) { return cand_key[x] > tau; });
         const int need_eq = rem - n_gt;
-        // among keys == tau: the need_eq lowest indices (binary search on the index)
-        int ilim = 0;                                        // select eq keys with index < ilim... found below
-        {
+        // among keys == tau: the need_eq lowest indices (binary search on the index, skipped
+        // when every equal key is taken -- the usual case of one)
+        const int n_eq = block_count([&](int x) { return cand_key[x] == tau; });
+        int ilim = 1 << 30;
+        if (n_eq > need_eq) {
             int lo = 0;                                      // largest bound with count(idx < bound) <= need_eq
             for (int bit = 18; bit >= 0; --bit) {
                 const int candb = lo | (1 << bit);
-                int cnt = 0;
-                for (int x = tid; x < nc; x += NT)
-                    cnt += (cand_key[x] == tau && cand_idx[x] < candb) ? 1 : 0;
-                cnt = block_scan_int<NT>(cnt, sh_scan).y;
-                if (cnt <= need_eq)
+                if (block_count([&](int x) { return cand_key[x] == tau && cand_idx[x] < candb; }) <= need_eq)
                     lo = candb;
             }
             ilim = lo;

@@ -128,7 +128,9 @@ def test_workspace_sizes():
     # are enough units, else partials for the combine
     sel, fwd = _ws(params())
     assert sel == 2 * 2 * 1 * 8 * 8 and fwd > 0 and fwd % (130 * 4) == 0
-    assert _ws(params(batch=256, total_q=256, max_k=4096, total_k=256 * 4096)) == (2 * 256 * 1 * 8 * 8, 0)
+    assert _ws(params(batch=64, total_q=64, max_k=4096, total_k=64 * 4096))[0] == 2 * 64 * 1 * 8 * 8
+    # rows x KV heads >= 256: one workgroup per (row, KV head) selects from LDS, no workspace
+    assert _ws(params(batch=128, total_q=128, max_k=4096, total_k=128 * 4096)) == (0, 0)
     assert _ws(params(max_k=32768, total_k=65536, topk=32))[0] == 2 * 2 * 4 * 32 * 8
     # prefill: scores of every (row, block) are kept: h_kv * rows * nb_max * 4
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)

@@ -78,10 +78,22 @@ DECODE_EDGE = {
 }
 
 
-@pytest.mark.parametrize("case", list(DECODE_EDGE))
-def test_decode_selection_cases(case):
-    """One query per sequence: the part-scoring + merge selection plan."""
-    w = small("bf16_decode_32k").scaled(**DECODE_EDGE[case])
+# selection plans for rows of one query with at most 1024 candidates: parts of 128
+# candidates + a merge (few rows), or one 16-wavefront workgroup per (row, KV head)
+ROW_PLANS = {"parts": "1", "fused": "5"}
+
+
+@pytest.mark.parametrize("plan", list(ROW_PLANS))
+@pytest.mark.parametrize("case", list(DECODE_EDGE) + ["default", "max_cand"])
+def test_decode_selection_cases(case, plan, monkeypatch):
+    """One query per sequence: both selection plans for rows of up to 1024 candidates."""
+    monkeypatch.setenv("SPARSE_ATTN_SELECT_PLAN", ROW_PLANS[plan])
+    w = small("bf16_decode_32k")
+    if case == "max_cand":                # 1024 candidates: two scoring passes of the fused plan
+        w = w.scaled(block=4, topk=40, n_init=0, window=1, seqlens_k=[4096, 4096, 3001, 1030, 130])
+        assert w.nb_max == 1024
+    elif case != "default":
+        w = w.scaled(**DECODE_EDGE[case])
     x, xg = parity.gen_pair(w)
     parity.full_check(w, x, xg)
 

@@ -244,39 +244,51 @@ __global__ __launch_bounds__(256) void append_pool_kernel(KP P, const T *__restr
     if (!pooled_block(P, s, kPoolAppended, n_blk_iter, jj, j))
         return;
     const int t0 = max(0, j * P.g - P.pool_overlap), t1 = min(j * P.g + P.g, s.n_k);   // pooling window
+    // UN token rounds of the window are loaded before any is summed (the window of a
+    // 64-token block is 4 rounds: one memory latency instead of four); the sums run
+    // in token-round order as without the batching.
+    constexpr int UN = 4;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int it = 0; it < P.g + P.pool_overlap; it += TG) {
-        const int t = t0 + it + tg;
-        const bool ok = t < t1;
-        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (ok) {
-            const long long crow = (k_base + map.row(t)) * P.h_kv + c;
-            if (t >= s.q0 && t < s.q0 + s.n_q) {
-                const long long nrow = (s.q_off + (t - s.q0)) * P.h_kv + c;
-                load8(k_new + nrow * D + chunk * 8, x);
-                constexpr int PPC = 8 * (int)sizeof(T) / 16;        // 16-byte pieces per 8 elements
-                if (t >= j * P.g)                                    // the block's own tokens only
+    for (int it0 = 0; it0 < P.g + P.pool_overlap; it0 += UN * TG) {
+        float x[UN][8];
 #pragma unroll
-                    for (int u = 0; u < PPC; u++) {
-                        copy_piece(k_new, k, nrow, crow, D, chunk * PPC + u);
-                        copy_piece(v_new, v, nrow, crow, D, chunk * PPC + u);
-                    }
-            } else {
-                load8(k + crow * D + chunk * 8, x);
-            }
-        }
-        float sc = 1.0f;
-        if (POOL == 1) {
-            float ss = 0.f;
+        for (int u = 0; u < UN; u++) {
+            const int t = t0 + it0 + u * TG + tg;
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                ss += x[e] * x[e];
-            ss = group_sum<L>(ss);
-            sc = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+                x[u][e] = 0.f;
+            if (t < t1) {
+                const long long crow = (k_base + map.row(t)) * P.h_kv + c;
+                if (t >= s.q0 && t < s.q0 + s.n_q) {
+                    const long long nrow = (s.q_off + (t - s.q0)) * P.h_kv + c;
+                    load8(k_new + nrow * D + chunk * 8, x[u]);
+                    constexpr int PPC = 8 * (int)sizeof(T) / 16;        // 16-byte pieces per 8 elements
+                    if (t >= j * P.g)                                    // the block's own tokens only
+#pragma unroll
+                        for (int w = 0; w < PPC; w++) {
+                            copy_piece(k_new, k, nrow, crow, D, chunk * PPC + w);
+                            copy_piece(v_new, v, nrow, crow, D, chunk * PPC + w);
+                        }
+                } else {
+                    load8(k + crow * D + chunk * 8, x[u]);
+                }
+            }
         }
 #pragma unroll
-        for (int e = 0; e < 8; e++)
-            acc[e] += x[e] * sc;
+        for (int u = 0; u < UN; u++) {
+            float sc = 1.0f;
+            if (POOL == 1) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    ss += x[u][e] * x[u][e];
+                ss = group_sum<L>(ss);
+                sc = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                acc[e] += x[u][e] * sc;
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; e++)

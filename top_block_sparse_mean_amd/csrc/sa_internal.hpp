@@ -5,7 +5,7 @@
 
 namespace sa {
 
-enum { kSelectEmpty = 0, kSelectRow = 1, kSelectSplit = 2, kSelectTile = 3, kSelectHeads = 4 };
+enum { kSelectEmpty = 0, kSelectRow = 1, kSelectSplit = 2, kSelectTile = 3, kSelectHeads = 4, kSelectRowFused = 5 };
 
 hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, int n_tail, hipStream_t st);
 hipError_t launch_append(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,

@@ -87,7 +87,9 @@ template <int KPL, typename Emit>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int need, Emit emit)
 {
     const int lane = lane_id();
-    // counts come from ballots (one scalar popcount per slot): no cross-lane data moves
+    // counts come from ballots (one scalar popcount per slot): no cross-lane data moves.
+    // A threshold with exactly `need` keys at or above it ends the search: those keys
+    // are the selection (keys equal to it included), whatever the lower bits.
     uint32_t tau = 0;
     for (int bit = 31; bit >= 0; --bit) {
         uint32_t cand = tau | (1u << bit);
@@ -97,6 +99,8 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
             cnt += __popcll(__ballot(m * kWave + lane < n && key[m] >= cand));
         if (cnt >= need)
             tau = cand;
+        if (cnt == need)
+            break;
     }
     int gt = 0;
 #pragma unroll
@@ -171,6 +175,8 @@ __device__ __forceinline__ void refine_topk(const uint32_t *sk, const int *si, i
                 cnt += __popcll(__ballot(m * kWave + lane < c && key[m] >= cand));
             if (cnt >= need)
                 tau = cand;
+            if (cnt == need)                            // exactly the selection: done
+                break;
         }
     }
     int gt = 0;
@@ -377,23 +383,75 @@ __device__ __forceinline__ const KT *key_row(const KP &P, const KT *base, const 
 
 // ---------------------------------------------------------------- score_rows (split)
 
-// Selector slice of this lane: Qs[sub*VPL .. +VPL] summed over the row's queries and group c's heads.
+// Selector slice of this lane: Qs[sub*VPL .. +VPL] summed over the row's queries and
+// group c's heads, pair p = (query q_first + p / G, head p % G) added in ascending p.
+// The pairs' slices are loaded kSelBatch at a time as raw words: selector_issue
+// loads the first batch (called before the key loads, so its latency overlaps
+// theirs), selector_finish sums it and loads and sums the rest.
+constexpr int kSelBatch = 8;
+
+template <typename T, int VPL>
+struct SelBuf {
+    static constexpr int W = VPL * (int)sizeof(T) / 4;   // 32-bit words per slice
+    uint32_t w[kSelBatch][W];
+};
+
 template <typename T, int D, int VPL>
-__device__ __forceinline__ void selector_slice(const KP &P, const T *q, const RowGeo &r, int c, int sub,
-                                               float (&qs)[VPL])
+__device__ __forceinline__ void selector_issue(const KP &P, const T *q, const RowGeo &r, int c, int sub,
+                                               SelBuf<T, VPL> &buf, int p0 = 0)
 {
+    constexpr int W = SelBuf<T, VPL>::W;
+    const int np = (int)(r.q_last - r.q_first) * P.G;
+#pragma unroll
+    for (int b = 0; b < kSelBatch; b++) {
+        const int p = p0 + b;
+        if (p < np) {
+            const long long i = r.q_first + p / P.G;
+            const T *qi = q + (i * P.h_q + (long long)c * P.G + p % P.G) * D + sub * VPL;
+            if constexpr (W == 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(qi);
+                buf.w[b][0] = v.x;
+                buf.w[b][1] = v.y;
+            } else {
+                const uint4 v = *reinterpret_cast<const uint4 *>(qi);
+                buf.w[b][0] = v.x;
+                buf.w[b][1] = v.y;
+                buf.w[b][2] = v.z;
+                buf.w[b][3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < W; x++)
+                buf.w[b][x] = 0u;
+        }
+    }
+}
+
+template <typename T, int D, int VPL>
+__device__ __forceinline__ void selector_finish(const KP &P, const T *q, const RowGeo &r, int c, int sub,
+                                                SelBuf<T, VPL> &buf, float (&qs)[VPL])
+{
+    constexpr int W = SelBuf<T, VPL>::W;
+    static_assert(W == 2 || W == 4, "selector slices of 8 or 16 bytes");
 #pragma unroll
     for (int e = 0; e < VPL; e++)
         qs[e] = 0.f;
-    for (long long i = r.q_first; i < r.q_last; i++) {
-        const T *qi = q + (i * P.h_q + (long long)c * P.G) * D + sub * VPL;
-        for (int h = 0; h < P.G; h++) {
+    const int np = (int)(r.q_last - r.q_first) * P.G;
+    for (int p0 = 0; p0 < np; p0 += kSelBatch) {
+        if (p0 > 0)
+            selector_issue<T, D, VPL>(P, q, r, c, sub, buf, p0);
 #pragma unroll
-            for (int e = 0; e < VPL; e++) {
-                if constexpr (sizeof(T) == 2)
-                    qs[e] += bf16_to_f32(qi[h * D + e]);
-                else
-                    qs[e] += qi[h * D + e];
+        for (int b = 0; b < kSelBatch; b++) {
+            if (p0 + b < np) {
+#pragma unroll
+                for (int x = 0; x < W; x++) {
+                    if constexpr (sizeof(T) == 2) {
+                        qs[2 * x] += __uint_as_float(buf.w[b][x] << 16);
+                        qs[2 * x + 1] += __uint_as_float(buf.w[b][x] & 0xffff0000u);
+                    } else {
+                        qs[x] += __uint_as_float(buf.w[b][x]);
+                    }
+                }
             }
         }
     }
@@ -461,8 +519,10 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
                 dst[j] = order_key(sc);
         }
     };
+    SelBuf<T, VPL> sb;
+    selector_issue<T, D, VPL>(P, q, r, c, sub, sb);
     load(ra, 0);
-    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
+    selector_finish<T, D, VPL>(P, q, r, c, sub, sb, qv);
     for (int rd = 0; rd < rounds; rd += 2) {
         if (rd + 1 < rounds)
             load(rb, rd + 1);
@@ -726,6 +786,7 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(KP P, const float *__
 // (order key, position) pairs in the workspace.  select_merge: one wavefront per
 // row selects the row's `need` best among the parts' survivors, which contain it.
 constexpr int kPartCand = 128;
+constexpr int kRowMaxCand = 1024;   // candidates of a row that the part and row plans hold
 
 __host__ __device__ inline int part_cap(int topk) { return topk < kPartCand ? topk : kPartCand; }
 
@@ -751,6 +812,8 @@ __global__ __launch_bounds__(256) void select_part_kernel(KP P, const T *__restr
     const int i0 = part * kPartCand, i1 = min(i0 + kPartCand, r.n_cand);
     if (i0 >= i1)
         return;
+    SelBuf<T, VPL> sb;
+    selector_issue<T, D, VPL>(P, q, r, c, sub, sb);
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -758,7 +821,7 @@ __global__ __launch_bounds__(256) void select_part_kernel(KP P, const T *__restr
         raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, r.j_lo + i))[sub];
     }
     float qv[VPL];
-    selector_slice<T, D, VPL>(P, q, r, c, sub, qv);
+    selector_finish<T, D, VPL>(P, q, r, c, sub, sb, qv);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
@@ -842,6 +905,88 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
     // rank keeps the lower block index on equal scores
     auto emit = [&](int slot, int j) { out[slot] = r.j_lo + sh_pos[wv][j]; };
     wave_select<KPL>(kr, m_tot, r.need, emit, sh_k[wv], sh_i[wv]);
+    for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
+        out[s2] = -1;
+}
+
+// One workgroup of 16 wavefronts per (row, KV head), for batches whose rows x KV
+// heads give every CU a workgroup: the row's candidates are scored into LDS in
+// passes of kRowPass (U rounds of 16 x GPW key rows, all loads of a pass issued
+// before any is reduced), then wavefront 0 selects the row's need best.  Same
+// per-candidate arithmetic as select_part; no workspace and one launch instead of
+// part + merge.  grid: (rows, h_kv).
+constexpr int kRowPass = 512;
+
+template <typename T, typename KT, int D>
+__global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
+                                                          const KT *__restrict__ kbase, int32_t *__restrict__ idx,
+                                                          int32_t *__restrict__ n_idx)
+{
+    using RD = RowDot<KT, D>;
+    constexpr int L = RD::L, VPL = RD::VPL;
+    constexpr int GPW = kWave / L, NG = 16 * GPW;
+    constexpr int U = kRowPass / NG;
+    __shared__ uint32_t sh_key[kRowMaxCand];
+    __shared__ uint32_t sh_k[kFilterCap];
+    __shared__ int sh_i[kFilterCap];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    RowGeo r = row_geo(P, row);
+    int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    if (r.need == r.n_cand || r.need == 0) {
+        if (tid == 0)
+            n_idx[(long long)c * P.rows + row] = r.need;
+        if (r.need == 0)
+            for (int s2 = tid; s2 < P.topk; s2 += blockDim.x)
+                out[s2] = -1;
+        else
+            write_all(P, out, r, tid, blockDim.x);
+        return;
+    }
+    float qv[VPL];
+    SelBuf<T, VPL> sb;
+    selector_issue<T, D, VPL>(P, q, r, c, sub, sb);
+    for (int p0 = 0; p0 < r.n_cand; p0 += kRowPass) {
+        const int i1 = min(p0 + kRowPass, r.n_cand);
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = min(p0 + u * NG + grp, i1 - 1);
+            raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, r.j_lo + i))[sub];
+        }
+        if (p0 == 0)
+            selector_finish<T, D, VPL>(P, q, r, c, sub, sb, qv);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const float sc = group_sum<L>(slice_dot<VPL>(raw[u], qv));
+            const int i = p0 + u * NG + grp;
+            if (sub == 0 && i < i1)
+                sh_key[i] = order_key(sc);
+        }
+    }
+    __syncthreads();
+    if (tid >= kWave)
+        return;
+    if (lane == 0)
+        n_idx[(long long)c * P.rows + row] = r.need;
+    auto emit = [&](int slot, int i) { out[slot] = r.j_lo + i; };
+    if (r.n_cand <= 8 * kWave) {
+        uint32_t kr[8];
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const int i = m * kWave + lane;
+            kr[m] = i < r.n_cand ? sh_key[i] : 0u;
+        }
+        wave_select<8>(kr, r.n_cand, r.need, emit, sh_k, sh_i);
+    } else {
+        uint32_t kr[kRowMaxCand / kWave];
+#pragma unroll
+        for (int m = 0; m < kRowMaxCand / kWave; m++) {
+            const int i = m * kWave + lane;
+            kr[m] = i < r.n_cand ? sh_key[i] : 0u;
+        }
+        wave_select<kRowMaxCand / kWave>(kr, r.n_cand, r.need, emit, sh_k, sh_i);
+    }
     for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
         out[s2] = -1;
 }
@@ -1190,6 +1335,23 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
     uint32_t prefix = 0, pmask = 0;
     int rem = need;
     bool gather = false;
+    // Block-wide counts at one barrier each: wavefront ballots summed by LDS atomics
+    // into one of three rotating counters (the one two rounds ahead is cleared once
+    // every thread has read the last round's).
+    if (tid < 3)
+        sh_cnt3[tid] = 0;
+    __syncthreads();
+    int rnd = 0;
+    auto block_total = [&](int wave_cnt) -> int {        // wave_cnt: uniform across the wavefront
+        if (lane == 0 && wave_cnt)
+            atomicAdd(&sh_cnt3[rnd % 3], wave_cnt);
+        __syncthreads();
+        const int tot = sh_cnt3[rnd % 3];
+        if (tid == 0)
+            sh_cnt3[(rnd + 2) % 3] = 0;
+        rnd++;
+        return tot;
+    };
     if (need <= NT / 2 && n >= 65536) {
         // Long rows (its 32 block-wide counting rounds cost more than a histogram on
         // short ones).  Threshold from the per-thread maxima: at least min(n, NT) >= need threads hold
@@ -1200,11 +1362,14 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         // exponent bins.  More than kCompactCap such keys fall back to the histograms.
         uint32_t mx = 0u;
         for_each_key<NT>(row_keys, r.j_lo, n, [&](int, uint32_t k) { mx = max(mx, k); });
-        uint32_t t0 = 0u;
+        uint32_t t0 = 0u;                                  // a threshold that need maxima reach
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = t0 | (1u << bit);
-            if (block_scan_int<NT>(mx >= cand ? 1 : 0, sh_scan).y >= need)
+            const int cnt = block_total(__popcll(__ballot(mx >= cand)));
+            if (cnt >= need)
                 t0 = cand;
+            if (cnt == need)
+                break;
         }
         if (tid == 0)
             sh_ncand = 0;
@@ -1284,37 +1449,26 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         __syncthreads();
     }
     if (gather) {
-        // exact pick of rem among the gathered keys: tau = rem-th largest key.  Each count
-        // is one barrier: wavefront ballots summed by LDS atomics into one of three
-        // rotating counters (the one two rounds ahead is cleared once every thread has
-        // read the last round's).
+        // exact pick of rem among the gathered keys: tau = rem-th largest key
         const int nc = sh_ncand;
-        if (tid < 3)
-            sh_cnt3[tid] = 0;
-        __syncthreads();
-        int rnd = 0;
         auto block_count = [&](auto pred) -> int {
             int cnt = 0;
             for (int base = 0; base < nc; base += NT) {
                 const int x = base + tid;
                 cnt += __popcll(__ballot(x < nc && pred(x)));
             }
-            if (lane == 0 && cnt)
-                atomicAdd(&sh_cnt3[rnd % 3], cnt);
-            __syncthreads();
-            const int tot = sh_cnt3[rnd % 3];
-            if (tid == 0)
-                sh_cnt3[(rnd + 2) % 3] = 0;
-            rnd++;
-            return tot;
+            return block_total(cnt);
         };
         uint32_t tau = prefix;
         for (int bit = 31; bit >= 0; --bit) {
             if (pmask & (1u << bit))
                 continue;                                    // fixed by the prefix
             const uint32_t cand = tau | (1u << bit);
-            if (block_count([&](int x) { return cand_key[x] >= cand; }) >= rem)
+            const int cnt = block_count([&](int x) { return cand_key[x] >= cand; });
+            if (cnt >= rem)
                 tau = cand;
+            if (cnt == rem)                                  // exactly the selection: done
+                break;
         }
         const int n_gt = block_count([&](int x) { return cand_key[x] > tau; });
         const int need_eq = rem - n_gt;
@@ -1407,17 +1561,18 @@ __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 // ---------------------------------------------------------------- dispatch
 
 static constexpr int kWaveTopkMax = 2048;
-static constexpr int kRowMaxCand = 1024;
 static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (8 rounds of 64)
 
 // Candidate capacity of a row, and the row stride of the score-key workspace (a
 // multiple of 4, so every row starts 16-byte aligned).
+static constexpr long long kRowFusedMin = 256;          // rows x KV heads for the fused row plan
+
 static long long cand_cap(const KP &P) { return P.g == 1 ? P.max_k : P.nb_max; }
 static long long key_stride(const KP &P) { return (cand_cap(P) + 3) / 4 * 4; }
 
 size_t select_workspace_bytes(const KP &P, int plan)
 {
-    if (plan == kSelectEmpty)
+    if (plan == kSelectEmpty || plan == kSelectRowFused)
         return 0;
     if (plan == kSelectHeads) {                           // order keys, and every head's logits for SOFTMAX
         const size_t per = (size_t)P.h_kv * (size_t)P.rows * (size_t)key_stride(P) * sizeof(uint32_t);
@@ -1439,10 +1594,12 @@ int select_plan(const KP &P)
         return kSelectHeads;
     bool few_rows = P.shared || P.max_q <= 8;
     long long max_cand = P.g == 1 ? P.max_k : P.nb_max;
-    int plan = !few_rows ? kSelectTile : (max_cand <= kRowMaxCand ? kSelectRow : kSelectSplit);
+    // one workgroup per (row, KV head) once that gives every CU one; parts + merge below
+    const int row_plan = P.rows * P.h_kv >= kRowFusedMin ? kSelectRowFused : kSelectRow;
+    int plan = !few_rows ? kSelectTile : (max_cand <= kRowMaxCand ? row_plan : kSelectSplit);
     if (const char *e = getenv("SPARSE_ATTN_SELECT_PLAN")) {       // tuning override
         int v = atoi(e);
-        if (few_rows && (v == kSelectSplit || (v == kSelectRow && max_cand <= kRowMaxCand)))
+        if (few_rows && (v == kSelectSplit || ((v == kSelectRow || v == kSelectRowFused) && max_cand <= kRowMaxCand)))
             plan = v;
     }
     return plan;
@@ -1459,6 +1616,14 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     if (plan == kSelectEmpty) {
         long long n = P.rows * P.h_kv;
         select_empty_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(P, n_idx);
+        return hipGetLastError();
+    }
+    if (plan == kSelectRowFused) {
+        dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
+        if (P.g == 1)
+            select_row_kernel<T, T, D><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
+        else
+            select_row_kernel<T, float, D><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
         return hipGetLastError();
     }
     if (plan == kSelectRow) {

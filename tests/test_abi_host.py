@@ -136,6 +136,12 @@ def test_workspace_sizes():
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
     sel, fwd = _ws(p)
     assert sel == 2 * 4096 * 64 * 4
+    # long prefill rows (> 2048 candidates): the scores plus each row's maxima of every
+    # 32 candidates (row stride rounded up to a multiple of 4)
+    p = params(batch=1, max_q=512, total_q=512, max_k=65536, total_k=65536, block=4)
+    assert _ws(p)[0] == 2 * 512 * (16384 + 512) * 4
+    p = params(batch=1, max_q=512, total_q=512, max_k=65536 + 4 * 33, total_k=65536 + 4 * 33, block=4)
+    assert _ws(p)[0] == 2 * 512 * (16384 + 36 + 516) * 4
     # token-level shared selection with long rows: scores in the workspace
     p = params(block=1, shared_selection=1, max_q=6, total_q=12, max_k=20000, total_k=40000, topk=3000)
     sel, _ = _ws(p)

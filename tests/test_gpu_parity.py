@@ -153,17 +153,29 @@ def _integer_inputs(w, lo=-2, hi=2, seed=0):
     return x
 
 
-@pytest.mark.parametrize("case", ["wave", "compact", "tile"])
+@pytest.mark.parametrize("case", ["wave", "compact", "tile", "tile_long"])
 def test_topk_exact_ties(case):
     from workloads import draft_decode
     if case == "compact":      # token-level shared rows with > 2048 candidates
         w = draft_decode(batch=3, median=5000, lo=4500, hi=9000, seed=11)
     elif case == "wave":       # decode rows, <= 2048 candidates
         w = small("bf16_decode_32k")
-    else:                      # prefill rows (MFMA fp32 scores) with 4097 candidates, mean pooling
+    elif case == "tile":       # prefill rows (MFMA fp32 scores) with 4097 candidates, mean pooling
         w = small("bf16_chunked_prefill_1m").scaled(pool=POOL_MEAN)
+    else:                      # rows long enough for the top-k to start from the group maxima
+        w = small("bf16_chunked_prefill_1m").scaled(pool=POOL_MEAN, seqlens_k=[65536 + 3], seqlens_q=[64])
     x = _integer_inputs(w)
     parity.full_check(w, x, parity.to_device(x))
+
+
+@pytest.mark.parametrize("n_k,n_q,k", [(65536 + 3, 96, 64), (270000 + 1, 40, 512), (131072 + 17, 33, 200)])
+def test_long_rows_group_maxima(n_k, n_q, k):
+    """Prefill rows of >= 4k groups of 32 candidates: the top-k reads only the groups whose
+    score maximum (kept by the scoring kernel) reaches the k-th largest group maximum."""
+    w = small("bf16_chunked_prefill_1m").scaled(seqlens_k=[n_k], seqlens_q=[n_q], topk=k)
+    assert (n_k - n_q - w.window) // w.block - 1 >= 4 * 32 * k        # every row takes that path
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
 
 
 def test_topk_all_scores_equal():

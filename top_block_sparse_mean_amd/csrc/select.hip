@@ -81,6 +81,38 @@ __device__ __forceinline__ void write_all(const KP &P, int32_t *out, const RowGe
 
 // ---------------------------------------------------------------- top-k cores
 
+// One wavefront, given tau = the need-th largest of n keys (or any threshold with
+// exactly need keys at or above it; key i at lane i % 64, slot i / 64): emit(slot, i)
+// for every key above tau and the lowest-index keys equal to it, need in all, slots
+// 0 .. need-1 in ascending i.
+template <int KPL, typename Emit>
+__device__ __forceinline__ void emit_above(const uint32_t (&key)[KPL], int n, int need, uint32_t tau, Emit emit)
+{
+    const int lane = lane_id();
+    int gt = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++)
+        gt += __popcll(__ballot(m * kWave + lane < n && key[m] > tau));
+    const int need_eq = need - gt;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int i = m * kWave + lane;
+        const bool valid = i < n;
+        const bool is_gt = valid && key[m] > tau;
+        const bool is_eq = valid && key[m] == tau;
+        const unsigned long long meq = __ballot(is_eq);
+        const int rank = eq_seen + lanes_below(meq);
+        eq_seen += __popcll(meq);
+        const bool s = is_gt || (is_eq && rank < need_eq);
+        const unsigned long long ms = __ballot(s);
+        const int slot = base + lanes_below(ms);
+        if (s && slot < need)
+            emit(slot, i);
+        base += __popcll(ms);
+    }
+}
+
 // One wavefront: the `need` largest of n keys (key i at lane i % 64, slot i / 64);
 // emit(slot, i) is called for each selected key, slots 0 .. need-1 in ascending i.
 template <int KPL, typename Emit>
@@ -102,28 +134,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
         if (cnt == need)
             break;
     }
-    int gt = 0;
-#pragma unroll
-    for (int m = 0; m < KPL; m++)
-        gt += __popcll(__ballot(m * kWave + lane < n && key[m] > tau));
-    int need_eq = need - gt;
-    int base = 0, eq_seen = 0;
-#pragma unroll
-    for (int m = 0; m < KPL; m++) {
-        int i = m * kWave + lane;
-        bool valid = i < n;
-        bool is_gt = valid && key[m] > tau;
-        bool is_eq = valid && key[m] == tau;
-        unsigned long long meq = __ballot(is_eq);
-        int rank = eq_seen + lanes_below(meq);
-        eq_seen += __popcll(meq);
-        bool s = is_gt || (is_eq && rank < need_eq);
-        unsigned long long ms = __ballot(s);
-        const int slot = base + lanes_below(ms);
-        if (s && slot < need)
-            emit(slot, i);
-        base += __popcll(ms);
-    }
+    emit_above<KPL>(key, n, need, tau, emit);
 }
 
 // Writes the selected block indices j_base + i to out[slot].
@@ -909,6 +920,63 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
         out[s2] = -1;
 }
 
+// The need-th largest of n keys (n >= need >= 1), found by the 16 wavefronts of a
+// 1024-thread workgroup that each hold all n keys in registers (key i at lane i % 64,
+// slot i / 64).  The bits above `shift + 4` are fixed by tau (every key >= tau, and
+// at least need of them); the rest are found 4 bits per round: wavefront w counts the
+// keys >= tau | w << shift, the counts meet in LDS (two buffers: one barrier per
+// round) and every wavefront takes the largest digit whose count still reaches
+// need.  A count of exactly need ends the search early: the keys at or above the
+// returned value are then exactly the need largest.
+template <int KPL>
+__device__ __forceinline__ uint32_t block_threshold16(const uint32_t (&kr)[KPL], int n, int need, uint32_t tau,
+                                                      int shift, int (*sh_cnt)[16])
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    for (int rd = 0; shift >= 0; rd++, shift -= 4) {
+        const uint32_t cand = tau | ((uint32_t)w << shift);
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; m++)
+            cnt += __popcll(__ballot(m * kWave + lane < n && kr[m] >= cand));
+        if (lane == 0)
+            sh_cnt[rd & 1][w] = cnt;
+        __syncthreads();
+        const int cl = sh_cnt[rd & 1][lane & 15];
+        // digit 0 keeps tau itself, which always has >= need keys at or above it
+        const unsigned long long ok = __ballot(lane < 16 && cl >= need);
+        const int d = 63 - __clzll(ok);
+        tau |= (uint32_t)d << shift;
+        if (__builtin_amdgcn_readlane(cl, d) == need)
+            break;
+    }
+    return tau;
+}
+
+// Selection among a row's n <= 64 * KPL keys in LDS by the 16 wavefronts of a
+// workgroup: the threshold by block_threshold16, then wavefront 0 emits the
+// selection in ascending index (keys above it, then the lowest-index keys equal to it).
+template <int KPL>
+__device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, int (*sh_cnt)[16], const RowGeo &r,
+                                           int32_t *out, int32_t *n_idx_row)
+{
+    const int lane = lane_id(), n = r.n_cand, need = r.need;
+    uint32_t kr[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int i = m * kWave + lane;
+        kr[m] = i < n ? sh_key[i] : 0u;
+    }
+    const uint32_t tau = block_threshold16<KPL>(kr, n, need, 0u, 28, sh_cnt);
+    if (threadIdx.x >= kWave)
+        return;
+    if (lane == 0)
+        *n_idx_row = need;
+    emit_above<KPL>(kr, n, need, tau, [&](int slot, int i) { out[slot] = r.j_lo + i; });
+    for (int s2 = need + lane; s2 < P.topk; s2 += kWave)
+        out[s2] = -1;
+}
+
 // One workgroup of 16 wavefronts per (row, KV head), for batches whose rows x KV
 // heads give every CU a workgroup: the row's candidates are scored into LDS in
 // passes of kRowPass (U rounds of 16 x GPW key rows, all loads of a pass issued
@@ -927,8 +995,7 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     constexpr int GPW = kWave / L, NG = 16 * GPW;
     constexpr int U = kRowPass / NG;
     __shared__ uint32_t sh_key[kRowMaxCand];
-    __shared__ uint32_t sh_k[kFilterCap];
-    __shared__ int sh_i[kFilterCap];
+    __shared__ int sh_cnt[2][16];
     const long long row = blockIdx.x;
     const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
     RowGeo r = row_geo(P, row);
@@ -965,30 +1032,10 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
         }
     }
     __syncthreads();
-    if (tid >= kWave)
-        return;
-    if (lane == 0)
-        n_idx[(long long)c * P.rows + row] = r.need;
-    auto emit = [&](int slot, int i) { out[slot] = r.j_lo + i; };
-    if (r.n_cand <= 8 * kWave) {
-        uint32_t kr[8];
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const int i = m * kWave + lane;
-            kr[m] = i < r.n_cand ? sh_key[i] : 0u;
-        }
-        wave_select<8>(kr, r.n_cand, r.need, emit, sh_k, sh_i);
-    } else {
-        uint32_t kr[kRowMaxCand / kWave];
-#pragma unroll
-        for (int m = 0; m < kRowMaxCand / kWave; m++) {
-            const int i = m * kWave + lane;
-            kr[m] = i < r.n_cand ? sh_key[i] : 0u;
-        }
-        wave_select<kRowMaxCand / kWave>(kr, r.n_cand, r.need, emit, sh_k, sh_i);
-    }
-    for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
-        out[s2] = -1;
+    if (r.n_cand <= 8 * kWave)
+        row_select<8>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row);
+    else
+        row_select<kRowMaxCand / kWave>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row);
 }
 
 // ---------------------------------------------------------------- score_tile (MFMA fp32)
@@ -1061,11 +1108,43 @@ __device__ __forceinline__ void key_write(const KeyStage<N> &st, unsigned char *
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Maxima of 8 values over each 16-lane row, transposed: v[t] (t = 0..7) of all 16
+// lanes reduce to lane l holding the maximum of v[l & 7].  Each exchange step halves
+// the values a lane holds: the lane keeps the half its lane bit selects and sends
+// the other half to a partner whose bit differs (xor 1, xor 2 by quad permutes;
+// rotations by 4 and 8 lanes flip bits 2 and 3).
+__device__ __forceinline__ uint32_t row16_max8(const uint32_t (&v)[8], int li)
+{
+    uint32_t a[4], b[2];
+    const bool b0 = li & 1, b1 = li & 2, b2 = li & 4;
+#pragma unroll
+    for (int p = 0; p < 4; p++)
+        a[p] = max(b0 ? v[2 * p + 1] : v[2 * p], dpp_u32<0xB1>(b0 ? v[2 * p] : v[2 * p + 1]));
+#pragma unroll
+    for (int p = 0; p < 2; p++)          // a[p] holds t = 2p + bit0
+        b[p] = max(b1 ? a[2 * p + 1] : a[2 * p], dpp_u32<0x4E>(b1 ? a[2 * p] : a[2 * p + 1]));
+    uint32_t c = max(b2 ? b[1] : b[0], dpp_u32<0x124>(b2 ? b[0] : b[1]));   // t = 4 bit2 + 2 bit1 + bit0
+    return max(c, dpp_u32<0x128>(c));
+}
+
+// With gmax: also the largest order key of every group of kGroupCols consecutive
+// candidates (group x = candidates first_cand + 32x ..; 0 where a row has none),
+// gmax[(c * rows + row) * gstride + x], so a top-k over long rows can skip the groups
+// that cannot hold a selected key.  Each wavefront's 32 columns of a tile are one group.
+constexpr int kGroupCols = 32;
+
 template <typename T, typename KT, int D>
 __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__restrict__ q,
                                                             const KT *__restrict__ kbase,
                                                             uint32_t *__restrict__ ws, long long stride,
-                                                            int col_tiles)
+                                                            int col_tiles, uint32_t *__restrict__ gmax,
+                                                            long long gstride)
 {
     constexpr int KG = D / 16;
     constexpr int kRowBytes = D * (int)sizeof(KT);       // one candidate key row
@@ -1081,7 +1160,8 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
     int jlo_last, jhi_last;
     row_cands(P, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
     jhi_last = min(jhi_last, (int)stride);
-    const int jc0 = jlo_last + blockIdx.x * col_tiles * 64;
+    const int jc_base = jlo_last;                         // = first_cand for a row with candidates
+    const int jc0 = jc_base + blockIdx.x * col_tiles * 64;
     if (jc0 >= jhi_last)
         return;
     const int jc1 = min(jc0 + col_tiles * 64, jhi_last);
@@ -1162,19 +1242,30 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
                         acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a][st], bv[bb][st], acc[a][bb], 0, 0, 0);
         }
         // row = r0 + wr + 16a + 4lk + i, candidate = jt + wc + 16bb + li
+        uint32_t mx[8];
 #pragma unroll
         for (int a = 0; a < 2; a++) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int rl = r0 + wr + 16 * a + 4 * lk + i;
                 uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride;
+                mx[4 * a + i] = 0u;
 #pragma unroll
                 for (int bb = 0; bb < 2; bb++) {
                     const int j = jt + wc + 16 * bb + li;
-                    if (j >= j_first && j < jh_row[a][i])
-                        dst[j] = order_key(acc[a][bb][i]);
+                    const uint32_t key = order_key(acc[a][bb][i]);
+                    const bool ok = j >= j_first && j < jh_row[a][i];
+                    if (ok)
+                        dst[j] = key;
+                    mx[4 * a + i] = max(mx[4 * a + i], ok ? key : 0u);
                 }
             }
+        }
+        if (gmax && jt + wc < jc1) {                         // groups past the chunk hold no candidate
+            const uint32_t m = row16_max8(mx, li);           // row t = li & 7: a = t / 4, i = t % 4
+            const int t = li & 7, rl = r0 + wr + 16 * (t >> 2) + 4 * lk + (t & 3);
+            if (li < 8 && rl < r_end)
+                gmax[((long long)c * P.rows + s.q_off + rl) * gstride + (unsigned)(jt + wc - jc_base) / kGroupCols] = m;
         }
     };
     const int n_t = (jc1 - jc0 + 63) / 64;
@@ -1255,7 +1346,7 @@ __device__ __forceinline__ int2 block_scan_int(int v, int *sh)
 }
 
 constexpr int kCompactMaxN = 262144;     // candidates per row (bitmap of 8192 words in LDS)
-constexpr int kCompactCap = 4096;        // keys kept for the exact last step
+constexpr int kCompactCap = 4032;        // keys kept for the exact last step (LDS of two workgroups per CU)
 
 // Calls f(i, key) for every key i in [0, n) of a row whose keys start at element
 // j_lo of a 16-byte aligned row base: 16-byte loads, eight per thread in flight.
@@ -1298,9 +1389,13 @@ __device__ __forceinline__ void for_each_key(const uint32_t *row, int j_lo, int 
 //  3. the remaining picks are made exactly inside LDS (binary search on the key, then
 //     on the index for equal keys: ties go to the lower index);
 //  4. the bitmap is compacted into ascending indices.
-// The keys are read from the workspace two to four times in all.
+// The keys are read from the workspace two to four times in all.  With the group
+// maxima of the scoring (gmax, rows of >= 4k groups of 32 keys), step 0 instead
+// takes t0 = a value that k group maxima reach and reads only the groups whose
+// maximum reaches it (about k of them, k x 128 bytes instead of the whole row).
 __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
-                                                            int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
+                                                            int32_t *__restrict__ idx, int32_t *__restrict__ n_idx,
+                                                            const uint32_t *__restrict__ gmax, long long gstride)
 {
     constexpr int NT = 1024, NW = NT / kWave;
     __shared__ int hist[4096];
@@ -1310,6 +1405,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
     __shared__ int sh_scan[NW];
     __shared__ int sh_digit, sh_above, sh_ncand;
     __shared__ int sh_cnt3[3];
+    __shared__ int sh_cnt16[2][16];
     const long long row = blockIdx.x;
     const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id();
     RowGeo r = row_geo(P, row);
@@ -1352,7 +1448,83 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         rnd++;
         return tot;
     };
-    if (need <= NT / 2 && n >= 65536) {
+    const int ng = (n + kGroupCols - 1) / kGroupCols;
+    if (gmax && need <= NT / 2 && ng >= 4 * need) {
+        // Thread tid owns the gpt consecutive groups from gpt * tid, so at least
+        // min(ng, 513) >= need threads own one.  t0 = the need-th largest of the threads'
+        // maxima over their groups: need keys reach it, so the need-th largest key does
+        // and every selected key is >= t0.  Only the groups whose maximum reaches t0
+        // are read.  ng <= 8192.
+        const uint32_t *gm_row = gmax + ((long long)c * P.rows + row) * gstride;
+        const int gpt = (ng + NT - 1) / NT;
+        uint32_t gm[kCompactMaxN / kGroupCols / NT];
+        uint32_t tm = 0u;
+#pragma unroll
+        for (int m = 0; m < kCompactMaxN / kGroupCols / NT; m++) {
+            const int x = gpt * tid + m;
+            gm[m] = m < gpt && x < ng ? gm_row[x] : 0u;
+            tm = max(tm, gm[m]);
+        }
+        hist[tid] = (int)tm;
+        __syncthreads();
+        uint32_t kr[NT / kWave];
+#pragma unroll
+        for (int m = 0; m < NT / kWave; m++)
+            kr[m] = (uint32_t)hist[m * kWave + lane];
+        const uint32_t t0 = block_threshold16<NT / kWave>(kr, NT, need, 0u, 28, sh_cnt16);
+        // the groups reaching t0, listed in ascending order (in hist)
+        int f = 0;
+#pragma unroll
+        for (int m = 0; m < kCompactMaxN / kGroupCols / NT; m++)
+            f += m < gpt && gpt * tid + m < ng && gm[m] >= t0 ? 1 : 0;
+        const int2 sc = block_scan_int<NT>(f, sh_scan);       // its barriers also retire the reads of hist
+        const int n_grp = sc.y;
+        if (n_grp <= 4096) {
+            int o = sc.x;
+#pragma unroll
+            for (int m = 0; m < kCompactMaxN / kGroupCols / NT; m++)
+                if (m < gpt && gpt * tid + m < ng && gm[m] >= t0)
+                    hist[o++] = gpt * tid + m;
+        }
+        if (tid == 0)
+            sh_ncand = 0;
+        __syncthreads();
+        if (n_grp <= 4096) {
+            // their keys >= t0 into cand_key / cand_idx (one LDS atomic per wavefront and round)
+            const uint32_t *keys = row_keys + r.j_lo;
+            const int tot = n_grp * kGroupCols;
+            constexpr int U = 16;
+            for (int e0 = 0; e0 < tot; e0 += NT * U) {
+                uint32_t kv[U];
+                int iv[U];
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const int e = e0 + u * NT + tid;
+                    iv[u] = e < tot ? hist[e / kGroupCols] * kGroupCols + e % kGroupCols : n;
+                    kv[u] = iv[u] < n ? keys[iv[u]] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const bool take = iv[u] < n && kv[u] >= t0;
+                    const unsigned long long mk = __ballot(take);
+                    if (mk) {
+                        int base = 0;
+                        if (lane == 0)
+                            base = atomicAdd(&sh_ncand, __popcll(mk));
+                        base = __builtin_amdgcn_readfirstlane(base);
+                        const int slot = base + lanes_below(mk);
+                        if (take && slot < kCompactCap) {
+                            cand_key[slot] = kv[u];
+                            cand_idx[slot] = iv[u];
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        gather = n_grp <= 4096 && sh_ncand <= kCompactCap;
+        __syncthreads();
+    } else if (need <= NT / 2 && n >= 65536) {
         // Long rows (its 32 block-wide counting rounds cost more than a histogram on
         // short ones).  Threshold from the per-thread maxima: at least min(n, NT) >= need threads hold
         // keys, so at least `need` keys are >= t0 = the need-th largest thread maximum
@@ -1460,21 +1632,44 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
             return block_total(cnt);
         };
         uint32_t tau = prefix;
-        for (int bit = 31; bit >= 0; --bit) {
-            if (pmask & (1u << bit))
-                continue;                                    // fixed by the prefix
-            const uint32_t cand = tau | (1u << bit);
-            const int cnt = block_count([&](int x) { return cand_key[x] >= cand; });
-            if (cnt >= rem)
-                tau = cand;
-            if (cnt == rem)                                  // exactly the selection: done
-                break;
+        int n_gt, n_eq;
+        const int free_bits = 32 - __popc(pmask);              // the prefix fixes the top bits
+        if (nc <= NT && free_bits % 4 == 0) {
+            // every wavefront holds all gathered keys: 4 bits per round, then the counts
+            // above and at tau without a barrier
+            uint32_t kr[NT / kWave];
+#pragma unroll
+            for (int m = 0; m < NT / kWave; m++) {
+                const int x = m * kWave + lane;
+                kr[m] = x < nc ? cand_key[x] : 0u;
+            }
+            if (free_bits > 0)
+                tau = block_threshold16<NT / kWave>(kr, nc, rem, prefix, free_bits - 4, sh_cnt16);
+            n_gt = 0;
+            n_eq = 0;
+#pragma unroll
+            for (int m = 0; m < NT / kWave; m++) {
+                const bool valid = m * kWave + lane < nc;
+                n_gt += __popcll(__ballot(valid && kr[m] > tau));
+                n_eq += __popcll(__ballot(valid && kr[m] == tau));
+            }
+        } else {
+            for (int bit = 31; bit >= 0; --bit) {
+                if (pmask & (1u << bit))
+                    continue;                                    // fixed by the prefix
+                const uint32_t cand = tau | (1u << bit);
+                const int cnt = block_count([&](int x) { return cand_key[x] >= cand; });
+                if (cnt >= rem)
+                    tau = cand;
+                if (cnt == rem)                                  // exactly the selection: done
+                    break;
+            }
+            n_gt = block_count([&](int x) { return cand_key[x] > tau; });
+            n_eq = block_count([&](int x) { return cand_key[x] == tau; });
         }
-        const int n_gt = block_count([&](int x) { return cand_key[x] > tau; });
         const int need_eq = rem - n_gt;
         // among keys == tau: the need_eq lowest indices (binary search on the index, skipped
         // when every equal key is taken -- the usual case of one)
-        const int n_eq = block_count([&](int x) { return cand_key[x] == tau; });
         int ilim = 1 << 30;
         if (n_eq > need_eq) {
             int lo = 0;                                      // largest bound with count(idx < bound) <= need_eq
@@ -1570,6 +1765,16 @@ static constexpr long long kRowFusedMin = 256;          // rows x KV heads for t
 static long long cand_cap(const KP &P) { return P.g == 1 ? P.max_k : P.nb_max; }
 static long long key_stride(const KP &P) { return (cand_cap(P) + 3) / 4 * 4; }
 
+// Group maxima of the scores (tile scoring followed by the compacting top-k): their
+// row stride, or 0 when not kept.
+static long long gmax_stride(const KP &P, int plan)
+{
+    const long long stride = key_stride(P);
+    if (plan != kSelectTile || stride <= kWaveTopkMax || stride > kCompactMaxN || getenv("SPARSE_ATTN_TOPK_RADIX"))
+        return 0;
+    return ((stride + kGroupCols - 1) / kGroupCols + 3) / 4 * 4;
+}
+
 size_t select_workspace_bytes(const KP &P, int plan)
 {
     if (plan == kSelectEmpty || plan == kSelectRowFused)
@@ -1583,7 +1788,7 @@ size_t select_workspace_bytes(const KP &P, int plan)
         const long long n_part = (stride + kPartCand - 1) / kPartCand;
         return (size_t)P.h_kv * (size_t)P.rows * (size_t)n_part * (size_t)part_cap(P.topk) * 2 * sizeof(uint32_t);
     }
-    return (size_t)P.h_kv * (size_t)P.rows * (size_t)stride * sizeof(uint32_t);
+    return (size_t)P.h_kv * (size_t)P.rows * (size_t)(stride + gmax_stride(P, plan)) * sizeof(uint32_t);
 }
 
 int select_plan(const KP &P)
@@ -1613,6 +1818,8 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     int plan = select_plan(P);
     const long long stride = plan == kSelectRow ? cand_cap(P) : key_stride(P);
     uint32_t *wsk = (uint32_t *)ws;
+    const long long gms = gmax_stride(P, plan);
+    uint32_t *gm = gms ? wsk + (size_t)P.h_kv * (size_t)P.rows * (size_t)stride : nullptr;
     if (plan == kSelectEmpty) {
         long long n = P.rows * P.h_kv;
         select_empty_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(P, n_idx);
@@ -1702,9 +1909,11 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         dim3 grid((unsigned)((stride + col_tiles * 64 - 1) / (col_tiles * 64)), (unsigned)((P.max_q + 63) / 64),
                   (unsigned)(P.h_kv * P.batch));
         if (P.g == 1)
-            score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, col_tiles);
+            score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, col_tiles, gm,
+                                                                   gms);
         else
-            score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride, col_tiles);
+            score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride, col_tiles, gm,
+                                                                       gms);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -1720,7 +1929,7 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         topk_wave_kernel<32><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
     else if (stride <= kCompactMaxN && !getenv("SPARSE_ATTN_TOPK_RADIX"))
         topk_compact_kernel<<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
-                                                                                           n_idx);
+                                                                                           n_idx, gm, gms);
     else
         topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
             P, wsk, stride, idx, n_idx);

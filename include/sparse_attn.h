@@ -204,8 +204,10 @@ sa_status sparse_attn_compress_tail(const sa_params *p, int32_t n_tail_blocks, c
  *   k_cmp         pooled keys as from sparse_attn_compress; the blocks holding a
  *                 new token are recomputed from the cache, or NULL to skip
  *                 pooling (always skipped when block == 1)
- * Two kernels on `stream`: the row scatter, then the pooling of the touched
- * blocks (which reads the rows the first wrote). */
+ * One kernel on `stream`: with pooling, one workgroup per (sequence, KV head,
+ * touched block) writes the new rows of that block and pools its window, taking
+ * the new tokens from k_new and the others from the cache; without, a row
+ * scatter. */
 sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
                                 float *k_cmp, void *stream);
 

@@ -119,6 +119,20 @@ def test_bucket_index_and_retrieval(shape):
     assert np.abs(lse.cpu().t().reshape(-1).double().numpy() - att["lse"]).max() < parity.lse_tol(w)
 
 
+@pytest.mark.parametrize("plan", ["1", "5"])
+def test_bucket_decode_rows_both_plans(plan, monkeypatch):
+    """One query per sequence: the centroid scores of a row are ranked by the part + merge
+    plan ("1") and by the one-workgroup-per-row plan ("5") alike."""
+    monkeypatch.setenv("SPARSE_ATTN_SELECT_PLAN", plan)
+    w = SHAPES["multi_head"]()
+    w = w.scaled(topk=_width(w))
+    x, xg = parity.gen_pair(w)
+    p, gx, idx, n_idx, out, lse = _run(w, x, xg)
+    ox = oracle.bucket_build(w, oracle.compress(w, x["k"]))
+    diff = _check_build(w, gx, ox)
+    assert _check_select(w, x, ox, idx, n_idx, diff) >= (w.rows * w.h_kv) // 2
+
+
 def test_full_chunked_prefill_1m_buckets_sampled():
     """The 1M chunk with the LSA bucket index: 2048 cluster blocks clustered, 256 buckets
     (about 2048 keys) per query; sampled rows and requests against the oracle."""

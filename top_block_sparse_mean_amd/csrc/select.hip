@@ -1293,17 +1293,17 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     const int c = blockIdx.y, lane = lane_id();
     if (row >= P.rows)
         return;
-    // the candidate range of any row with candidates starts at n_init / g: load first, then
-    // resolve the row's geometry while the loads are in flight
-    const int j_first = first_cand(P);
+    // only the row's own candidates are read (a causal row of a prefill holds fewer than
+    // the stride: on average half of it)
+    RowGeo r = row_geo(P, row);
     const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
+    const bool pick = r.need != r.n_cand;
     uint32_t kr[KPL];
 #pragma unroll
     for (int m = 0; m < KPL; m++) {
-        long long j = j_first + m * kWave + lane;
-        kr[m] = j < stride ? src[j] : 0u;
+        const int i = m * kWave + lane;
+        kr[m] = pick && i < r.n_cand ? src[r.j_lo + i] : 0u;
     }
-    RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     if (lane == 0)
         n_idx[(long long)c * P.rows + row] = r.need;

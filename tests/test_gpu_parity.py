@@ -178,6 +178,17 @@ def test_long_rows_group_maxima(n_k, n_q, k):
     parity.full_check(w, x, xg)
 
 
+def test_long_rows_per_thread_maxima():
+    """Rows of >= 65536 candidates scored per head (the max-over-heads group score, no
+    group maxima): the top-k gathers the keys above the k-th largest per-thread maximum."""
+    from workloads import SELECT_MAX
+    w = small("bf16_chunked_prefill_1m").scaled(seqlens_k=[270000 + 1], seqlens_q=[24], topk=512,
+                                                select_mode=SELECT_MAX)
+    assert (w.seqlens_k[0] - 24 - w.window) // w.block - 1 >= 65536
+    x, xg = parity.gen_pair(w)
+    parity.full_check(w, x, xg)
+
+
 def test_topk_all_scores_equal():
     """Every candidate scores the same: the k lowest indices (all-equal keys overflow the
     compaction buffer of the large-row top-k)."""

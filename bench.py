@@ -117,6 +117,9 @@ class Step:
             self.w = w
         self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
+        # the scoring kernel is timed live only where it dominates the step (each event
+        # record costs ~1.5 us of a decode step)
+        self.time_select = w.name in SELECT_DOMINANT and not buckets
         self.index = sa.BucketIndex(self.p, w.bucket_block, w.bucket_count, w.bucket_cap) if buckets else None
         sel_b, fwd_b = sa.workspace_size(self.p)
         self.ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
@@ -151,8 +154,9 @@ class Step:
                 sa.compress(self.p, x["k"], self.k_cmp)   # the cache's pooled keys, built before decoding
 
     def __call__(self, events=None, stages=None):
-        """stages: (TimingEvents, four events) recorded before compress, after compress,
-        after select and after fwd."""
+        """events: four events, recorded around the selection's scoring kernel ([0], [1])
+        and the main attention kernel ([2], [3]).  stages: (TimingEvents, four events)
+        recorded before compress, after compress, after select and after fwd."""
         x = self.x
         mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
         mark(0)
@@ -166,10 +170,11 @@ class Step:
         if self.index is not None:
             sa.bucket_select(self.p, x["q"], self.index, self.w.bucket_topk, self.idx, self.n_idx, ws=self.ws_bkt)
         else:
-            sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
+            sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel,
+                      events=events[0:2] if events is not None and self.time_select else None)
         mark(2)
         sa.fwd(self.p, x["q"], x["k"], x["v"], self.idx, self.n_idx, out=self.out, ws=self.ws_fwd,
-               events=events)
+               events=None if events is None else events[2:4])
         mark(3)
 
 
@@ -275,21 +280,34 @@ def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks, buckets=False):
         add("append", stage_ms[0], None, "launch")
     elif g > 1:
         add("compress", stage_ms[0], w.total_k * w.h_kv * d * elt + w.h_kv * sum(nb) * d * 4, "hbm")
+    amount, bound = select_work(w, buckets)
+    add("select", stage_ms[1], amount, bound)
     if decode:
-        sel_bytes = (w.h_kv * sum(nb) * d * 4) if g > 1 else (w.h_kv * w.total_k * d * elt)
-        add("select", stage_ms[1], sel_bytes + w.total_q * w.h_q * d * elt, "hbm")
         add("fwd", stage_ms[2], attn_bytes, "hbm")
     else:
-        cand = 0
-        for nk, nq in zip(w.seqlens_k, w.seqlens_q):
-            p = range(nk - nq, nk)
-            if buckets:        # the centroids of the complete cluster blocks before each row
-                cand += sum((q + 1) // w.bucket_block * w.bucket_count for q in p)
-            else:
-                cand += sum(q // g + 1 for q in p)
-        add("select", stage_ms[1], 2.0 * d * w.h_kv * cand, "mfma_fp32")
         add("fwd", stage_ms[2], attn_flops, "mfma_bf16" if w.dtype == DTYPE_BF16 else "alu_fp32")
     return rep
+
+
+def select_work(w, buckets=False):
+    """Algorithmic work of the selection's scoring: decode rows read the pooled keys (or,
+    with g = 1, the raw keys) once per step, plus the selector queries (bytes, HBM);
+    prefill rows score every causally visible block of every row per KV head (2 d flop
+    each, fp32 MFMA)."""
+    d, g = w.head_dim, w.block
+    elt = 2 if w.dtype == DTYPE_BF16 else 4
+    if w.name in DECODE:
+        nb = [-(-nk // g) for nk in w.seqlens_k]
+        sel_bytes = (w.h_kv * sum(nb) * d * 4) if g > 1 else (w.h_kv * w.total_k * d * elt)
+        return sel_bytes + w.total_q * w.h_q * d * elt, "hbm"
+    cand = 0
+    for nk, nq in zip(w.seqlens_k, w.seqlens_q):
+        p = range(nk - nq, nk)
+        if buckets:        # the centroids of the complete cluster blocks before each row
+            cand += sum((q + 1) // w.bucket_block * w.bucket_count for q in p)
+        else:
+            cand += sum(q // g + 1 for q in p)
+    return 2.0 * d * w.h_kv * cand, "mfma_fp32"
 
 
 def needle_recall(w, idx_host, n_idx_host):
@@ -314,8 +332,15 @@ KERNEL_SOURCES = {
                              CSRC + "sa_internal.hpp"],
     "sa::attn_wg_kernel": [CSRC + "attn_prefill.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
                            CSRC + "sa_internal.hpp"],
+    "sa::score_rows_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
+    "sa::score_tile_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
+    "sa::attn_valu_kernel": [CSRC + "attn.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
 }
-DOMINANT = {"bf16_decode_32k": "sa::attn_mfma_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel"}
+DOMINANT = {"bf16_decode_32k": "sa::attn_mfma_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel",
+            "bf16_draft_decode": "sa::score_rows_kernel", "bf16_chunked_prefill_1m": "sa::score_tile_kernel",
+            "tiny_fp32_prefill": "sa::attn_valu_kernel"}
+# workloads whose step is dominated by the selection's scoring kernel (rocprofv3 kernel stats)
+SELECT_DOMINANT = ("bf16_draft_decode", "bf16_chunked_prefill_1m")
 
 
 def sources_sha256(files):
@@ -578,7 +603,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    tev = TimingEvents(args.steps)
+    tev = TimingEvents(args.steps, width=4)
     evs = tev.pairs
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -591,7 +616,8 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    attn_ms = tev.mean_ms()
+    attn_ms = tev.mean_ms(2, 3)
+    score_ms = tev.mean_ms(0, 1) if step.time_select else None
     tev.close()
 
     # per-stage times, from events recorded between the three calls, in a pass of its own
@@ -632,6 +658,25 @@ def main():
             roof["frac_of_measured"] = round(roof["achieved"] / peaks["bf16_gemm_tflops"], 4)
         value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
         attn_bytes = None
+    roof = {"kernel": "sa::attn_mfma_kernel" if args.lsa_buckets else DOMINANT.get(w.name, "attention"), **roof}
+    if w.name in SELECT_DOMINANT and score_ms:
+        # the selection's scoring kernel dominates these steps: the roofline is its own,
+        # the attention kernel's figure is kept beside it
+        amount, bound = select_work(w)
+        attn_roof = {k: v for k, v in roof.items() if k != "kernel"}
+        attn_roof["kernel"] = "sa::attn_mfma_kernel"
+        if bound == "hbm":
+            ach = amount / (score_ms * 1e-3) / 1e9
+            roof = dict(kernel=DOMINANT[w.name], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), measured_peak=peaks["copy_gbs"],
+                        frac_of_measured=round(ach / peaks["copy_gbs"], 4))
+        else:
+            ach = amount / (score_ms * 1e-3) / 1e12
+            roof = dict(kernel=DOMINANT[w.name], bound="mfma", dtype="fp32", achieved=round(ach, 2),
+                        peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP32_PEAK_TFLOPS, 4),
+                        measured_peak=peaks["fp32_gemm_tflops"],
+                        frac_of_measured=round(ach / peaks["fp32_gemm_tflops"], 4))
+        roof["attention"] = attn_roof
     roof["traffic"] = measured_traffic(w.name)
 
     extra = {}
@@ -677,6 +722,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "attn_kernel_ms": round(attn_ms, 5),
+        **({"score_kernel_ms": round(score_ms, 5)} if score_ms else {}),
         "attn_algorithmic_bytes": attn_bytes,
         "attended_tokens": a_tot,
         "wall_s": round(wall, 4),

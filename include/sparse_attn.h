@@ -108,7 +108,9 @@ typedef struct sa_params {
     int32_t dtype;             /* sa_dtype of Q, K, V and O                             */
     void *timing_events[2];    /* optional hipEvent_t pair: when both are set,
                                   sparse_attn_fwd records [0] right before and [1]
-                                  right after its main attention kernel on `stream`  */
+                                  right after its main attention kernel on `stream`,
+                                  sparse_attn_select around its scoring kernel (the
+                                  one that reads the keys; the top-k follows)       */
     /* Paged K/V cache (optional; NULL block_table = the packed layout above).
      * With a block table every K and V argument of every call is a page pool
      * [pool_rows, h_kv, d] and token t of sequence b is pool row

@@ -159,11 +159,21 @@ def append_kv(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tens
                                                                _ptr(k_cmp), _stream(stream)))
 
 
+def _set_events(p: Params, events) -> None:
+    """The params' timing event pair: torch.cuda.Event objects (recorded once, so their
+    handles exist) or raw hipEvent_t handles as ints; None clears it."""
+    for i in range(2):
+        e = None if events is None else events[i]
+        p.s.timing_events[i] = e if e is None or isinstance(e, int) else e.cuda_event
+
+
 def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Optional[torch.Tensor],
            idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
-           ws: Optional[torch.Tensor] = None, stream=None, attn_lse: Optional[torch.Tensor] = None):
+           ws: Optional[torch.Tensor] = None, stream=None, attn_lse: Optional[torch.Tensor] = None,
+           events=None):
     """Top-k selection.  With select_mode SA_SELECT_ATTN, q_sel are the verify queries and
-    ``attn_lse`` [h_q, total_q] the log-sum-exp their dense attention pass returned."""
+    ``attn_lse`` [h_q, total_q] the log-sum-exp their dense attention pass returned.
+    ``events`` = (begin, end) pair recorded around the scoring kernel, as for fwd."""
     dev = q_sel.device
     if idx is None:
         idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
@@ -171,11 +181,13 @@ def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Opt
         n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
     ws, nbytes = _ws(workspace_size(p)[0], dev, ws)
     p.s.attn_lse = None if attn_lse is None else attn_lse.data_ptr()
+    _set_events(p, events)
     try:
         st = lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx), _ptr(n_idx), _ptr(ws),
                                       nbytes, _stream(stream))
     finally:
         p.s.attn_lse = None
+        _set_events(p, None)
     check("sparse_attn_select", st)
     return idx, n_idx
 
@@ -191,15 +203,12 @@ def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch
     if want_lse and lse is None:
         lse = torch.empty((p.s.h_q, p.s.total_q), dtype=torch.float32, device=q.device)
     ws, nbytes = _ws(workspace_size(p)[1], q.device, ws)
-    if events is not None:
-        p.s.timing_events[0] = events[0] if isinstance(events[0], int) else events[0].cuda_event
-        p.s.timing_events[1] = events[1] if isinstance(events[1], int) else events[1].cuda_event
+    _set_events(p, events)
     try:
         st = lib().sparse_attn_fwd(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_idx), _ptr(out),
                                    _ptr(lse), _ptr(ws), nbytes, _stream(stream))
     finally:
-        p.s.timing_events[0] = None
-        p.s.timing_events[1] = None
+        _set_events(p, None)
     check("sparse_attn_fwd", st)
     return (out, lse) if want_lse else out
 

@@ -352,7 +352,8 @@ sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float 
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
         return fail(SA_ERR_WORKSPACE, "select needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
-    return device_status(sa::launch_select(kp, p->dtype, q_sel, k_cmp, k, idx, n_idx, ws, (hipStream_t)stream),
+    return device_status(sa::launch_select(kp, p->dtype, q_sel, k_cmp, k, idx, n_idx, ws, (hipStream_t)stream,
+                                           p->timing_events[0], p->timing_events[1]),
                          "select launch");
 }
 

@@ -27,7 +27,8 @@ hipError_t launch_bucket_select(const KP &P, int dtype, const void *q_sel, const
 int select_plan(const KP &P);
 size_t select_workspace_bytes(const KP &P, int plan);
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
-                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st);
+                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st, void *ev0 = nullptr,
+                         void *ev1 = nullptr);
 
 bool wg_fwd_ok(const KP &P, int dtype);
 hipError_t launch_fwd_wg(const KP &P, const void *q, const void *k, const void *v, const int32_t *idx,

@@ -1812,8 +1812,15 @@ int select_plan(const KP &P)
 
 template <typename T, int D>
 static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k_cmp, const void *k,
-                                  int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st)
+                                  int32_t *idx, int32_t *n_idx, void *ws, hipEvent_t ev0, hipEvent_t ev1,
+                                  hipStream_t st)
 {
+    // the optional event pair brackets the scoring kernel (the one that reads the keys)
+    const bool timed = ev0 && ev1;
+    auto mark = [&](hipEvent_t ev) {
+        if (timed)
+            (void)hipEventRecord(ev, st);
+    };
     const T *q = (const T *)q_sel;
     int plan = select_plan(P);
     const long long stride = plan == kSelectRow ? cand_cap(P) : key_stride(P);
@@ -1827,10 +1834,12 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     }
     if (plan == kSelectRowFused) {
         dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
+        mark(ev0);
         if (P.g == 1)
             select_row_kernel<T, T, D><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
         else
             select_row_kernel<T, float, D><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
+        mark(ev1);
         return hipGetLastError();
     }
     if (plan == kSelectRow) {
@@ -1839,10 +1848,12 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         uint32_t *ws_k = wsk;
         int32_t *ws_i = (int32_t *)(wsk + n_slot);
         dim3 grid((unsigned)(P.rows * n_part), (unsigned)P.h_kv);
+        mark(ev0);
         if (P.g == 1)
             select_part_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, ws_k, ws_i, n_part);
         else
             select_part_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, ws_k, ws_i, n_part);
+        mark(ev1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1860,6 +1871,7 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             select_merge_kernel<16><<<mgrid, dim3(256), 0, st>>>(P, ws_k, ws_i, n_part, idx, n_idx);
         return hipGetLastError();
     }
+    mark(ev0);
     if (plan == kSelectHeads) {
         // 128-candidate chunks while the grid would hold fewer than 1024 workgroups (decode)
         float *ws_l = reinterpret_cast<float *>(wsk + (size_t)P.h_kv * (size_t)P.rows * (size_t)stride);
@@ -1915,6 +1927,7 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             score_tile_kernel<T, float, D><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride, col_tiles, gm,
                                                                        gms);
     }
+    mark(ev1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -1937,13 +1950,14 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
 }
 
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
-                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st)
+                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st, void *ev0, void *ev1)
 {
+    hipEvent_t e0 = (hipEvent_t)ev0, e1 = (hipEvent_t)ev1;
     if (dtype == 1)
-        return P.d == 128 ? launch_select_t<uint16_t, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, st)
-                          : launch_select_t<uint16_t, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, st);
-    return P.d == 128 ? launch_select_t<float, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, st)
-                      : launch_select_t<float, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, st);
+        return P.d == 128 ? launch_select_t<uint16_t, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st)
+                          : launch_select_t<uint16_t, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st);
+    return P.d == 128 ? launch_select_t<float, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st)
+                      : launch_select_t<float, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st);
 }
 
 } // namespace sa

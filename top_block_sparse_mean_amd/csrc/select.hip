@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
     constexpr int GPW = kWave / L, NG = 4 * GPW;
-    constexpr int U = 64 / NG < 1 ? 1 : 64 / NG;      // 64 rows per round
+    constexpr int U = 8;                               // key rows per lane group and round (128 bf16, 64 fp32)
     constexpr int RW = U * NG;
     const long long row = blockIdx.x / n_chunk;
     const int chunk = (int)(blockIdx.x % n_chunk);
@@ -1756,7 +1756,7 @@ __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 // ---------------------------------------------------------------- dispatch
 
 static constexpr int kWaveTopkMax = 2048;
-static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (8 rounds of 64)
+static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (a multiple of every round size)
 
 // Candidate capacity of a row, and the row stride of the score-key workspace (a
 // multiple of 4, so every row starts 16-byte aligned).

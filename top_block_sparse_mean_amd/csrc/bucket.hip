@@ -46,6 +46,7 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
     __shared__ int sh_size[kBucketMaxM], sh_alive[kBucketMaxM], sh_root[kBucketMaxM], sh_nn[kBucketMaxM];
     __shared__ int sh_into[kBucketMaxM], sh_pair[kBucketMaxM], sh_bk[kBucketMaxM], sh_off[kBucketMaxM + 1];
     __shared__ float sh_nnc[kBucketMaxM];
+    __shared__ int sh_chg[kBucketMaxM];       // merged or absorbed in the last round: its costs change
     const int M = B.C / P.g, capg = B.cap / P.g, NB = B.NB;
     const int span = B.nblk - B.from;                            // blocks from B.from on
     const int blk = B.from + (int)(blockIdx.x % span);
@@ -71,13 +72,16 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
         sh_size[x] = 1;
         sh_alive[x] = 1;
         sh_root[x] = x;
+        sh_chg[x] = 1;
     }
     int count = M;
     __syncthreads();
     while (count > NB) {
-        for (int pi = tid; pi < M * M; pi += 256) {          // pair costs, lower name first
+        // pair costs, lower name first; a pair of two unchanged buckets keeps its cost
+        // (the same arithmetic on the same sums and sizes)
+        for (int pi = tid; pi < M * M; pi += 256) {
             const int a = pi / M, o = pi % M;
-            if (o <= a)
+            if (o <= a || !(sh_chg[a] | sh_chg[o]))
                 continue;
             float wv = INFINITY;
             if (sh_alive[a] && sh_alive[o] && sh_size[a] + sh_size[o] <= capg)
@@ -126,9 +130,14 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
             if (a >= 0)
                 sh_s[a * D + x % D] += sh_s[x];
         }
+        if (tid < M)
+            sh_chg[tid] = 0;
+        __syncthreads();
         if (tid < M && sh_into[tid] >= 0) {
             atomicAdd(&sh_size[sh_into[tid]], sh_size[tid]);
             sh_alive[tid] = 0;
+            sh_chg[tid] = 1;
+            sh_chg[sh_into[tid]] = 1;
         }
         __syncthreads();
         if (tid < M) {

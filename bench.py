@@ -160,15 +160,21 @@ class Step:
         x = self.x
         mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
         mark(0)
-        if self.decode:
+        # decode: append + select in one call (one launch for decode rows); the stage
+        # pass times them as two calls
+        joined = self.decode and stages is None and self.index is None
+        if self.decode and not joined:
             sa.append_kv(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp)
-        elif self.k_cmp is not None:
+        elif self.k_cmp is not None and not self.decode:
             sa.compress(self.p, x["k"], self.k_cmp)
             if self.index is not None:      # the chunk's new cluster blocks; earlier ones are frozen
                 sa.bucket_build(self.p, self.k_cmp, self.index, build_from=self.build_from)
         mark(1)
         if self.index is not None:
             sa.bucket_select(self.p, x["q"], self.index, self.w.bucket_topk, self.idx, self.n_idx, ws=self.ws_bkt)
+        elif joined:
+            sa.append_select(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp, x["q"], self.idx, self.n_idx,
+                             ws=self.ws_sel, events=events[0:2] if events is not None and self.time_select else None)
         else:
             sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel,
                       events=events[0:2] if events is not None and self.time_select else None)
@@ -719,6 +725,7 @@ def main():
                                                                           else "packed"),
                    "select_mode": args.select_mode, "pool_overlap": w.pool_overlap,
                    "selector": "lsa_buckets" if args.lsa_buckets else "blocks",
+                   **({"append": "sparse_attn_append_select (one launch for decode rows)"} if decode else {}),
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "attn_kernel_ms": round(attn_ms, 5),

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 6
+#define SPARSE_ATTN_ABI_VERSION 7
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -234,6 +234,20 @@ sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const voi
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp,
                              const void *k, int32_t *idx, int32_t *n_idx, void *ws,
                              size_t ws_bytes, void *stream);
+
+/* A decode step's append and selection in one call: the same results as
+ * sparse_attn_append_kv(p, k_new, v_new, k, v, k_cmp) followed by
+ * sparse_attn_select(p, q_sel, k_cmp, k, idx, n_idx, ws).  For decode rows (one
+ * query per sequence, block > 1 with k_cmp, window >= block, a batch whose rows x
+ * KV heads fill the GPU) one launch does both: the workgroup that selects for a
+ * sequence and KV head first writes that sequence's new token and re-pools the
+ * blocks whose pooling window holds it, none of which can be a candidate (the
+ * token's own block lies inside the window).  Otherwise two launches.  Arguments as
+ * for those two calls (select_mode SA_SELECT_ATTN is rejected: it selects from a
+ * verify pass); ws of select_bytes. */
+sa_status sparse_attn_append_select(const sa_params *p, const void *k_new, const void *v_new, void *k,
+                                    void *v, float *k_cmp, const void *q_sel, int32_t *idx, int32_t *n_idx,
+                                    void *ws, size_t ws_bytes, void *stream);
 
 /* Build the bucket index from pooled keys (LSA deep-read, §2.2: streaming Ward
  * clustering into buckets, centroids = normalised member sums).  Every round, each

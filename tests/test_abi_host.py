@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 6
+    assert sa.abi_version() == 7
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -151,6 +151,25 @@ def test_workspace_sizes():
     # per-head group scores: order keys of every (row, block); SOFTMAX also keeps every head's logit
     assert _ws(params(select_mode=2))[0] == 2 * 2 * 64 * 4
     assert _ws(params(select_mode=1))[0] == 2 * 2 * 64 * 4 * (1 + 4)
+
+
+def test_append_select_rejects_bad_arguments():
+    vp = ctypes.c_void_p
+    ok = [vp(FAKE)] * 5
+    p = ctypes.byref(params())
+    # k_new missing; then q_sel missing; then a misaligned k_cmp
+    assert status("sparse_attn_append_select", p, None, *ok[:4], vp(FAKE), vp(FAKE), vp(FAKE), None, 0, None) == INVALID
+    assert status("sparse_attn_append_select", p, *ok, None, vp(FAKE), vp(FAKE), None, 0, None) == INVALID
+    assert status("sparse_attn_append_select", p, *ok[:4], vp(FAKE + 4), vp(FAKE), vp(FAKE), vp(FAKE), None, 0,
+                  None) == INVALID
+    # the verify-pass score needs sparse_attn_select
+    pa = params(select_mode=3)
+    pa.attn_lse = FAKE
+    assert status("sparse_attn_append_select", ctypes.byref(pa), *ok, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1 << 30,
+                  None) == INVALID
+    assert "SA_SELECT_ATTN" in _lib.lib().sparse_attn_last_error().decode()
+    # decode rows need no select workspace once rows x KV heads fill the GPU; small batches do
+    assert status("sparse_attn_append_select", p, *ok, vp(FAKE), vp(FAKE), vp(FAKE), None, 0, None) == WORKSPACE
 
 
 def test_calls_reject_null_and_misaligned_pointers():

@@ -28,8 +28,8 @@ from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM
                    SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaBucketIndex,
                    SaParams, SparseAttnError, check, lib)
 
-__all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select", "fwd",
-           "BucketIndex", "bucket_build", "bucket_select",
+__all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select",
+           "append_select", "fwd", "BucketIndex", "bucket_build", "bucket_select",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
            "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
 
@@ -189,6 +189,26 @@ def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Opt
         p.s.attn_lse = None
         _set_events(p, None)
     check("sparse_attn_select", st)
+    return idx, n_idx
+
+
+def append_select(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  k_cmp: Optional[torch.Tensor], q_sel: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                  n_idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None, events=None):
+    """append_kv then select, in one launch for decode rows (``events`` as for select)."""
+    dev = q_sel.device
+    if idx is None:
+        idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
+    if n_idx is None:
+        n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
+    ws, nbytes = _ws(workspace_size(p)[0], dev, ws)
+    _set_events(p, events)
+    try:
+        st = lib().sparse_attn_append_select(p.ref(), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v), _ptr(k_cmp),
+                                             _ptr(q_sel), _ptr(idx), _ptr(n_idx), _ptr(ws), nbytes, _stream(stream))
+    finally:
+        _set_events(p, None)
+    check("sparse_attn_append_select", st)
     return idx, n_idx
 
 

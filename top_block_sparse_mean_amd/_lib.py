@@ -18,8 +18,8 @@ SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX, SA_SELECT_ATTN = 0, 1, 2, 3
 # Every symbol include/sparse_attn.h declares.
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
-           "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_fwd",
-           "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select")
+           "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_append_select",
+           "sparse_attn_fwd", "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select")
 
 
 class SaParams(ctypes.Structure):
@@ -96,6 +96,7 @@ def lib():
         L.sparse_attn_compress.argtypes = [P, vp, vp, vp]
         L.sparse_attn_compress_tail.argtypes = [P, ctypes.c_int32, vp, vp, vp]
         L.sparse_attn_select.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sparse_attn_append_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int

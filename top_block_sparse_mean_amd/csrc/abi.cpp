@@ -329,12 +329,10 @@ sa_status sparse_attn_bucket_select(const sa_params *p, const void *q_sel, const
                          "bucket select launch");
 }
 
-sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,
-                             int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes, void *stream)
+// The selection's arguments and workspace (after check_params).
+static sa_status check_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,
+                              const int32_t *idx, const int32_t *n_idx, const void *ws, size_t ws_bytes)
 {
-    sa_status s = check_params(p);
-    if (s != SA_OK)
-        return s;
     if (!q_sel || !n_idx || (!idx && p->topk > 0))
         return fail(SA_ERR_INVALID_ARG, "q_sel, idx and n_idx are required");
     const bool attn = p->select_mode == SA_SELECT_ATTN;
@@ -352,9 +350,43 @@ sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float 
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
         return fail(SA_ERR_WORKSPACE, "select needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
+    return SA_OK;
+}
+
+sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,
+                             int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s == SA_OK)
+        s = check_select(p, q_sel, k_cmp, k, idx, n_idx, ws, ws_bytes);
+    if (s != SA_OK)
+        return s;
+    sa::KP kp = make_kp(p);
     return device_status(sa::launch_select(kp, p->dtype, q_sel, k_cmp, k, idx, n_idx, ws, (hipStream_t)stream,
                                            p->timing_events[0], p->timing_events[1]),
                          "select launch");
+}
+
+sa_status sparse_attn_append_select(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
+                                    float *k_cmp, const void *q_sel, int32_t *idx, int32_t *n_idx, void *ws,
+                                    size_t ws_bytes, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!k_new || !v_new || !k || !v)
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k and v are required");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(v) || (k_cmp && !aligned16(k_cmp)))
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k, v and k_cmp must be 16-byte aligned");
+    if (p->select_mode == SA_SELECT_ATTN)
+        return fail(SA_ERR_INVALID_ARG, "SA_SELECT_ATTN selects from a verify pass: use sparse_attn_select");
+    s = check_select(p, q_sel, k_cmp, k, idx, n_idx, ws, ws_bytes);
+    if (s != SA_OK)
+        return s;
+    sa::KP kp = make_kp(p);
+    return device_status(sa::launch_append_select(kp, p->dtype, k_new, v_new, k, v, k_cmp, q_sel, idx, n_idx, ws,
+                                                  (hipStream_t)stream, p->timing_events[0], p->timing_events[1]),
+                         "append_select launch");
 }
 
 sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v, const int32_t *idx,

@@ -1,0 +1,157 @@
+// append_common.hpp -- the decode-time append as workgroup-sized work items, shared
+// by the append kernels (compress.hip) and the decode selection kernel that runs the
+// append in its own launch (select.hip).
+//
+// The append writes each sequence's newest keys and values to its cache rows and
+// re-pools every block whose pooling window holds a new token (SparDA summary,
+// Method: InfLLM-V2 pools keys by a parameter-free mean; LSA deep-read, §2.2: the
+// sum of L2-normalised keys), so the pooled keys stay equal to a fresh pooling of
+// the grown cache.
+#pragma once
+
+#include "sa_common.hpp"
+
+namespace sa {
+
+// Which pooled rows a launch computes: every block, the last n_blk_iter blocks of
+// each sequence, or the blocks holding a sequence's query positions (the tokens an
+// append wrote).  Returns false when jj is past the sequence's range.
+enum { kPoolAll = 0, kPoolTail = 1, kPoolAppended = 2 };
+
+__device__ __forceinline__ bool pooled_block(const KP &P, const Seq &s, int mode, int n_blk_iter, int jj, int &j)
+{
+    const int nb = (s.n_k + P.g - 1) / P.g;
+    int last = nb - 1;
+    if (mode == kPoolAll) {
+        j = jj;
+    } else if (mode == kPoolTail) {
+        j = nb - n_blk_iter + jj;
+    } else {
+        j = s.q0 / P.g + jj;          // a token also lies in the windows of the blocks up to o tokens after it
+        last = s.n_q > 0 ? min(last, (s.q0 + s.n_q - 1 + P.pool_overlap) / P.g) : -1;
+    }
+    return j >= 0 && j <= last && j < P.nb_max;
+}
+
+// Blocks per sequence an append may touch: M consecutive tokens lie in the pooling
+// windows of at most ceil((M + o) / g) + 1 blocks.
+__host__ __forceinline__ int append_pool_blocks(const KP &P)
+{
+    long long n_blk = ((long long)P.max_q + P.pool_overlap + P.g - 1) / P.g + 1;
+    return (int)(n_blk < P.nb_max ? n_blk : P.nb_max);
+}
+
+// Copy of one token's 16-byte piece: k_new / v_new row i -> cache row `row`.
+template <typename T>
+__device__ __forceinline__ void copy_piece(const T *src, T *dst, long long src_row, long long dst_row, int width,
+                                           int x)
+{
+    reinterpret_cast<uint4 *>(dst + dst_row * width)[x] = reinterpret_cast<const uint4 *>(src + src_row * width)[x];
+}
+
+// No pooling (g = 1 or no pooled keys), item i = new token row i: its h_kv x d keys
+// and values go to the cache row of position q0_b + (i - q_off).  256 threads.
+template <typename T>
+__device__ __forceinline__ void append_rows_item(const KP &P, const T *k_new, const T *v_new, T *k, T *v,
+                                                 long long i)
+{
+    const int b = seq_of_query(P, i);
+    const Seq s = seq_info(P, b);
+    const long long row = kv_base(P, s) + kv_map(P, b).row(s.q0 + (int)(i - s.q_off));
+    const int width = P.h_kv * P.d, pieces = width * (int)sizeof(T) / 16;
+    for (int x = threadIdx.x; x < pieces; x += 256) {
+        copy_piece(k_new, k, i, row, width, x);
+        copy_piece(v_new, v, i, row, width, x);
+    }
+}
+
+// With pooling, item = (sequence, KV head, touched block) over append_pool_blocks
+// blocks per sequence.  New tokens in the block's pooling window are taken from
+// k_new / v_new (and written to the cache when they belong to the block itself);
+// its other tokens are read from the cache; the window is pooled as the pooling
+// kernels pool it.  Each new (token, head) belongs to one block, so every cache row
+// is written by one item, and no item reads a row another writes.  The first 256
+// threads do the work (the same summation order whatever the workgroup size); every
+// thread of the workgroup calls it, and it ends with a barrier, so a workgroup may
+// run several items in turn.  UN token rounds of the pooling window are loaded at a
+// time (registers against memory latency; the sums run in token order whatever UN).
+template <typename T, int D, int POOL, int UN = 4>
+__device__ __forceinline__ void append_pool_item(const KP &P, const T *k_new, const T *v_new, T *k, T *v,
+                                                 float *k_cmp, int n_blk_iter, long long item)
+{
+    constexpr int L = D / 8, TG = 256 / L;
+    __shared__ float sh[TG][D];
+    const int jj = (int)(item % n_blk_iter);
+    const int c = (int)((item / n_blk_iter) % P.h_kv);
+    const int b = (int)(item / ((long long)n_blk_iter * P.h_kv));
+    const int tid = threadIdx.x, chunk = tid % L, tg = tid / L;
+    const bool act = tid < 256;
+    const Seq s = seq_info(P, b);
+    const long long k_base = kv_base(P, s);
+    const KvMap map = kv_map(P, b);
+    int j;
+    if (!pooled_block(P, s, kPoolAppended, n_blk_iter, jj, j))
+        return;
+    const int t0 = max(0, j * P.g - P.pool_overlap), t1 = min(j * P.g + P.g, s.n_k);   // pooling window
+    // UN token rounds of the window are loaded before any is summed (with UN = 4 the
+    // window of a 64-token block is one memory latency instead of four); the sums run
+    // in token-round order as without the batching.
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int it0 = 0; it0 < P.g + P.pool_overlap; it0 += UN * TG) {
+        float x[UN][8];
+#pragma unroll
+        for (int u = 0; u < UN; u++) {
+            const int t = t0 + it0 + u * TG + tg;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                x[u][e] = 0.f;
+            if (act && t < t1) {
+                const long long crow = (k_base + map.row(t)) * P.h_kv + c;
+                if (t >= s.q0 && t < s.q0 + s.n_q) {
+                    const long long nrow = (s.q_off + (t - s.q0)) * P.h_kv + c;
+                    load8(k_new + nrow * D + chunk * 8, x[u]);
+                    constexpr int PPC = 8 * (int)sizeof(T) / 16;        // 16-byte pieces per 8 elements
+                    if (t >= j * P.g)                                    // the block's own tokens only
+#pragma unroll
+                        for (int w = 0; w < PPC; w++) {
+                            copy_piece(k_new, k, nrow, crow, D, chunk * PPC + w);
+                            copy_piece(v_new, v, nrow, crow, D, chunk * PPC + w);
+                        }
+                } else {
+                    load8(k + crow * D + chunk * 8, x[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; u++) {
+            float sc = 1.0f;
+            if (POOL == 1) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    ss += x[u][e] * x[u][e];
+                ss = group_sum<L>(ss);
+                sc = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                acc[e] += x[u][e] * sc;
+        }
+    }
+    if (act)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            sh[tg][chunk * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+        for (int g2 = 0; g2 < TG; g2++)
+            sum += sh[g2][tid];
+        if (POOL == 0)
+            sum *= 1.0f / (float)(t1 - t0);
+        k_cmp[(((long long)c * P.batch + b) * P.nb_max + j) * D + tid] = sum;
+    }
+    __syncthreads();                  // sh is free again
+}
+
+} // namespace sa

@@ -14,30 +14,11 @@
 // norm of each key: its d/8 owners are adjacent lanes of one wavefront and sum
 // their squares with xor shuffles; every lane runs the same g iterations so
 // the shuffles stay converged.
+#include "append_common.hpp"
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
 namespace sa {
-
-// Which pooled rows a launch computes: every block, the last n_blk_iter blocks of
-// each sequence, or the blocks holding a sequence's query positions (the tokens an
-// append wrote).  Returns false when jj is past the sequence's range.
-enum { kPoolAll = 0, kPoolTail = 1, kPoolAppended = 2 };
-
-__device__ __forceinline__ bool pooled_block(const KP &P, const Seq &s, int mode, int n_blk_iter, int jj, int &j)
-{
-    const int nb = (s.n_k + P.g - 1) / P.g;
-    int last = nb - 1;
-    if (mode == kPoolAll) {
-        j = jj;
-    } else if (mode == kPoolTail) {
-        j = nb - n_blk_iter + jj;
-    } else {
-        j = s.q0 / P.g + jj;          // a token also lies in the windows of the blocks up to o tokens after it
-        last = s.n_q > 0 ? min(last, (s.q0 + s.n_q - 1 + P.pool_overlap) / P.g) : -1;
-    }
-    return j >= 0 && j <= last && j < P.nb_max;
-}
 
 template <typename T, int D, int POOL>
 __global__ __launch_bounds__(256) void compress_kernel(KP P, const T *__restrict__ k,
@@ -193,115 +174,21 @@ hipError_t launch_compress(const KP &P, int dtype, const void *k, float *k_cmp, 
 
 // ---------------------------------------------------------------- append
 
-// Copy of one token's 16-byte piece: k_new / v_new row i -> cache row `row`.
-template <typename T>
-__device__ __forceinline__ void copy_piece(const T *src, T *dst, long long src_row, long long dst_row, int width,
-                                           int x)
-{
-    reinterpret_cast<uint4 *>(dst + dst_row * width)[x] = reinterpret_cast<const uint4 *>(src + src_row * width)[x];
-}
-
-// No pooling (g = 1 or no pooled keys): one workgroup per new token row i copies
-// its h_kv x d keys and values to the cache row of position q0_b + (i - q_off).
+// The append's work items (append_common.hpp), one workgroup each.
 template <typename T>
 __global__ __launch_bounds__(256) void append_rows_kernel(KP P, const T *__restrict__ k_new,
                                                           const T *__restrict__ v_new, T *__restrict__ k,
                                                           T *__restrict__ v)
 {
-    const long long i = blockIdx.x;
-    const int b = seq_of_query(P, i);
-    const Seq s = seq_info(P, b);
-    const long long row = kv_base(P, s) + kv_map(P, b).row(s.q0 + (int)(i - s.q_off));
-    const int width = P.h_kv * P.d, pieces = width * (int)sizeof(T) / 16;
-    for (int x = threadIdx.x; x < pieces; x += blockDim.x) {
-        copy_piece(k_new, k, i, row, width, x);
-        copy_piece(v_new, v, i, row, width, x);
-    }
+    append_rows_item<T>(P, k_new, v_new, k, v, blockIdx.x);
 }
 
-// With pooling: one workgroup per (sequence, KV head, block whose pooling window
-// holds a new token).  New tokens in the window are taken from k_new / v_new
-// (and written to the cache when they belong to the block itself); its other
-// tokens are read from the cache; the window is pooled exactly as
-// compress_few_kernel pools it.  Each new (token, head) belongs to one block, so
-// every cache row is written by one workgroup, and no workgroup reads a row
-// another writes.
 template <typename T, int D, int POOL>
 __global__ __launch_bounds__(256) void append_pool_kernel(KP P, const T *__restrict__ k_new,
                                                           const T *__restrict__ v_new, T *__restrict__ k,
                                                           T *__restrict__ v, float *__restrict__ k_cmp, int n_blk_iter)
 {
-    constexpr int L = D / 8, TG = 256 / L;
-    __shared__ float sh[TG][D];
-    const int jj = blockIdx.x % n_blk_iter;
-    const int c = (blockIdx.x / n_blk_iter) % P.h_kv;
-    const int b = blockIdx.x / (n_blk_iter * P.h_kv);
-    const int tid = threadIdx.x, chunk = tid % L, tg = tid / L;
-    const Seq s = seq_info(P, b);
-    const long long k_base = kv_base(P, s);
-    const KvMap map = kv_map(P, b);
-    int j;
-    if (!pooled_block(P, s, kPoolAppended, n_blk_iter, jj, j))
-        return;
-    const int t0 = max(0, j * P.g - P.pool_overlap), t1 = min(j * P.g + P.g, s.n_k);   // pooling window
-    // UN token rounds of the window are loaded before any is summed (the window of a
-    // 64-token block is 4 rounds: one memory latency instead of four); the sums run
-    // in token-round order as without the batching.
-    constexpr int UN = 4;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int it0 = 0; it0 < P.g + P.pool_overlap; it0 += UN * TG) {
-        float x[UN][8];
-#pragma unroll
-        for (int u = 0; u < UN; u++) {
-            const int t = t0 + it0 + u * TG + tg;
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                x[u][e] = 0.f;
-            if (t < t1) {
-                const long long crow = (k_base + map.row(t)) * P.h_kv + c;
-                if (t >= s.q0 && t < s.q0 + s.n_q) {
-                    const long long nrow = (s.q_off + (t - s.q0)) * P.h_kv + c;
-                    load8(k_new + nrow * D + chunk * 8, x[u]);
-                    constexpr int PPC = 8 * (int)sizeof(T) / 16;        // 16-byte pieces per 8 elements
-                    if (t >= j * P.g)                                    // the block's own tokens only
-#pragma unroll
-                        for (int w = 0; w < PPC; w++) {
-                            copy_piece(k_new, k, nrow, crow, D, chunk * PPC + w);
-                            copy_piece(v_new, v, nrow, crow, D, chunk * PPC + w);
-                        }
-                } else {
-                    load8(k + crow * D + chunk * 8, x[u]);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UN; u++) {
-            float sc = 1.0f;
-            if (POOL == 1) {
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; e++)
-                    ss += x[u][e] * x[u][e];
-                ss = group_sum<L>(ss);
-                sc = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                acc[e] += x[u][e] * sc;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-        sh[tg][chunk * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-        float sum = 0.f;
-        for (int g2 = 0; g2 < TG; g2++)
-            sum += sh[g2][tid];
-        if (POOL == 0)
-            sum *= 1.0f / (float)(t1 - t0);
-        k_cmp[(((long long)c * P.batch + b) * P.nb_max + j) * D + tid] = sum;
-    }
+    append_pool_item<T, D, POOL>(P, k_new, v_new, k, v, k_cmp, n_blk_iter, blockIdx.x);
 }
 
 template <typename T, int D>
@@ -313,17 +200,14 @@ static hipError_t launch_append_t(const KP &P, const void *k_new, const void *v_
                                                                              (const T *)v_new, (T *)k, (T *)v);
         return hipGetLastError();
     }
-    // M consecutive tokens lie in the windows of at most ceil((M + o) / g) + 1 blocks
-    long long n_blk = ((long long)P.max_q + P.pool_overlap + P.g - 1) / P.g + 1;
-    if (n_blk > P.nb_max)
-        n_blk = P.nb_max;
+    const int n_blk = append_pool_blocks(P);
     const dim3 grid((unsigned)(P.batch * n_blk * P.h_kv));
     if (P.pool == 1)
         append_pool_kernel<T, D, 1><<<grid, dim3(256), 0, st>>>(P, (const T *)k_new, (const T *)v_new, (T *)k,
-                                                                (T *)v, k_cmp, (int)n_blk);
+                                                                (T *)v, k_cmp, n_blk);
     else
         append_pool_kernel<T, D, 0><<<grid, dim3(256), 0, st>>>(P, (const T *)k_new, (const T *)v_new, (T *)k,
-                                                                (T *)v, k_cmp, (int)n_blk);
+                                                                (T *)v, k_cmp, n_blk);
     return hipGetLastError();
 }
 

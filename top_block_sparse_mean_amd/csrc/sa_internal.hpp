@@ -24,6 +24,19 @@ size_t bucket_select_workspace_bytes(const KP &P, const BucketArgs &B, int kb);
 hipError_t launch_bucket_select(const KP &P, int dtype, const void *q_sel, const BucketArgs &B, int kb, int32_t *idx,
                                 int32_t *n_idx, void *ws, hipStream_t st);
 
+// A decode step's append run by the selection kernel's launch (select.hip): the
+// step's new keys and values, the cache they go to, the pooled keys to re-pool, and
+// the blocks per sequence the pooling items cover (0: no append in the launch).
+struct SelAppend {
+    const void *k_new, *v_new;
+    void *k, *v;
+    float *k_cmp;
+    int n_blk;
+};
+hipError_t launch_append_select(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
+                                float *k_cmp, const void *q_sel, int32_t *idx, int32_t *n_idx, void *ws,
+                                hipStream_t st, void *ev0 = nullptr, void *ev1 = nullptr);
+
 int select_plan(const KP &P);
 size_t select_workspace_bytes(const KP &P, int plan);
 hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,

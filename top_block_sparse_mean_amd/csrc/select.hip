@@ -25,6 +25,7 @@
 
 #include <algorithm>
 
+#include "append_common.hpp"
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
@@ -988,7 +989,7 @@ constexpr int kRowPass = 512;
 template <typename T, typename KT, int D>
 __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
                                                           const KT *__restrict__ kbase, int32_t *__restrict__ idx,
-                                                          int32_t *__restrict__ n_idx)
+                                                          int32_t *__restrict__ n_idx, SelAppend app)
 {
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
@@ -1000,6 +1001,25 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
     RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
+    // the step's append for this row's sequence and KV head (one query per sequence):
+    // its new token's rows and the blocks whose pooling window holds it, none of which
+    // is a candidate of the row (the launcher checks window >= block).  It runs first:
+    // beside the key loads in flight its registers would spill.
+    auto append = [&]() {
+        if (app.n_blk == 0)
+            return;
+        const int b = seq_of_query(P, row);
+        const T *kn = (const T *)app.k_new, *vn = (const T *)app.v_new;
+        T *kw = (T *)app.k, *vw = (T *)app.v;
+        for (int jj = 0; jj < app.n_blk; jj++) {
+            const long long item = ((long long)b * P.h_kv + c) * app.n_blk + jj;
+            if (P.pool == 1)
+                append_pool_item<T, D, 1>(P, kn, vn, kw, vw, app.k_cmp, app.n_blk, item);
+            else
+                append_pool_item<T, D, 0>(P, kn, vn, kw, vw, app.k_cmp, app.n_blk, item);
+        }
+    };
+    append();
     if (r.need == r.n_cand || r.need == 0) {
         if (tid == 0)
             n_idx[(long long)c * P.rows + row] = r.need;
@@ -1813,7 +1833,7 @@ int select_plan(const KP &P)
 template <typename T, int D>
 static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k_cmp, const void *k,
                                   int32_t *idx, int32_t *n_idx, void *ws, hipEvent_t ev0, hipEvent_t ev1,
-                                  hipStream_t st)
+                                  hipStream_t st, const SelAppend &app)
 {
     // the optional event pair brackets the scoring kernel (the one that reads the keys)
     const bool timed = ev0 && ev1;
@@ -1836,9 +1856,9 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
         mark(ev0);
         if (P.g == 1)
-            select_row_kernel<T, T, D><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx);
+            select_row_kernel<T, T, D><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx, app);
         else
-            select_row_kernel<T, float, D><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx);
+            select_row_kernel<T, float, D><<<grid, dim3(1024), 0, st>>>(P, q, k_cmp, idx, n_idx, app);
         mark(ev1);
         return hipGetLastError();
     }
@@ -1949,15 +1969,41 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     return hipGetLastError();
 }
 
-hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
-                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st, void *ev0, void *ev1)
+static hipError_t launch_select_app(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
+                                    int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st, void *ev0, void *ev1,
+                                    const SelAppend &app)
 {
     hipEvent_t e0 = (hipEvent_t)ev0, e1 = (hipEvent_t)ev1;
     if (dtype == 1)
-        return P.d == 128 ? launch_select_t<uint16_t, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st)
-                          : launch_select_t<uint16_t, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st);
-    return P.d == 128 ? launch_select_t<float, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st)
-                      : launch_select_t<float, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st);
+        return P.d == 128 ? launch_select_t<uint16_t, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st, app)
+                          : launch_select_t<uint16_t, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st, app);
+    return P.d == 128 ? launch_select_t<float, 128>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st, app)
+                      : launch_select_t<float, 64>(P, q_sel, k_cmp, k, idx, n_idx, ws, e0, e1, st, app);
+}
+
+hipError_t launch_select(const KP &P, int dtype, const void *q_sel, const float *k_cmp, const void *k,
+                         int32_t *idx, int32_t *n_idx, void *ws, hipStream_t st, void *ev0, void *ev1)
+{
+    return launch_select_app(P, dtype, q_sel, k_cmp, k, idx, n_idx, ws, st, ev0, ev1,
+                             SelAppend{nullptr, nullptr, nullptr, nullptr, nullptr, 0});
+}
+
+// The append, then the selection.  Decode rows (one query per sequence, the row plan,
+// pooled keys, window >= block so that no block the append re-pools is a candidate)
+// run the append inside the selection's launch; otherwise two launches.
+hipError_t launch_append_select(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
+                                float *k_cmp, const void *q_sel, int32_t *idx, int32_t *n_idx, void *ws,
+                                hipStream_t st, void *ev0, void *ev1)
+{
+    const bool fused = k_cmp && P.g > 1 && !P.shared && P.max_q == 1 && P.window >= P.g && P.bucket_nb == 0 &&
+                       select_plan(P) == kSelectRowFused;
+    if (fused)
+        return launch_select_app(P, dtype, q_sel, k_cmp, k, idx, n_idx, ws, st, ev0, ev1,
+                                 SelAppend{k_new, v_new, k, v, k_cmp, append_pool_blocks(P)});
+    hipError_t e = launch_append(P, dtype, k_new, v_new, k, v, k_cmp, st);
+    if (e != hipSuccess)
+        return e;
+    return launch_select(P, dtype, q_sel, k_cmp, k, idx, n_idx, ws, st, ev0, ev1);
 }
 
 } // namespace sa

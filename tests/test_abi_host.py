@@ -132,25 +132,26 @@ def test_workspace_sizes():
     # rows x KV heads >= 256: one workgroup per (row, KV head) selects from LDS, no workspace
     assert _ws(params(batch=128, total_q=128, max_k=4096, total_k=128 * 4096)) == (0, 0)
     assert _ws(params(max_k=32768, total_k=65536, topk=32))[0] == 2 * 2 * 4 * 32 * 8
-    # prefill: scores of every (row, block) are kept: h_kv * rows * nb_max * 4
+    # prefill: scores of every (row, block) are kept, rows padded to a multiple of 32 plus
+    # 32 (the first candidate's group starts a 128-byte line): h_kv * rows * (64 + 32) * 4
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
     sel, fwd = _ws(p)
-    assert sel == 2 * 4096 * 64 * 4
+    assert sel == 2 * 4096 * 96 * 4
     # long prefill rows (> 2048 candidates): the scores plus each row's maxima of every
     # 32 candidates (row stride rounded up to a multiple of 4)
     p = params(batch=1, max_q=512, total_q=512, max_k=65536, total_k=65536, block=4)
-    assert _ws(p)[0] == 2 * 512 * (16384 + 512) * 4
+    assert _ws(p)[0] == 2 * 512 * (16384 + 32 + 512) * 4
     p = params(batch=1, max_q=512, total_q=512, max_k=65536 + 4 * 33, total_k=65536 + 4 * 33, block=4)
-    assert _ws(p)[0] == 2 * 512 * (16384 + 36 + 516) * 4
+    assert _ws(p)[0] == 2 * 512 * (16384 + 64 + 32 + 516) * 4
     # token-level shared selection with long rows: scores in the workspace
     p = params(block=1, shared_selection=1, max_q=6, total_q=12, max_k=20000, total_k=40000, topk=3000)
     sel, _ = _ws(p)
-    assert sel == 2 * 2 * 20000 * 4
+    assert sel == 2 * 2 * (20000 + 32) * 4
     # k = 0: nothing to score
     assert _ws(params(topk=0))[0] == 0
     # per-head group scores: order keys of every (row, block); SOFTMAX also keeps every head's logit
-    assert _ws(params(select_mode=2))[0] == 2 * 2 * 64 * 4
-    assert _ws(params(select_mode=1))[0] == 2 * 2 * 64 * 4 * (1 + 4)
+    assert _ws(params(select_mode=2))[0] == 2 * 2 * 96 * 4
+    assert _ws(params(select_mode=1))[0] == 2 * 2 * 96 * 4 * (1 + 4)
 
 
 def test_append_select_rejects_bad_arguments():

@@ -31,6 +31,12 @@
 
 namespace sa {
 
+// Score-key rows (the workspace of the scoring plans) store candidate j of a row at
+// column j + key_col0(P), in rows whose pitch is a multiple of 32: the first
+// candidate's group of 32 starts a 128-byte line, so the tile scorer's 32-candidate
+// runs are whole cache lines.
+__host__ __device__ __forceinline__ int key_col0(const KP &P) { return (32 - first_cand(P) % 32) % 32; }
+
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- row geometry
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
             raw[u] = reinterpret_cast<const uint4 *>(key_row<KT, D>(P, kbase, r, c, j))[sub];
         }
     };
-    uint32_t *dst = ws + ((long long)c * P.rows + row) * stride;
+    uint32_t *dst = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
     float qv[VPL];
     auto reduce = [&](const uint4 (&raw)[U], int rd) {
 #pragma unroll
@@ -603,7 +609,7 @@ __global__ __launch_bounds__(256) void score_heads_kernel(KP P, const T *__restr
         sh_q[x] = acc;
     }
     __syncthreads();
-    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
     float *logits = ws_l + ((long long)c * P.rows + row) * P.G * stride;
     // heads outer, rows inner: one read of a head's query slice per round
     auto reduce = [&](const uint4 (&raw)[U], int rd) {
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(256) void score_attn_kernel(KP P, const T *__restri
     __syncthreads();
     const KvMap kmap = kv_map(P, r.b);
     const T *kb = k + (P.block_table ? 0 : r.k_off * P.h_kv) * D + (long long)c * D;
-    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
     const int rounds = (j1 - j0 + RW - 1) / RW;
     for (int rd = 0; rd < rounds; rd++) {
         float acc[U];
@@ -781,7 +787,7 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(KP P, const float *__
         }
     }
     __syncthreads();
-    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride;
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
     for (int j = r.j_lo + tid; j < r.j_hi; j += 256) {
         float sc = 0.f;
         for (int h = 0; h < P.G; h++)
@@ -1269,7 +1275,7 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int rl = r0 + wr + 16 * a + 4 * lk + i;
-                uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride;
+                uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride + key_col0(P);
                 mx[4 * a + i] = 0u;
 #pragma unroll
                 for (int bb = 0; bb < 2; bb++) {
@@ -1317,7 +1323,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     // only the row's own candidates are read (a causal row of a prefill holds fewer than
     // the stride: on average half of it)
     RowGeo r = row_geo(P, row);
-    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride;
+    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
     const bool pick = r.need != r.n_cand;
     uint32_t kr[KPL];
 #pragma unroll
@@ -1444,8 +1450,9 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
             out[s2] = -1;
         return;
     }
-    const uint32_t *row_keys = ws + ((long long)c * P.rows + row) * stride;   // 16-byte aligned
-    const uint32_t *keys = row_keys + r.j_lo;
+    const uint32_t *row_keys = ws + ((long long)c * P.rows + row) * stride;   // 128-byte aligned
+    const int j_lo = r.j_lo + key_col0(P);                  // the row's first candidate in row_keys
+    const uint32_t *keys = row_keys + j_lo;
     const int nword = (n + 31) / 32;
     for (int x = tid; x < nword; x += NT)
         bitmap[x] = 0u;
@@ -1512,7 +1519,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         __syncthreads();
         if (n_grp <= 4096) {
             // their keys >= t0 into cand_key / cand_idx (one LDS atomic per wavefront and round)
-            const uint32_t *keys = row_keys + r.j_lo;
+            const uint32_t *keys = row_keys + j_lo;
             const int tot = n_grp * kGroupCols;
             constexpr int U = 16;
             for (int e0 = 0; e0 < tot; e0 += NT * U) {
@@ -1554,7 +1561,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         // the row for need = 512 of 262144) -- no histogram atomics on the crowded
         // exponent bins.  More than kCompactCap such keys fall back to the histograms.
         uint32_t mx = 0u;
-        for_each_key<NT>(row_keys, r.j_lo, n, [&](int, uint32_t k) { mx = max(mx, k); });
+        for_each_key<NT>(row_keys, j_lo, n, [&](int, uint32_t k) { mx = max(mx, k); });
         uint32_t t0 = 0u;                                  // a threshold that need maxima reach
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = t0 | (1u << bit);
@@ -1567,7 +1574,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         if (tid == 0)
             sh_ncand = 0;
         __syncthreads();
-        for_each_key<NT>(row_keys, r.j_lo, n, [&](int i, uint32_t k) {
+        for_each_key<NT>(row_keys, j_lo, n, [&](int i, uint32_t k) {
             if (k >= t0) {
                 const int slot = atomicAdd(&sh_ncand, 1);
                 if (slot < kCompactCap) {
@@ -1589,7 +1596,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
             for (int x = tid; x < nb; x += NT)
                 hist[x] = 0;
             __syncthreads();
-            for_each_key<NT>(row_keys, r.j_lo, n, [&](int, uint32_t k) {
+            for_each_key<NT>(row_keys, j_lo, n, [&](int, uint32_t k) {
                 if ((k & pmask) == prefix)
                     atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
             });
@@ -1630,7 +1637,7 @@ __global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t
         __syncthreads();
         const uint32_t top_of_bin = prefix | ~pmask;
         gather = cnt_bin <= kCompactCap;
-        for_each_key<NT>(row_keys, r.j_lo, n, [&](int i, uint32_t k) {
+        for_each_key<NT>(row_keys, j_lo, n, [&](int i, uint32_t k) {
             if (k > top_of_bin) {
                 atomicOr(&bitmap[i >> 5], 1u << (i & 31));
             } else if (gather && (k & pmask) == prefix) {
@@ -1761,7 +1768,8 @@ __global__ __launch_bounds__(NT) void topk_block_kernel(KP P, const uint32_t *__
                                       : r, threadIdx.x, NT);
         return;
     }
-    block_topk<NT>(ws + ((long long)c * P.rows + row) * stride + r.j_lo, r.n_cand, r.need, r.j_lo, out);
+    block_topk<NT>(ws + ((long long)c * P.rows + row) * stride + key_col0(P) + r.j_lo, r.n_cand, r.need, r.j_lo,
+                   out);
     for (int s = r.need + (int)threadIdx.x; s < P.topk; s += NT)
         out[s] = -1;
 }
@@ -1779,21 +1787,22 @@ __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 static constexpr int kWaveTopkMax = 2048;
 static constexpr int kSplitChunk = 512;  // candidates per scoring workgroup (a multiple of every round size)
 
-// Candidate capacity of a row, and the row stride of the score-key workspace (a
-// multiple of 4, so every row starts 16-byte aligned).
+// Candidate capacity of a row, and the row pitch of the score-key workspace (a
+// multiple of 32 with room for the key_col0 shift, so every row starts a 128-byte
+// line).
 static constexpr long long kRowFusedMin = 256;          // rows x KV heads for the fused row plan
 
 static long long cand_cap(const KP &P) { return P.g == 1 ? P.max_k : P.nb_max; }
-static long long key_stride(const KP &P) { return (cand_cap(P) + 3) / 4 * 4; }
+static long long key_stride(const KP &P) { return (cand_cap(P) + 31) / 32 * 32 + 32; }
 
 // Group maxima of the scores (tile scoring followed by the compacting top-k): their
 // row stride, or 0 when not kept.
 static long long gmax_stride(const KP &P, int plan)
 {
-    const long long stride = key_stride(P);
-    if (plan != kSelectTile || stride <= kWaveTopkMax || stride > kCompactMaxN || getenv("SPARSE_ATTN_TOPK_RADIX"))
+    const long long cap = cand_cap(P);
+    if (plan != kSelectTile || cap <= kWaveTopkMax || cap > kCompactMaxN || getenv("SPARSE_ATTN_TOPK_RADIX"))
         return 0;
-    return ((stride + kGroupCols - 1) / kGroupCols + 3) / 4 * 4;
+    return ((cap + kGroupCols - 1) / kGroupCols + 3) / 4 * 4;
 }
 
 size_t select_workspace_bytes(const KP &P, int plan)
@@ -1956,15 +1965,16 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     if (e != hipSuccess)
         return e;
     dim3 tgrid((unsigned)((P.rows + 3) / 4), (unsigned)P.h_kv);
-    if (stride <= 256)
+    const long long cap = cand_cap(P);                     // the top-k kernel by the candidates a row can hold
+    if (cap <= 256)
         topk_wave_kernel<4><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
-    else if (stride <= 512)
+    else if (cap <= 512)
         topk_wave_kernel<8><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
-    else if (stride <= 1024)
+    else if (cap <= 1024)
         topk_wave_kernel<16><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
-    else if (stride <= kWaveTopkMax)
+    else if (cap <= kWaveTopkMax)
         topk_wave_kernel<32><<<tgrid, dim3(256), 0, st>>>(P, wsk, stride, idx, n_idx);
-    else if (stride <= kCompactMaxN && !getenv("SPARSE_ATTN_TOPK_RADIX"))
+    else if (cap <= kCompactMaxN && !getenv("SPARSE_ATTN_TOPK_RADIX"))
         topk_compact_kernel<<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(P, wsk, stride, idx,
                                                                                            n_idx, gm, gms);
     else

@@ -484,27 +484,25 @@ int or_attend(int batch, int h_q, int h_kv, int d, const int32_t *cu_q, const in
  * size <= cap groups), and the pairs that are each other's cheapest merge together
  * (if that would leave fewer than NB buckets, only the cheapest pairs do, enough to
  * reach NB); rounds repeat until NB buckets remain or no pair may merge.  Ward's
- * criterion for buckets A, B with member sums S and sizes n is
- * n_A n_B / (n_A + n_B) |S_A/n_A - S_B/n_B|^2, evaluated here as
- * |n_B S_A - n_A S_B|^2 / (n_A n_B (n_A + n_B)) in fp32 with fused multiply-adds
- * over the head dimension in order (the precision the kernel decides in).  Ties:
- * the lower bucket (a bucket is named by its smallest member).  A bucket's centroid
+ * criterion for buckets A, B with member sums S and sizes n is the growth of the
+ * within-bucket sum of squares when they merge,
+ * n_A n_B / (n_A + n_B) |S_A/n_A - S_B/n_B|^2, computed as written in fp64 from
+ * the fp64 pooled keys (member sums in fp64 too).  Ties: the lower bucket (a
+ * bucket is named by its smallest member).  A bucket's centroid
  * is the normalised sum of its members.  Output per block: members grouped by
  * bucket (buckets in name order, members ascending), NB + 1 offsets, NB centroids
  * (fp64), and the smallest relative margin of any decision taken (second best vs
  * best partner; first excluded vs last merged pair), so tests can tell a
  * near-tied block from a wrong one.
  */
-static float ward_cost(const float *sa, int na, const float *sb, int nb, int d)
+static double ward_cost(const double *sa, int na, const double *sb, int nb, int d)
 {
-    float acc = 0.0f;
-    const float fa = (float)na, fb = (float)nb;
+    double dist2 = 0.0;                      /* |mean_A - mean_B|^2 */
     for (int e = 0; e < d; e++) {
-        const float t = fa * sb[e];
-        const float diff = fmaf(fb, sa[e], -t);
-        acc = fmaf(diff, diff, acc);
+        const double diff = sa[e] / na - sb[e] / nb;
+        dist2 += diff * diff;
     }
-    return acc * (1.0f / (float)(na * nb * (na + nb)));
+    return (double)na * nb / (na + nb) * dist2;
 }
 
 int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int C, int NB, int cap_tok,
@@ -534,14 +532,14 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
                 off[x] = 0;
             continue;
         }
-        float *S = (float *)malloc(sizeof(float) * (size_t)M * d);
+        double *S = (double *)malloc(sizeof(double) * (size_t)M * d);
         int *size = (int *)malloc(sizeof(int) * M), *alive = (int *)malloc(sizeof(int) * M);
         int *root = (int *)malloc(sizeof(int) * M), *nn = (int *)malloc(sizeof(int) * M);
-        float *nnc = (float *)malloc(sizeof(float) * M);
+        double *nnc = (double *)malloc(sizeof(double) * M);
         for (int x = 0; x < M; x++) {
             const double *src = k_cmp + (((int64_t)c * batch + b) * nb_max + cb * M + x) * d;
             for (int e = 0; e < d; e++)
-                S[x * d + e] = (float)src[e];
+                S[x * d + e] = src[e];
             size[x] = 1;
             alive[x] = 1;
             root[x] = x;
@@ -554,12 +552,11 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
                 nn[a] = -1;
                 if (!alive[a])
                     continue;
-                float best = INFINITY, second = INFINITY;
+                double best = INFINITY, second = INFINITY;
                 for (int o = 0; o < M; o++) {
                     if (o == a || !alive[o] || size[a] + size[o] > capg)
                         continue;
-                    const int lo = a < o ? a : o, hi = a < o ? o : a;      /* symmetric: lower name first */
-                    float w = ward_cost(S + lo * d, size[lo], S + hi * d, size[hi], d);
+                    double w = ward_cost(S + a * d, size[a], S + o * d, size[o], d);
                     if (w < best) {
                         second = best;
                         best = w;
@@ -572,7 +569,7 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
                 if (nn[a] >= 0) {
                     any = 1;
                     if (second < INFINITY) {
-                        double r = best > 0.0f ? ((double)second - best) / best : (second > 0.0f ? INFINITY : 0.0);
+                        double r = best > 0.0 ? (second - best) / best : (second > 0.0 ? INFINITY : 0.0);
                         if (r < mg)
                             mg = r;
                     }
@@ -595,8 +592,8 @@ int or_bucket_build(int batch, int h_kv, int d, const int32_t *cu_k, int g, int 
                 }
             int take = np < count - NB ? np : count - NB;
             if (take < np && take > 0) {
-                float lo = nnc[pa[take - 1]], hi = nnc[pa[take]];
-                double r = lo > 0.0f ? ((double)hi - lo) / lo : (hi > 0.0f ? INFINITY : 0.0);
+                double lo = nnc[pa[take - 1]], hi = nnc[pa[take]];
+                double r = lo > 0.0 ? (hi - lo) / lo : (hi > 0.0 ? INFINITY : 0.0);
                 if (r < mg)
                     mg = r;
             }

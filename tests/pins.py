@@ -360,6 +360,15 @@ def pin_bucket_ward_weighting():
     assert _buckets(ix) == [[0, 1], [2, 3]]
 
 
+def pin_bucket_ward_uses_means():
+    """Ward's cost compares bucket means: after {0, 1} merges (mean 10.1), point 2 at 11
+    costs 2/3 * 0.9^2 = 0.54 to join it and point 3 at 19 costs 32 to join point 2, so
+    {0, 1, 2} forms; comparing member sums (20.2) instead would pair {0, 1} with point 3."""
+    pts = [(10.0, 0.0), (10.2, 0.0), (11.0, 0.0), (19.0, 0.0)]
+    w, ix = _bucket_index(pts, C=4, NB=2, cap=4)
+    assert _buckets(ix) == [[0, 1, 2], [3]]
+
+
 def pin_bucket_invariants():
     """Random keys: each complete cluster block is partitioned into exactly NB buckets of at
     most cap/g groups, named and listed in order; centroids are normalised member sums;

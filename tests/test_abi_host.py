@@ -154,6 +154,21 @@ def test_workspace_sizes():
     assert _ws(params(select_mode=1))[0] == 2 * 2 * 96 * 4 * (1 + 4)
 
 
+def test_long_attended_sets_leave_the_gather_kernel():
+    """The bf16 gather kernel lists each split's tokens in LDS (8192 per split, at most 64
+    splits merged by the combine); a set longer than 64 * 8192 tokens must go to the VALU
+    kernel, which walks positions with no list (at most 32 splits). Checked through the
+    attention workspace each plan asks for; nothing runs on a device."""
+    part = 8 * 130 * 4                      # one split's partials of the query's 8 heads, d = 128
+    at_cap = params(batch=1, max_q=1, total_q=1, max_k=1 << 19, total_k=1 << 19, topk=8192)
+    assert _ws(at_cap)[1] == 64 * part       # 524288 tokens: gather kernel, 64 splits of 8192
+    beyond = params(batch=1, max_q=1, total_q=1, max_k=1 << 20, total_k=1 << 20, topk=16384)
+    assert _ws(beyond)[1] == 32 * part       # 1048576 tokens: VALU kernel
+    drafts = params(batch=1, max_q=6, total_q=6, max_k=(1 << 20) + 6, total_k=(1 << 20) + 6, block=1,
+                    topk=1 << 20, shared_selection=1, h_q=4)
+    assert _ws(drafts)[1] == 6 * 4 * 32 * 130 * 4
+
+
 def test_append_select_rejects_bad_arguments():
     vp = ctypes.c_void_p
     ok = [vp(FAKE)] * 5

@@ -2,8 +2,8 @@
 
 Build: every complete cluster block's partition into buckets must equal the
 oracle's, except in blocks where the oracle saw a near-tied decision (relative
-margin < 1e-4): the merges are decided in fp32 on both sides, from pooled keys
-that each side computes itself, so a near tie may go either way.  Centroids of
+margin < 1e-4): the oracle decides its merges in fp64 and the kernel in fp32,
+each from pooled keys it computes itself, so a near tie may go either way.  Centroids of
 equal partitions agree to fp32 rounding.  Retrieval: rows whose visible blocks all
 partition alike must select the oracle's groups (or sit on a bucket-score near
 tie).  Attention runs on the GPU's table and is compared with the oracle's

@@ -39,8 +39,8 @@ MUTANTS = {
                                "int64_t t0 = (int64_t)cs[x].j * g, t1 = t0;"),
     "attn_last_query_only": ("for (int64_t i = qa; i < qb; i++) {\n                int64_t p_i",
                              "for (int64_t i = qb - 1; i < qb; i++) {\n                int64_t p_i"),
-    "ward_unweighted": ("return acc * (1.0f / (float)(na * nb * (na + nb)));",
-                        "return acc * (1.0f / (float)(na * na * nb * nb));"),
+    "ward_unweighted": ("return (double)na * nb / (na + nb) * dist2;", "return dist2;"),
+    "ward_sums_not_means": ("const double diff = sa[e] / na - sb[e] / nb;", "const double diff = sa[e] - sb[e];"),
     "ward_not_mutual": ("if (alive[a] && nn[a] > a && nn[nn[a]] == a)", "if (alive[a] && nn[a] > a)"),
     "ward_truncate_dearest": ("(nnc[pa[y]] < nnc[pa[y - 1]] ||", "(nnc[pa[y]] > nnc[pa[y - 1]] ||"),
     "ward_ignore_cap": ("if (o == a || !alive[o] || size[a] + size[o] > capg)", "if (o == a || !alive[o])"),

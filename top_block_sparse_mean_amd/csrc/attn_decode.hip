@@ -163,19 +163,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
     }
 }
 
+// Largest attended set of any unit (init + selected blocks + window, plus the
+// drafts of a shared selection), bounded by the longest cache.
+static long long mfma_set_max(const KP &P)
+{
+    long long a_max = (long long)P.n_init + (long long)P.topk * P.g + P.window + (P.shared ? P.max_q : 0);
+    return a_max > P.max_k ? P.max_k : a_max;
+}
+
+// The gather kernel keeps each split's token list in LDS (kTokCap entries) and
+// the combine merges at most kMaxSplits splits, so it serves sets of at most
+// kMaxSplits * kTokCap tokens; longer sets take the VALU kernel, which walks
+// the set's positions with no list.
 bool mfma_fwd_ok(const KP &P, int dtype)
 {
     if (dtype != 1)
         return false;
     long long rows = P.shared ? (long long)P.max_q * P.G : P.G;
-    return rows <= 16;
+    return rows <= 16 && mfma_set_max(P) <= (long long)kMaxSplits * kTokCap;
 }
 
 int mfma_fwd_splits(const KP &P)
 {
-    long long a_max = (long long)P.n_init + (long long)P.topk * P.g + P.window + (P.shared ? P.max_q : 0);
-    if (a_max > P.max_k)
-        a_max = P.max_k;
+    const long long a_max = mfma_set_max(P);
     long long units = (P.shared ? P.batch : P.total_q) * P.h_kv;
     long long need = (a_max + kTokCap - 1) / kTokCap;          // the token list must fit in LDS
     long long fill = (256 + units - 1) / units;                // at least one workgroup per CU
@@ -188,8 +198,8 @@ int mfma_fwd_splits(const KP &P)
         if (v > 0)
             sp = v > need ? v : need;
     }
-    if (sp > 64)
-        sp = 64;
+    if (sp > kMaxSplits)                                       // need <= kMaxSplits (mfma_fwd_ok)
+        sp = kMaxSplits;
     return sp < 1 ? 1 : (int)sp;
 }
 

@@ -122,6 +122,8 @@ __device__ __forceinline__ void compute_chunk(const ChunkRegs<D> &r, uint32_t li
 }
 
 constexpr int kTokCap = 8192;
+// Splits of one attended set: attn_combine reads one split per lane of a wavefront.
+constexpr int kMaxSplits = 64;
 
 // Exclusive scan of one int per thread over a 512-thread workgroup; (exclusive, total).
 __device__ __forceinline__ int2 block_scan_int_512(int v, int *sh)

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 7
+#define SPARSE_ATTN_ABI_VERSION 8
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -288,6 +288,21 @@ sa_status sparse_attn_bucket_select(const sa_params *p, const void *q_sel, const
 sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v,
                           const int32_t *idx, const int32_t *n_idx, void *out, float *lse,
                           void *ws, size_t ws_bytes, void *stream);
+
+/* sparse_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the split partials kept in a fixed 32 MiB
+ * device array that the library holds on each GPU it runs on until the process
+ * ends, instead of a caller workspace.  Arguments as for sparse_attn_fwd less
+ * the workspace.  Parameters whose partials would exceed 32 MiB (fwd_bytes of
+ * sparse_attn_workspace_size) return SA_ERR_WORKSPACE before any HIP call.
+ * The first call on a device looks up the array's address (no allocation).
+ * Every call on one GPU shares that array, so calls that overlap in time on one
+ * GPU (other streams, other threads) race; it needs no clearing (every split
+ * writes all its partials before the combine reads them). */
+sa_status sparse_attn_fwd_noalloc(const sa_params *p, const void *q, const void *k, const void *v,
+                                  const int32_t *idx, const int32_t *n_idx, void *out, float *lse,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

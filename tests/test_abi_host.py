@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 7
+    assert sa.abi_version() == 8
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -167,6 +167,19 @@ def test_long_attended_sets_leave_the_gather_kernel():
     drafts = params(batch=1, max_q=6, total_q=6, max_k=(1 << 20) + 6, total_k=(1 << 20) + 6, block=1,
                     topk=1 << 20, shared_selection=1, h_q=4)
     assert _ws(drafts)[1] == 6 * 4 * 32 * 130 * 4
+
+
+def test_fwd_noalloc_rejects_partials_above_its_scratch():
+    """The no-allocation attention keeps split partials in a fixed 32 MiB device array: a
+    decode batch whose 524288-token sets need 64 splits (34 MB of partials) is refused on
+    the host with SA_ERR_WORKSPACE before any HIP call; a missing pointer is refused too."""
+    vp = ctypes.c_void_p
+    big = params(batch=32, h_q=32, h_kv=8, max_q=1, total_q=32, max_k=1 << 19, total_k=32 << 19, topk=8192)
+    assert _ws(big)[1] == 32 * 32 * 64 * 130 * 4 > 32 << 20
+    args = [vp(FAKE)] * 6 + [None, None]
+    assert status("sparse_attn_fwd_noalloc", ctypes.byref(big), *args) == WORKSPACE
+    assert b"32" in _lib.lib().sparse_attn_last_error()
+    assert status("sparse_attn_fwd_noalloc", ctypes.byref(params()), None, *args[1:]) == INVALID
 
 
 def test_append_select_rejects_bad_arguments():

@@ -29,7 +29,7 @@ from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM
                    SaParams, SparseAttnError, check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select",
-           "append_select", "fwd", "BucketIndex", "bucket_build", "bucket_select",
+           "append_select", "fwd", "fwd_noalloc", "BucketIndex", "bucket_build", "bucket_select",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
            "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
 
@@ -231,6 +231,16 @@ def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch
         _set_events(p, None)
     check("sparse_attn_fwd", st)
     return (out, lse) if want_lse else out
+
+
+def fwd_noalloc(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                n_idx: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """fwd with every buffer supplied by the caller and the split partials in the library's
+    fixed device scratch: allocates nothing (for callers that cannot allocate)."""
+    st = lib().sparse_attn_fwd_noalloc(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_idx), _ptr(out),
+                                       _ptr(lse), _stream(stream))
+    check("sparse_attn_fwd_noalloc", st)
+    return out
 
 
 class BucketIndex:

@@ -19,7 +19,8 @@ SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX, SA_SELECT_ATTN = 0, 1, 2, 3
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
            "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_append_select",
-           "sparse_attn_fwd", "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select")
+           "sparse_attn_fwd", "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select",
+           "sparse_attn_fwd_noalloc")
 
 
 class SaParams(ctypes.Structure):
@@ -98,6 +99,7 @@ def lib():
         L.sparse_attn_select.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_append_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L

@@ -389,8 +389,8 @@ sa_status sparse_attn_append_select(const sa_params *p, const void *k_new, const
                          "append_select launch");
 }
 
-sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v, const int32_t *idx,
-                          const int32_t *n_idx, void *out, float *lse, void *ws, size_t ws_bytes, void *stream)
+static sa_status check_fwd(const sa_params *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                           const int32_t *n_idx, const void *out)
 {
     sa_status s = check_params(p);
     if (s != SA_OK)
@@ -399,6 +399,15 @@ sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, cons
         return fail(SA_ERR_INVALID_ARG, "q, k, v, out, idx and n_idx are required");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(SA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    return SA_OK;
+}
+
+sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                          const int32_t *n_idx, void *out, float *lse, void *ws, size_t ws_bytes, void *stream)
+{
+    sa_status s = check_fwd(p, q, k, v, idx, n_idx, out);
+    if (s != SA_OK)
+        return s;
     sa::KP kp = make_kp(p);
     int splits = sa::fwd_splits(kp);
     size_t need = sa::fwd_workspace_bytes(kp, splits);
@@ -408,6 +417,30 @@ sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, cons
     return device_status(sa::launch_fwd(kp, p->dtype, q, k, v, idx, n_idx, out, lse, ws, splits,
                                         p->timing_events[0], p->timing_events[1], (hipStream_t)stream),
                          "fwd launch");
+}
+
+sa_status sparse_attn_fwd_noalloc(const sa_params *p, const void *q, const void *k, const void *v,
+                                  const int32_t *idx, const int32_t *n_idx, void *out, float *lse, void *stream)
+{
+    sa_status s = check_fwd(p, q, k, v, idx, n_idx, out);
+    if (s != SA_OK)
+        return s;
+    sa::KP kp = make_kp(p);
+    int splits = sa::fwd_splits(kp);
+    size_t need = sa::fwd_workspace_bytes(kp, splits);
+    if (need > sa::kNoAllocScratchBytes)
+        return fail(SA_ERR_WORKSPACE, "fwd_noalloc: these parameters need %zu bytes of split partials, above the "
+                    "fixed %zu-byte device scratch; use sparse_attn_fwd with a workspace", need,
+                    sa::kNoAllocScratchBytes);
+    void *scratch = nullptr;
+    if (need > 0) {
+        hipError_t e = sa::noalloc_scratch(&scratch);
+        if (e != hipSuccess)
+            return device_status(e, "fwd_noalloc scratch lookup");
+    }
+    return device_status(sa::launch_fwd(kp, p->dtype, q, k, v, idx, n_idx, out, lse, scratch, splits,
+                                        p->timing_events[0], p->timing_events[1], (hipStream_t)stream),
+                         "fwd_noalloc launch");
 }
 
 } // extern "C"

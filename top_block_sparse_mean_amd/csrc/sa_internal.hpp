@@ -61,4 +61,8 @@ hipError_t launch_fwd(const KP &P, int dtype, const void *q, const void *k, cons
                       const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev_begin,
                       void *ev_end, hipStream_t st);
 
+// Fixed device scratch of sparse_attn_fwd_noalloc (one array per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 } // namespace sa

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 8
+#define SPARSE_ATTN_ABI_VERSION 9
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -226,14 +226,23 @@ sa_status sparse_attn_append_kv(const sa_params *p, const void *k_new, const voi
  *          ascending order, padded with -1; rows = total_q, or batch when
  *          shared_selection = 1
  *   n_idx  [h_kv, rows] int32 out: number of selected blocks, min(k, |C|)
+ *   boundary_scores  [h_kv, rows, 2] fp32 out, or NULL: the row's need-th and
+ *          (need+1)-th largest scores, need = min(k, |C|) (the smallest score
+ *          kept and the largest left out), taken from the very fp32 values the
+ *          selection ranked, in the select mode's units (the default mode's
+ *          dot times 1/sqrt(d); the other modes' scores as they are); both NaN
+ *          for a row that keeps every candidate or none (nothing is ranked).
+ *          This is the near-tie audit of the stated tie rule: a row whose two
+ *          values differ by < 1e-4 relative sits on a near tie.  Costs an extra
+ *          pass over the scores on plans that keep them in the workspace.
  *   ws     workspace of at least select_bytes (sparse_attn_workspace_size),
  *          owned by the caller; its contents on entry do not matter.  Calls
  *          that share one workspace must not overlap in time.
  * Scores are computed in fp32 from fp32 pooled keys and fp32-summed queries;
  * equal scores keep the lower block index. */
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp,
-                             const void *k, int32_t *idx, int32_t *n_idx, void *ws,
-                             size_t ws_bytes, void *stream);
+                             const void *k, int32_t *idx, int32_t *n_idx, float *boundary_scores,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* A decode step's append and selection in one call: the same results as
  * sparse_attn_append_kv(p, k_new, v_new, k, v, k_cmp) followed by

@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 8
+    assert sa.abi_version() == 9
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -124,14 +124,14 @@ def _ws(p):
 
 def test_workspace_sizes():
     # decode shape: (key, position) survivors of each 128-candidate part of every (row, KV
-    # head), min(k, 128) per part; one attention split per (query, KV head) unit when there
-    # are enough units, else partials for the combine
+    # head), min(k + 1, 128) per part; one attention split per (query, KV head) unit when
+    # there are enough units, else partials for the combine
     sel, fwd = _ws(params())
-    assert sel == 2 * 2 * 1 * 8 * 8 and fwd > 0 and fwd % (130 * 4) == 0
-    assert _ws(params(batch=64, total_q=64, max_k=4096, total_k=64 * 4096))[0] == 2 * 64 * 1 * 8 * 8
+    assert sel == 2 * 2 * 1 * 9 * 8 and fwd > 0 and fwd % (130 * 4) == 0
+    assert _ws(params(batch=64, total_q=64, max_k=4096, total_k=64 * 4096))[0] == 2 * 64 * 1 * 9 * 8
     # rows x KV heads >= 256: one workgroup per (row, KV head) selects from LDS, no workspace
     assert _ws(params(batch=128, total_q=128, max_k=4096, total_k=128 * 4096)) == (0, 0)
-    assert _ws(params(max_k=32768, total_k=65536, topk=32))[0] == 2 * 2 * 4 * 32 * 8
+    assert _ws(params(max_k=32768, total_k=65536, topk=32))[0] == 2 * 2 * 4 * 33 * 8
     # prefill: scores of every (row, block) are kept, rows padded to a multiple of 32 plus
     # 32 (the first candidate's group starts a 128-byte line): h_kv * rows * (64 + 32) * 4
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
@@ -207,8 +207,14 @@ def test_calls_reject_null_and_misaligned_pointers():
     assert status("sparse_attn_compress", p, None, vp(FAKE), None) == INVALID
     assert status("sparse_attn_compress", p, vp(FAKE + 2), vp(FAKE), None) == INVALID
     assert status("sparse_attn_compress_tail", p, 0, vp(FAKE), vp(FAKE), None) == INVALID
-    assert status("sparse_attn_select", p, None, vp(FAKE), None, vp(FAKE), vp(FAKE), None, 0, None) == INVALID
-    assert status("sparse_attn_select", p, vp(FAKE), None, None, vp(FAKE), vp(FAKE), None, 0, None) == INVALID
+    assert status("sparse_attn_select", p, None, vp(FAKE), None, vp(FAKE), vp(FAKE), None, None, 0, None) == INVALID
+    assert status("sparse_attn_select", p, vp(FAKE), None, None, vp(FAKE), vp(FAKE), None, None, 0,
+                  None) == INVALID
+    # the boundary-score output is optional but must hold aligned fp32
+    pb = ctypes.byref(params(batch=128, total_q=128))      # row plan: no workspace needed
+    assert status("sparse_attn_select", pb, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE + 2), None, 0,
+                  None) == INVALID
+    assert "boundary_scores" in _lib.lib().sparse_attn_last_error().decode()
     assert status("sparse_attn_fwd", p, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), None, None, 0,
                   None) == INVALID
     assert status("sparse_attn_fwd", p, vp(FAKE + 8), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
@@ -223,10 +229,10 @@ def test_calls_reject_null_and_misaligned_pointers():
     # more than 64 (query, head) pairs are not built
     pa = ctypes.byref(params(select_mode=3))
     ws = vp(FAKE)
-    assert status("sparse_attn_select", pa, vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), ws, 1 << 30,
+    assert status("sparse_attn_select", pa, vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), None, ws, 1 << 30,
                   None) == INVALID
     assert "attn_lse" in _lib.lib().sparse_attn_last_error().decode()
-    assert status("sparse_attn_select", pa, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), ws, 1 << 30,
+    assert status("sparse_attn_select", pa, vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), None, ws, 1 << 30,
                   None) == INVALID
     assert "raw keys" in _lib.lib().sparse_attn_last_error().decode()
     big = params(select_mode=3, shared_selection=1, max_q=20, total_q=40, attn_lse=FAKE)   # 20 x 4 pairs
@@ -244,7 +250,8 @@ def test_calls_reject_small_workspace():
     assert r == WORKSPACE
     assert str(fwd) in _lib.lib().sparse_attn_last_error().decode()
     p = params(batch=1, max_q=4096, total_q=4096, max_k=4096, total_k=4096)
-    r = status("sparse_attn_select", ctypes.byref(p), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), None, 0, None)
+    r = status("sparse_attn_select", ctypes.byref(p), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), None, None, 0,
+               None)
     assert r == WORKSPACE
 
 

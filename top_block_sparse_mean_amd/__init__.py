@@ -170,26 +170,30 @@ def _set_events(p: Params, events) -> None:
 def select(p: Params, q_sel: torch.Tensor, k_cmp: Optional[torch.Tensor], k: Optional[torch.Tensor],
            idx: Optional[torch.Tensor] = None, n_idx: Optional[torch.Tensor] = None,
            ws: Optional[torch.Tensor] = None, stream=None, attn_lse: Optional[torch.Tensor] = None,
-           events=None):
+           events=None, boundary: Optional[torch.Tensor] = None, want_boundary: bool = False):
     """Top-k selection.  With select_mode SA_SELECT_ATTN, q_sel are the verify queries and
     ``attn_lse`` [h_q, total_q] the log-sum-exp their dense attention pass returned.
-    ``events`` = (begin, end) pair recorded around the scoring kernel, as for fwd."""
+    ``events`` = (begin, end) pair recorded around the scoring kernel, as for fwd.
+    With ``want_boundary`` (or a ``boundary`` tensor [h_kv, rows, 2] fp32) the call also
+    returns each row's need-th and (need+1)-th scores: (idx, n_idx, boundary)."""
     dev = q_sel.device
     if idx is None:
         idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
     if n_idx is None:
         n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
+    if want_boundary and boundary is None:
+        boundary = torch.empty((p.s.h_kv, p.rows, 2), dtype=torch.float32, device=dev)
     ws, nbytes = _ws(workspace_size(p)[0], dev, ws)
     p.s.attn_lse = None if attn_lse is None else attn_lse.data_ptr()
     _set_events(p, events)
     try:
-        st = lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx), _ptr(n_idx), _ptr(ws),
-                                      nbytes, _stream(stream))
+        st = lib().sparse_attn_select(p.ref(), _ptr(q_sel), _ptr(k_cmp), _ptr(k), _ptr(idx), _ptr(n_idx),
+                                      _ptr(boundary), _ptr(ws), nbytes, _stream(stream))
     finally:
         p.s.attn_lse = None
         _set_events(p, None)
     check("sparse_attn_select", st)
-    return idx, n_idx
+    return (idx, n_idx, boundary) if boundary is not None else (idx, n_idx)
 
 
 def append_select(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

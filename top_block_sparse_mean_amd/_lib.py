@@ -96,7 +96,7 @@ def lib():
         L.sparse_attn_workspace_size.argtypes = [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.sparse_attn_compress.argtypes = [P, vp, vp, vp]
         L.sparse_attn_compress_tail.argtypes = [P, ctypes.c_int32, vp, vp, vp]
-        L.sparse_attn_select.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sparse_attn_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_append_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]

@@ -134,6 +134,9 @@ sa::KP make_kp(const sa_params *p)
                              : 1.0f / std::sqrt((float)p->head_dim);
     k.attn_lse = p->attn_lse;
     k.bucket_c = k.bucket_nb = k.bucket_nblk = 0;
+    k.boundary = nullptr;
+    // boundary scores in the select mode's units: the default mode ranks by the unscaled dot
+    k.boundary_scale = p->select_mode == SA_SELECT_SUM ? 1.0f / std::sqrt((float)p->head_dim) : 1.0f;
     k.block_table = p->block_table;
     k.max_pages = p->block_table ? p->max_pages : 0;
     k.page_shift = 0;
@@ -354,14 +357,18 @@ static sa_status check_select(const sa_params *p, const void *q_sel, const float
 }
 
 sa_status sparse_attn_select(const sa_params *p, const void *q_sel, const float *k_cmp, const void *k,
-                             int32_t *idx, int32_t *n_idx, void *ws, size_t ws_bytes, void *stream)
+                             int32_t *idx, int32_t *n_idx, float *boundary_scores, void *ws, size_t ws_bytes,
+                             void *stream)
 {
     sa_status s = check_params(p);
     if (s == SA_OK)
         s = check_select(p, q_sel, k_cmp, k, idx, n_idx, ws, ws_bytes);
     if (s != SA_OK)
         return s;
+    if (boundary_scores && ((uintptr_t)boundary_scores & 3u))
+        return fail(SA_ERR_INVALID_ARG, "boundary_scores must be 4-byte aligned");
     sa::KP kp = make_kp(p);
+    kp.boundary = boundary_scores;
     return device_status(sa::launch_select(kp, p->dtype, q_sel, k_cmp, k, idx, n_idx, ws, (hipStream_t)stream,
                                            p->timing_events[0], p->timing_events[1]),
                          "select launch");

@@ -33,6 +33,10 @@ struct KP {
     // bucket selection (bucket_nb > 0): candidates are the buckets of the complete cluster
     // blocks of bucket_c tokens that end at or before p_sel, bucket_nb per block
     int bucket_c, bucket_nb, bucket_nblk;
+    // optional selection audit: [h_kv, rows, 2] fp32, each row's need-th and (need+1)-th
+    // scores (the smallest kept, the largest left out) times boundary_scale, or nullptr
+    float *boundary;
+    float boundary_scale;
 };
 
 struct Seq {
@@ -299,6 +303,12 @@ __device__ __forceinline__ uint32_t order_key(float s)
     if (u == 0x80000000u)
         u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key (a -0 score comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

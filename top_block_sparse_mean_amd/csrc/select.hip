@@ -167,6 +167,60 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
     return v;
 }
 
+// ---------------------------------------------------------------- boundary scores
+
+// The selection audit (P.boundary): per (row, KV head) the need-th largest score (the
+// smallest one kept) and the (need+1)-th (the largest one left out), from the very
+// keys the selection ranked.  Rows that keep every candidate or none have neither.
+__device__ __forceinline__ void boundary_none(const KP &P, long long row, int c)
+{
+    float *dst = P.boundary + (((long long)c * P.rows + row) << 1);
+    dst[0] = __builtin_nanf("");
+    dst[1] = __builtin_nanf("");
+}
+
+__device__ __forceinline__ void boundary_store(const KP &P, long long row, int c, uint32_t k_kept, uint32_t k_left)
+{
+    float *dst = P.boundary + (((long long)c * P.rows + row) << 1);
+    dst[0] = key_value(k_kept) * P.boundary_scale;
+    dst[1] = key_value(k_left) * P.boundary_scale;
+}
+
+// Marks key i as selected in a bit set in LDS (any lane may mark any key).
+__device__ __forceinline__ void mark_selected(uint32_t *bits, int i) { atomicOr(&bits[i >> 5], 1u << (i & 31)); }
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wavefront holding a row's n keys (key i at lane i % 64, slot i / 64), the
+// selected ones marked in `bits`: stores the smallest selected and the largest
+// unselected key (0 < need < n, so both exist).
+template <int KPL>
+__device__ __forceinline__ void wave_boundary(const KP &P, long long row, int c, const uint32_t (&key)[KPL], int n,
+                                              const uint32_t *bits)
+{
+    const int lane = lane_id();
+    uint32_t kept = 0xffffffffu, left = 0u;
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int i = m * kWave + lane;
+        if (i < n) {
+            if ((bits[i >> 5] >> (i & 31)) & 1u)
+                kept = min(kept, key[m]);
+            else
+                left = max(left, key[m]);
+        }
+    }
+    kept = wave_min_u32(kept);
+    left = wave_max_u32(left);
+    if (lane == 0)
+        boundary_store(P, row, c, kept, left);
+}
+
 // Exact selection among compacted candidates sk[0 .. c) (ascending positions), whose
 // keys all lie in [t0, kmax]: the bits above the first difference of t0 and kmax
 // are common to every candidate, so the threshold search starts below them.
@@ -807,7 +861,9 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(KP P, const float *__
 constexpr int kPartCand = 128;
 constexpr int kRowMaxCand = 1024;   // candidates of a row that the part and row plans hold
 
-__host__ __device__ inline int part_cap(int topk) { return topk < kPartCand ? topk : kPartCand; }
+// A part keeps its need + 1 best: the union of the parts' survivors then holds the row's
+// need best and its (need+1)-th (every key above that one is among the need best).
+__host__ __device__ inline int part_cap(int topk) { return topk < kPartCand ? topk + 1 : kPartCand; }
 
 template <typename T, typename KT, int D>
 __global__ __launch_bounds__(256) void select_part_kernel(KP P, const T *__restrict__ q,
@@ -859,7 +915,7 @@ __global__ __launch_bounds__(256) void select_part_kernel(KP P, const T *__restr
         const int i = m * kWave + lane;
         kr[m] = i < n ? sh_key[i] : 0u;
     }
-    const int keep = min(r.need, n);
+    const int keep = min(r.need + 1, n);
     if (keep == n) {                                     // the whole part survives
         for (int i = lane; i < n; i += kWave) {
             ws_k[slot0 + i] = sh_key[i];
@@ -883,14 +939,18 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
     __shared__ uint32_t sh_k[4][kFilterCap];
     __shared__ int sh_i[4][kFilterCap];
     __shared__ int sh_pos[4][64 * KPL];
+    __shared__ uint32_t sh_bits[4][2 * KPL];
     const long long row = (long long)blockIdx.x * 4 + threadIdx.x / kWave;
     const int c = blockIdx.y, lane = lane_id(), wv = threadIdx.x / kWave;
     if (row >= P.rows)
         return;
     RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
-    if (lane == 0)
+    if (lane == 0) {
         n_idx[(long long)c * P.rows + row] = r.need;
+        if (P.boundary && (r.need == r.n_cand || r.need == 0))
+            boundary_none(P, row, c);
+    }
     if (r.need == r.n_cand) {
         write_all(P, out, r, lane, kWave);
         return;
@@ -900,11 +960,11 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
             out[s2] = -1;
         return;
     }
-    // survivors: full parts keep m_full = min(need, kPartCand), the last part m_last
+    // survivors: full parts keep m_full = min(need + 1, kPartCand), the last part m_last
     const int cap = part_cap(P.topk);
     const int n_part_row = (r.n_cand + kPartCand - 1) / kPartCand;
-    const int m_full = min(r.need, kPartCand);
-    const int m_last = min(r.need, r.n_cand - (n_part_row - 1) * kPartCand);
+    const int m_full = min(r.need + 1, kPartCand);
+    const int m_last = min(r.need + 1, r.n_cand - (n_part_row - 1) * kPartCand);
     const int m_tot = (n_part_row - 1) * m_full + m_last;
     const long long base = ((long long)c * P.rows + row) * n_part * cap;
     uint32_t kr[KPL];
@@ -922,10 +982,24 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // the survivors are in ascending position order, so selecting among them by their
     // rank keeps the lower block index on equal scores
-    auto emit = [&](int slot, int j) { out[slot] = r.j_lo + sh_pos[wv][j]; };
+    const bool audit = P.boundary != nullptr;
+    if (audit) {
+        if (lane < 2 * KPL)
+            sh_bits[wv][lane] = 0u;
+        wave_lds_sync();
+    }
+    auto emit = [&](int slot, int j) {
+        out[slot] = r.j_lo + sh_pos[wv][j];
+        if (audit)
+            mark_selected(sh_bits[wv], j);
+    };
     wave_select<KPL>(kr, m_tot, r.need, emit, sh_k[wv], sh_i[wv]);
     for (int s2 = r.need + lane; s2 < P.topk; s2 += kWave)
         out[s2] = -1;
+    if (audit) {                                         // the (need+1)-th is a survivor
+        wave_lds_sync();
+        wave_boundary<KPL>(P, row, c, kr, m_tot, sh_bits[wv]);
+    }
 }
 
 // The need-th largest of n keys (n >= need >= 1), found by the 16 wavefronts of a
@@ -966,7 +1040,7 @@ __device__ __forceinline__ uint32_t block_threshold16(const uint32_t (&kr)[KPL],
 // selection in ascending index (keys above it, then the lowest-index keys equal to it).
 template <int KPL>
 __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, int (*sh_cnt)[16], const RowGeo &r,
-                                           int32_t *out, int32_t *n_idx_row)
+                                           int32_t *out, int32_t *n_idx_row, uint32_t *sh_bits, long long row, int c)
 {
     const int lane = lane_id(), n = r.n_cand, need = r.need;
     uint32_t kr[KPL];
@@ -980,9 +1054,23 @@ __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, 
         return;
     if (lane == 0)
         *n_idx_row = need;
-    emit_above<KPL>(kr, n, need, tau, [&](int slot, int i) { out[slot] = r.j_lo + i; });
+    const bool audit = P.boundary != nullptr;
+    if (audit) {
+        for (int x = lane; x < 2 * KPL; x += kWave)
+            sh_bits[x] = 0u;
+        wave_lds_sync();
+    }
+    emit_above<KPL>(kr, n, need, tau, [&](int slot, int i) {
+        out[slot] = r.j_lo + i;
+        if (audit)
+            mark_selected(sh_bits, i);
+    });
     for (int s2 = need + lane; s2 < P.topk; s2 += kWave)
         out[s2] = -1;
+    if (audit) {
+        wave_lds_sync();
+        wave_boundary<KPL>(P, row, c, kr, n, sh_bits);
+    }
 }
 
 // One workgroup of 16 wavefronts per (row, KV head), for batches whose rows x KV
@@ -1003,6 +1091,7 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     constexpr int GPW = kWave / L, NG = 16 * GPW;
     constexpr int U = kRowPass / NG;
     __shared__ uint32_t sh_key[kRowMaxCand];
+    __shared__ uint32_t sh_bits[kRowMaxCand / 32];
     __shared__ int sh_cnt[2][16];
     const long long row = blockIdx.x;
     const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
@@ -1028,8 +1117,11 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     };
     append();
     if (r.need == r.n_cand || r.need == 0) {
-        if (tid == 0)
+        if (tid == 0) {
             n_idx[(long long)c * P.rows + row] = r.need;
+            if (P.boundary)
+                boundary_none(P, row, c);
+        }
         if (r.need == 0)
             for (int s2 = tid; s2 < P.topk; s2 += blockDim.x)
                 out[s2] = -1;
@@ -1060,9 +1152,10 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
     }
     __syncthreads();
     if (r.n_cand <= 8 * kWave)
-        row_select<8>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row);
+        row_select<8>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row, sh_bits, row, c);
     else
-        row_select<kRowMaxCand / kWave>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row);
+        row_select<kRowMaxCand / kWave>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row, sh_bits,
+                                        row, c);
 }
 
 // ---------------------------------------------------------------- score_tile (MFMA fp32)
@@ -1778,8 +1871,67 @@ __global__ __launch_bounds__(NT) void topk_block_kernel(KP P, const uint32_t *__
 __global__ void select_empty_kernel(KP P, int32_t *__restrict__ n_idx)
 {
     long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < P.rows * P.h_kv)
+    if (i < P.rows * P.h_kv) {
         n_idx[i] = 0;
+        if (P.boundary)
+            boundary_none(P, i % P.rows, (int)(i / P.rows));
+    }
+}
+
+// Boundary scores of the plans that keep every candidate's key in the workspace: one
+// workgroup per (row, KV head) reads the row's keys and its selection (ascending,
+// kept in LDS when it fits, else searched in place) and reduces the smallest selected
+// and the largest unselected key.  Runs after the top-k, only for the audit.
+constexpr int kBoundarySel = 4096;
+
+__global__ __launch_bounds__(256) void boundary_ws_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
+                                                          const int32_t *__restrict__ idx)
+{
+    __shared__ int sh_sel[kBoundarySel];
+    __shared__ uint32_t sh_red[2][4];
+    const long long row = blockIdx.x;
+    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const RowGeo r = row_geo(P, row);
+    if (r.need == 0 || r.need == r.n_cand) {
+        if (tid == 0)
+            boundary_none(P, row, c);
+        return;
+    }
+    const int32_t *sel_g = idx + ((long long)c * P.rows + row) * P.topk;
+    const bool in_lds = r.need <= kBoundarySel;
+    if (in_lds)
+        for (int x = tid; x < r.need; x += 256)
+            sh_sel[x] = sel_g[x];
+    __syncthreads();
+    const int32_t *sel = in_lds ? sh_sel : sel_g;
+    const uint32_t *src = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
+    uint32_t kept = 0xffffffffu, left = 0u;
+    for (int i = tid; i < r.n_cand; i += 256) {
+        const int j = r.j_lo + i;
+        const uint32_t key = src[j];
+        int lo = 0, hi = r.need;                          // first selected index >= j
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sel[mid] < j)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        if (lo < r.need && sel[lo] == j)
+            kept = min(kept, key);
+        else
+            left = max(left, key);
+    }
+    kept = wave_min_u32(kept);
+    left = wave_max_u32(left);
+    if (lane == 0) {
+        sh_red[0][w] = kept;
+        sh_red[1][w] = left;
+    }
+    __syncthreads();
+    if (tid == 0)
+        boundary_store(P, row, c, min(min(sh_red[0][0], sh_red[0][1]), min(sh_red[0][2], sh_red[0][3])),
+                       max(max(sh_red[1][0], sh_red[1][1]), max(sh_red[1][2], sh_red[1][3])));
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1980,6 +2132,12 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     else
         topk_block_kernel<1024><<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(1024), 0, st>>>(
             P, wsk, stride, idx, n_idx);
+    if (P.boundary) {
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        boundary_ws_kernel<<<dim3((unsigned)P.rows, (unsigned)P.h_kv), dim3(256), 0, st>>>(P, wsk, stride, idx);
+    }
     return hipGetLastError();
 }
 

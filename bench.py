@@ -117,9 +117,8 @@ class Step:
             self.w = w
         self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
-        # the scoring kernel is timed live only where it dominates the step (each event
-        # record costs ~1.5 us of a decode step)
-        self.time_select = w.name in SELECT_DOMINANT and not buckets
+        # the kernel pass brackets the selection's scoring kernel (not with the bucket index)
+        self.time_select = not buckets
         self.index = sa.BucketIndex(self.p, w.bucket_block, w.bucket_count, w.bucket_cap) if buckets else None
         sel_b, fwd_b = sa.workspace_size(self.p)
         self.ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
@@ -219,8 +218,9 @@ def attended_total_exact(w, idx_host, n_idx_host, per_unit=False):
 
 def measured_peaks(device, prefill):
     """Achievable rates on this GPU, measured beside the published peaks: a 1 GiB
-    device-to-device copy (GB/s, bytes read + written) and, for prefill workloads,
-    8192^3 library GEMMs in bf16 and fp32 (TFLOP/s)."""
+    device-to-device copy (GB/s, bytes read + written), a 2 GiB read-only reduction
+    (GB/s read) and, for prefill workloads, 8192^3 library GEMMs in bf16 and fp32
+    (TFLOP/s)."""
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -237,7 +237,12 @@ def measured_peaks(device, prefill):
     src = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
     dst = torch.empty_like(src)
     out["copy_gbs"] = round(2 * n * 4 / timed(lambda: dst.copy_(src), 20) / 1e9, 1)
-    del src, dst
+    # read-only streaming: a full reduction of 2 GiB (bytes read; the ceiling of the
+    # read-only kernels: the decode gathers and the key scans)
+    big = torch.empty(2 * n, dtype=torch.float32, device=device).fill_(1.0)
+    acc = torch.empty((), dtype=torch.float32, device=device)
+    out["read_gbs"] = round(2 * n * 4 / timed(lambda: torch.sum(big, dim=0, out=acc), 20) / 1e9, 1)
+    del src, dst, big
     if prefill:
         m = 8192
         for name, dt in (("bf16_gemm_tflops", torch.bfloat16), ("fp32_gemm_tflops", torch.float32)):
@@ -268,7 +273,7 @@ def stage_report(w, stage_ms, attn_bytes, attn_flops, peaks, buckets=False):
             if bound == "hbm":
                 r.update(achieved=round(amount / (ms * 1e-3) / 1e9, 1), unit="GB/s",
                          frac=round(amount / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         frac_of_measured=round(amount / (ms * 1e-3) / 1e9 / peaks["copy_gbs"], 4))
+                         frac_of_measured=round(amount / (ms * 1e-3) / 1e9 / peaks["read_gbs"], 4))
             else:
                 peak, mkey = (BF16_PEAK_TFLOPS, "bf16_gemm_tflops") if bound == "mfma_bf16" else \
                              (FP32_PEAK_TFLOPS, "fp32_gemm_tflops")
@@ -549,12 +554,169 @@ def cpu_baseline(w, x, seconds=10.0):
                        f"(all heads), scaled x{scale:.1f} to the chunk")
 
 
+def bench_workload(w, args, device, peaks, headline):
+    """One workload at full size: W untimed steps, K timed steps bracketed by two events
+    (nothing else recorded inside), then a kernel pass of the same steps with events
+    around the selection's scoring kernel and the attention kernel (their launch
+    durations, on the stream they run on), a stage pass (events between the calls), and
+    the oracle on a bounded sample.  Returns the workload's figures."""
+    x = generate(w, device=device)
+    torch.cuda.synchronize()
+    if args.copy_probe_mib and headline:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=device).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    step = Step(w, x, device, page_size=args.page_size if headline else 0,
+                buckets=args.lsa_buckets and headline)
+    w = step.w
+    buckets = step.index is not None
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_begin.record()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_begin.elapsed_time(t_end) / args.steps
+
+    # kernel pass: the same steps, with events around the two kernels that read the data
+    n_k = max(1, min(args.steps, 20))
+    kev = TimingEvents(n_k, width=4)
+    for i in range(n_k):
+        step(events=kev.pairs[i])
+    torch.cuda.synchronize()
+    attn_ms = kev.mean_ms(2, 3)
+    score_ms = kev.mean_ms(0, 1) if step.time_select else None
+    kev.close()
+
+    # per-stage times, from events recorded between the three calls, in a pass of its own
+    sev = TimingEvents(n_k, width=4)
+    for i in range(n_k):
+        step(stages=(sev, sev.pairs[i]))
+    torch.cuda.synchronize()
+    stage_ms = [sev.mean_ms(0, 1), sev.mean_ms(1, 2), sev.mean_ms(2, 3)]
+    sev.close()
+
+    idx_h, n_h = step.idx.cpu().numpy(), step.n_idx.cpu().numpy()
+    a_tot = attended_total_exact(w, idx_h, n_h)
+    d = w.head_dim
+    elt = 2 if w.dtype == DTYPE_BF16 else 4
+    decode = w.name in DECODE
+    if decode:
+        a_read = attended_total_exact(w, idx_h, n_h, per_unit=True)
+        attn_bytes = a_read * 2 * d * elt + 2 * w.total_q * w.h_q * d * elt
+        roof = dict(bound="hbm", achieved=round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s")
+        roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
+        roof["measured_peak"] = peaks["read_gbs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / peaks["read_gbs"], 4)
+        value, unit, hib = ms_step * 1e3, "µs/step", False
+        flops = None
+    else:
+        G = w.group
+        flops = 4.0 * d * a_tot * G
+        # bf16 runs on the matrix cores; the fp32 path's attention runs on the vector ALU
+        peak = BF16_PEAK_TFLOPS if w.dtype == DTYPE_BF16 else FP32_PEAK_TFLOPS
+        roof = dict(bound="mfma" if w.dtype == DTYPE_BF16 else "alu",
+                    achieved=round(flops / (attn_ms * 1e-3) / 1e12, 2), peak=peak, unit="TFLOP/s")
+        roof["frac"] = round(roof["achieved"] / peak, 4)
+        if w.dtype == DTYPE_BF16:
+            roof["measured_peak"] = peaks["bf16_gemm_tflops"]
+            roof["frac_of_measured"] = round(roof["achieved"] / peaks["bf16_gemm_tflops"], 4)
+        value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
+        attn_bytes = None
+    roof = {"kernel": "sa::attn_mfma_kernel" if buckets else DOMINANT.get(w.name, "attention"), **roof}
+    sel_amount, sel_bound = select_work(w, buckets)
+    if w.name in SELECT_DOMINANT and score_ms and not buckets:
+        # the selection's scoring kernel dominates these steps: the roofline is its own,
+        # the attention kernel's figure is kept beside it
+        attn_roof = {k: v for k, v in roof.items() if k != "kernel"}
+        attn_roof["kernel"] = "sa::attn_mfma_kernel"
+        if sel_bound == "hbm":
+            ach = sel_amount / (score_ms * 1e-3) / 1e9
+            roof = dict(kernel=DOMINANT[w.name], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), measured_peak=peaks["read_gbs"],
+                        frac_of_measured=round(ach / peaks["read_gbs"], 4))
+        else:
+            ach = sel_amount / (score_ms * 1e-3) / 1e12
+            roof = dict(kernel=DOMINANT[w.name], bound="mfma", dtype="fp32", achieved=round(ach, 2),
+                        peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP32_PEAK_TFLOPS, 4),
+                        measured_peak=peaks["fp32_gemm_tflops"],
+                        frac_of_measured=round(ach / peaks["fp32_gemm_tflops"], 4))
+        roof["attention"] = attn_roof
+    roof["traffic"] = None if buckets else measured_traffic(w.name)
+
+    out = {"workload": w.name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": hib, "dtype": "bf16" if w.dtype == DTYPE_BF16 else "f32",
+           "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": d,
+                      "max_k": w.max_k, "queries": w.total_q, "block": w.block, "topk": w.topk,
+                      "n_init": w.n_init, "window": w.window,
+                      "kv_layout": f"paged{args.page_size}" if (args.page_size and headline) else "packed",
+                      "select_mode": {0: "sum", 1: "softmax", 2: "max"}[w.select_mode],
+                      "pool_overlap": w.pool_overlap, "selector": "lsa_buckets" if buckets else "blocks",
+                      **({"append": "sparse_attn_append_select (one launch for decode rows)"} if decode else {}),
+                      "parallelism": "single-gpu"},
+           "roofline": roof, "attn_kernel_ms": round(attn_ms, 5)}
+    if score_ms:
+        out["score_kernel_ms"] = round(score_ms, 5)
+    if decode and score_ms and sel_bound == "hbm":
+        # the two kernels that read the step's data, by their launch durations
+        tot = sel_amount + attn_bytes
+        ach = tot / ((score_ms + attn_ms) * 1e-3) / 1e9
+        out["select_plus_attn"] = {"bytes": int(tot), "kernel_ms": round(score_ms + attn_ms, 5), "bound": "hbm",
+                                   "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                   "frac_of_measured": round(ach / peaks["read_gbs"], 4)}
+    out["attn_algorithmic_bytes"] = attn_bytes
+    out["attended_tokens"] = a_tot
+    out["wall_s"] = round(wall, 4)
+    if w.name == "bf16_decode_32k":
+        hits = tot = 0
+        for b in range(w.batch):
+            for c in range(w.h_kv):
+                hb = hot_blocks(w, b, c)
+                sel = set(idx_h[c, b, :n_h[c, b]].tolist())
+                hits += sum(1 for j in hb if j in sel)
+                tot += len(hb)
+        out["hot_block_recall"] = round(hits / max(tot, 1), 4)
+    if w.structure == "needles":
+        out["needle_recall"] = needle_recall(w, idx_h, n_h)
+    if w.name == "bf16_draft_decode":
+        out["us_per_draft_token"] = round(ms_step * 1e3 / w.seqlens_q[0], 3)
+    out["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks, buckets=buckets)
+    if args.s3r_refresh and w.shared_selection and headline:
+        r = s3r_refresh(w, step, min(args.steps, 20), device)
+        r["round_us"] = round(ms_step * 1e3 + (r["verify_ms"] + r["refresh_ms"]) * 1e3, 2)
+        out["s3r"] = r
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, seconds=args.cpu_seconds)
+    del step, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# The metric is quoted on the decode step (the line's value) and the prefill rates; the
+# draft round is the other decode-shaped workload.  The tiny fp32 workload is a parity case.
+SECONDARY = ("bf16_prefill_128k", "bf16_chunked_prefill_1m", "bf16_draft_decode")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="bf16_decode_32k", choices=sorted(FULL))
+    ap.add_argument("--workload", default=None, choices=sorted(FULL),
+                    help="run this workload alone (default: the decode step as the line's value, with the "
+                         "128K prefill, the 1M-token chunk and the draft round beside it)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep K and V in a paged cache of this many tokens per page (0: packed)")
     ap.add_argument("--select-mode", choices=["sum", "softmax", "max"], default="sum",
@@ -578,6 +740,8 @@ def main():
                          "directories of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
     args = ap.parse_args()
     if args.record_counters:
+        if args.workload is None:
+            raise SystemExit("--record-counters needs --workload")
         cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d $REPO/{d} -o run "
                "-- python3 $REPO/bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline "
                "--copy-probe-mib 1024")
@@ -592,151 +756,39 @@ def main():
 
     device = "cuda"
     torch.cuda.set_device(0)
-    w = FULL[args.workload]().scaled(select_mode={"sum": 0, "softmax": 1, "max": 2}[args.select_mode],
-                                     pool_overlap=args.pool_overlap)
-    x = generate(w, device=device)
-    torch.cuda.synchronize()
-    if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=device).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    step = Step(w, x, device, page_size=args.page_size, buckets=args.lsa_buckets)
-    w = step.w
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    tev = TimingEvents(args.steps, width=4)
-    evs = tev.pairs
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_begin.record()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events=evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_begin.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    attn_ms = tev.mean_ms(2, 3)
-    score_ms = tev.mean_ms(0, 1) if step.time_select else None
-    tev.close()
-
-    # per-stage times, from events recorded between the three calls, in a pass of its own
-    n_st = min(args.steps, 20)
-    sev = TimingEvents(n_st, width=4)
-    for i in range(n_st):
-        step(stages=(sev, sev.pairs[i]))
-    torch.cuda.synchronize()
-    stage_ms = [sev.mean_ms(0, 1), sev.mean_ms(1, 2), sev.mean_ms(2, 3)]
-    sev.close()
-    peaks = measured_peaks(device, prefill=w.name not in DECODE)
-
-    idx_h, n_h = step.idx.cpu().numpy(), step.n_idx.cpu().numpy()
-    a_tot = attended_total_exact(w, idx_h, n_h)
-    d = w.head_dim
-    elt = 2 if w.dtype == DTYPE_BF16 else 4
-    decode = w.name in DECODE
-    if decode:
-        a_read = attended_total_exact(w, idx_h, n_h, per_unit=True)
-        attn_bytes = a_read * 2 * d * elt + 2 * w.total_q * w.h_q * d * elt
-        roof = dict(bound="hbm", achieved=round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s")
-        roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
-        roof["measured_peak"] = peaks["copy_gbs"]
-        roof["frac_of_measured"] = round(roof["achieved"] / peaks["copy_gbs"], 4)
-        value, unit, hib = ms_step * 1e3, "µs/step", False
-        flops = None
-    else:
-        G = w.group
-        flops = 4.0 * d * a_tot * G
-        # bf16 runs on the matrix cores; the fp32 path's attention runs on the vector ALU
-        peak = BF16_PEAK_TFLOPS if w.dtype == DTYPE_BF16 else FP32_PEAK_TFLOPS
-        roof = dict(bound="mfma" if w.dtype == DTYPE_BF16 else "alu",
-                    achieved=round(flops / (attn_ms * 1e-3) / 1e12, 2), peak=peak, unit="TFLOP/s")
-        roof["frac"] = round(roof["achieved"] / peak, 4)
-        if w.dtype == DTYPE_BF16:
-            roof["measured_peak"] = peaks["bf16_gemm_tflops"]
-            roof["frac_of_measured"] = round(roof["achieved"] / peaks["bf16_gemm_tflops"], 4)
-        value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
-        attn_bytes = None
-    roof = {"kernel": "sa::attn_mfma_kernel" if args.lsa_buckets else DOMINANT.get(w.name, "attention"), **roof}
-    if w.name in SELECT_DOMINANT and score_ms:
-        # the selection's scoring kernel dominates these steps: the roofline is its own,
-        # the attention kernel's figure is kept beside it
-        amount, bound = select_work(w)
-        attn_roof = {k: v for k, v in roof.items() if k != "kernel"}
-        attn_roof["kernel"] = "sa::attn_mfma_kernel"
-        if bound == "hbm":
-            ach = amount / (score_ms * 1e-3) / 1e9
-            roof = dict(kernel=DOMINANT[w.name], bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
-                        unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), measured_peak=peaks["copy_gbs"],
-                        frac_of_measured=round(ach / peaks["copy_gbs"], 4))
-        else:
-            ach = amount / (score_ms * 1e-3) / 1e12
-            roof = dict(kernel=DOMINANT[w.name], bound="mfma", dtype="fp32", achieved=round(ach, 2),
-                        peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP32_PEAK_TFLOPS, 4),
-                        measured_peak=peaks["fp32_gemm_tflops"],
-                        frac_of_measured=round(ach / peaks["fp32_gemm_tflops"], 4))
-        roof["attention"] = attn_roof
-    roof["traffic"] = measured_traffic(w.name)
-
-    extra = {}
-    if w.name == "bf16_decode_32k":
-        hits = tot = 0
-        for b in range(w.batch):
-            for c in range(w.h_kv):
-                hb = hot_blocks(w, b, c)
-                sel = set(idx_h[c, b, :n_h[c, b]].tolist())
-                hits += sum(1 for j in hb if j in sel)
-                tot += len(hb)
-        extra["hot_block_recall"] = round(hits / max(tot, 1), 4)
-    if w.structure == "needles":
-        extra["needle_recall"] = needle_recall(w, idx_h, n_h)
-    if w.name == "bf16_draft_decode":
-        extra["us_per_draft_token"] = round(ms_step * 1e3 / w.seqlens_q[0], 3)
-    extra["stages"] = stage_report(w, stage_ms, attn_bytes, flops, peaks, buckets=args.lsa_buckets)
-    if args.s3r_refresh and w.shared_selection:
-        r = s3r_refresh(w, step, min(args.steps, 20), device)
-        r["round_us"] = round(ms_step * 1e3 + (r["verify_ms"] + r["refresh_ms"]) * 1e3, 2)
-        extra["s3r"] = r
-    extra["measured_peaks"] = peaks
-
+    name = args.workload or "bf16_decode_32k"
+    others = [] if args.workload else list(SECONDARY)
+    peaks = measured_peaks(device, prefill=True)
+    w = FULL[name]().scaled(select_mode={"sum": 0, "softmax": 1, "max": 2}[args.select_mode],
+                            pool_overlap=args.pool_overlap)
+    head = bench_workload(w, args, device, peaks, headline=True)
+    print(f"# {name}: {head['value']} {head['unit']}", file=sys.stderr, flush=True)
     res = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": hib,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": head["higher_is_better"],
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == DTYPE_BF16 else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": d,
-                   "max_k": w.max_k, "queries": w.total_q, "block": w.block, "topk": w.topk,
-                   "n_init": w.n_init, "window": w.window, "kv_layout": (f"paged{args.page_size}" if args.page_size
-                                                                          else "packed"),
-                   "select_mode": args.select_mode, "pool_overlap": w.pool_overlap,
-                   "selector": "lsa_buckets" if args.lsa_buckets else "blocks",
-                   **({"append": "sparse_attn_append_select (one launch for decode rows)"} if decode else {}),
-                   "parallelism": "single-gpu"},
-        "roofline": roof,
-        "attn_kernel_ms": round(attn_ms, 5),
-        **({"score_kernel_ms": round(score_ms, 5)} if score_ms else {}),
-        "attn_algorithmic_bytes": attn_bytes,
-        "attended_tokens": a_tot,
-        "wall_s": round(wall, 4),
-        **extra,
+        **{k: v for k, v in head.items() if k not in ("workload", "value", "unit", "ms_per_step",
+                                                       "higher_is_better", "dtype")},
+        "measured_peaks": peaks,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x, seconds=args.cpu_seconds)
+    prefill, other = {}, {}
+    for o in others:
+        r = bench_workload(FULL[o](), args, device, peaks, headline=False)
+        print(f"# {o}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
+        (prefill if r["unit"] == "tok/s" else other)[o] = r
+    if prefill:
+        res["prefill"] = prefill
+    if other:
+        res["other_decode"] = other
     print(json.dumps(res), flush=True)
 
 

@@ -162,8 +162,9 @@ typedef struct sa_bucket_index {
 /* SPARSE_ATTN_ABI_VERSION of the built library. */
 int sparse_attn_abi_version(void);
 
-/* Static description of a status code; never NULL. */
-const char *sparse_attn_status_string(sa_status s);
+/* Static description of a status code (an sa_status value; any other value reads
+ * "unknown status"); never NULL. */
+const char *sparse_attn_status_string(int status);
 
 /* Detail of the calling thread's last non-OK status ("" if none); never NULL. */
 const char *sparse_attn_last_error(void);

@@ -69,6 +69,14 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(_lib.lib(), s)
 
 
+def test_every_export_has_a_c_signature():
+    """Each entry point's argument types are declared to ctypes: without them Python ints
+    travel as 32-bit C ints, and a size_t argument such as a workspace size would carry
+    whatever the upper half of its register held."""
+    L = _lib.lib()
+    assert [n for n in _lib.EXPORTS if getattr(L, n).argtypes is None] == []
+
+
 def test_status_strings():
     L = _lib.lib()
     names = [L.sparse_attn_status_string(i).decode() for i in range(5)]

@@ -1,6 +1,9 @@
 """ctypes view of libsparse_attn.so (the C ABI in include/sparse_attn.h).
 
 The library is loaded from this package directory only; there is no fallback.
+SPARSE_ATTN_LIB names another build of the same library to load instead (the tests
+use it for a build whose host code carries address and undefined-behaviour checks);
+it must exist too.
 """
 from __future__ import annotations
 
@@ -8,7 +11,7 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsparse_attn.so")
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(PKG, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(5)
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
@@ -89,6 +92,8 @@ def lib():
         P = ctypes.POINTER(SaParams)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.sparse_attn_abi_version.restype = ctypes.c_int
+        L.sparse_attn_abi_version.argtypes = []
+        L.sparse_attn_last_error.argtypes = []
         L.sparse_attn_status_string.restype = ctypes.c_char_p
         L.sparse_attn_status_string.argtypes = [ctypes.c_int]
         L.sparse_attn_last_error.restype = ctypes.c_char_p
@@ -100,6 +105,11 @@ def lib():
         L.sparse_attn_append_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sparse_attn_append_kv.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        BX = ctypes.POINTER(SaBucketIndex)
+        L.sparse_attn_bucket_build.argtypes = [P, vp, BX, vp]
+        L.sparse_attn_bucket_workspace_size.argtypes = [P, BX, ctypes.c_int32, ctypes.POINTER(sz)]
+        L.sparse_attn_bucket_select.argtypes = [P, vp, BX, ctypes.c_int32, vp, vp, vp, sz, vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L

@@ -24,33 +24,53 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Host-side address and undefined-behaviour checks for a test build (each flag applies to
+# the host pass only; the GPU code is built as usual).  Load such a library with the
+# compiler's address-sanitizer runtime preloaded and SPARSE_ATTN_LIB pointing at it.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def sanitizer_runtime() -> str:
+    """The address-sanitizer runtime of the compiler hipcc drives (to preload)."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return hits[-1]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False, out: str = OUT, build_dir: str = BUILD) -> str:
+    """Compile every source for gfx950 and link the library at `out`.  sanitize: host code
+    with address and undefined-behaviour checks (a test build; see SANITIZE)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    extra = SANITIZE if sanitize else []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"] \
+        if sanitize else []
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(OUT)
-    return OUT
+        print(out)
+    return out
 
 
 if __name__ == "__main__":

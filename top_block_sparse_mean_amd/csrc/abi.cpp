@@ -159,9 +159,9 @@ extern "C" {
 
 int sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 
-const char *sparse_attn_status_string(sa_status s)
+const char *sparse_attn_status_string(int status)
 {
-    switch (s) {
+    switch (status) {
     case SA_OK: return "ok";
     case SA_ERR_INVALID_ARG: return "invalid argument";
     case SA_ERR_UNSUPPORTED: return "unsupported configuration";

@@ -117,12 +117,17 @@ class Step:
             self.w = w
         self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
-        # the kernel pass brackets the selection's scoring kernel (not with the bucket index)
-        self.time_select = not buckets
+        # decode rows: the step is one sparse_attn_decode_step call (append, select and
+        # attend in one launch); the kernel pass brackets that launch
+        self.fused_step = self.decode and not w.shared_selection and w.block > 1 and not buckets
+        # the kernel pass brackets the selection's scoring kernel (not with the bucket
+        # index, nor when the step is one launch)
+        self.time_select = not buckets and not self.fused_step
         self.index = sa.BucketIndex(self.p, w.bucket_block, w.bucket_count, w.bucket_cap) if buckets else None
         sel_b, fwd_b = sa.workspace_size(self.p)
         self.ws_sel = torch.empty(max(sel_b, 16), dtype=torch.uint8, device=device)
         self.ws_fwd = torch.empty(max(fwd_b, 16), dtype=torch.uint8, device=device)
+        self.ws_step = self.ws_sel if sel_b >= fwd_b else self.ws_fwd
         self.k_cmp = torch.empty((w.h_kv, w.batch, self.p.nb_max, w.head_dim), dtype=torch.float32,
                                  device=device) if w.block > 1 else None
         self.idx = torch.empty((w.h_kv, self.p.rows, max(w.topk, 1)), dtype=torch.int32, device=device)
@@ -154,8 +159,10 @@ class Step:
 
     def __call__(self, events=None, stages=None):
         """events: four events, recorded around the selection's scoring kernel ([0], [1])
-        and the main attention kernel ([2], [3]).  stages: (TimingEvents, four events)
-        recorded before compress, after compress, after select and after fwd."""
+        and the main attention kernel ([2], [3]) -- around the one launch ([2], [3]) of a
+        fused decode step.  stages: (TimingEvents, four events) recorded before compress,
+        after compress, after select and after fwd (a decode step then runs as the three
+        calls it fuses)."""
         x = self.x
         mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
         mark(0)
@@ -169,6 +176,10 @@ class Step:
             if self.index is not None:      # the chunk's new cluster blocks; earlier ones are frozen
                 sa.bucket_build(self.p, self.k_cmp, self.index, build_from=self.build_from)
         mark(1)
+        if joined and self.fused_step:
+            sa.decode_step(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp, x["q"], self.idx, self.n_idx,
+                           out=self.out, ws=self.ws_step, events=None if events is None else events[2:4])
+            return
         if self.index is not None:
             sa.bucket_select(self.p, x["q"], self.index, self.w.bucket_topk, self.idx, self.n_idx, ws=self.ws_bkt)
         elif joined:
@@ -237,12 +248,14 @@ def measured_peaks(device, prefill):
     src = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
     dst = torch.empty_like(src)
     out["copy_gbs"] = round(2 * n * 4 / timed(lambda: dst.copy_(src), 20) / 1e9, 1)
-    # read-only streaming: a full reduction of 2 GiB (bytes read; the ceiling of the
-    # read-only kernels: the decode gathers and the key scans)
-    big = torch.empty(2 * n, dtype=torch.float32, device=device).fill_(1.0)
-    acc = torch.empty((), dtype=torch.float32, device=device)
-    out["read_gbs"] = round(2 * n * 4 / timed(lambda: torch.sum(big, dim=0, out=acc), 20) / 1e9, 1)
-    del src, dst, big
+    # read-only streaming: row sums of a 2 GiB [.., 4096] fp32 matrix (bytes read; the
+    # ceiling of the read-only kernels: the decode gathers and the key scans).  Of the
+    # library reductions tried this one reads fastest (a full reduction to one value
+    # reached only ~4 TB/s)
+    big = torch.empty((2 * n // 4096, 4096), dtype=torch.float32, device=device).fill_(1.0)
+    acc = torch.empty(big.shape[0], dtype=torch.float32, device=device)
+    out["read_gbs"] = round(2 * n * 4 / timed(lambda: torch.sum(big, dim=1, out=acc), 20) / 1e9, 1)
+    del src, dst, big, acc
     if prefill:
         m = 8192
         for name, dt in (("bf16_gemm_tflops", torch.bfloat16), ("fp32_gemm_tflops", torch.float32)):
@@ -341,13 +354,15 @@ CSRC = "top_block_sparse_mean_amd/csrc/"
 KERNEL_SOURCES = {
     "sa::attn_mfma_kernel": [CSRC + "attn_decode.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
                              CSRC + "sa_internal.hpp"],
+    "sa::decode_step_kernel": [CSRC + "select.hip", CSRC + "append_common.hpp", CSRC + "mfma_common.hpp",
+                               CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
     "sa::attn_wg_kernel": [CSRC + "attn_prefill.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
                            CSRC + "sa_internal.hpp"],
     "sa::score_rows_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
     "sa::score_tile_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
     "sa::attn_valu_kernel": [CSRC + "attn.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
 }
-DOMINANT = {"bf16_decode_32k": "sa::attn_mfma_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel",
+DOMINANT = {"bf16_decode_32k": "sa::decode_step_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel",
             "bf16_draft_decode": "sa::score_rows_kernel", "bf16_chunked_prefill_1m": "sa::score_tile_kernel",
             "tiny_fp32_prefill": "sa::attn_valu_kernel"}
 # workloads whose step is dominated by the selection's scoring kernel (rocprofv3 kernel stats)
@@ -611,14 +626,18 @@ def bench_workload(w, args, device, peaks, headline):
     d = w.head_dim
     elt = 2 if w.dtype == DTYPE_BF16 else 4
     decode = w.name in DECODE
+    sel_amount, sel_bound = select_work(w, buckets)
     if decode:
         a_read = attended_total_exact(w, idx_h, n_h, per_unit=True)
         attn_bytes = a_read * 2 * d * elt + 2 * w.total_q * w.h_q * d * elt
-        roof = dict(bound="hbm", achieved=round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
+        # one launch per step: its bytes are the pooled keys and the gathered K/V together
+        roof_bytes = attn_bytes + (sel_amount if step.fused_step else 0)
+        roof = dict(bound="hbm", achieved=round(roof_bytes / (attn_ms * 1e-3) / 1e9, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s")
         roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
         roof["measured_peak"] = peaks["read_gbs"]
         roof["frac_of_measured"] = round(roof["achieved"] / peaks["read_gbs"], 4)
+        roof["algorithmic_bytes"] = int(roof_bytes)
         value, unit, hib = ms_step * 1e3, "µs/step", False
         flops = None
     else:
@@ -634,8 +653,9 @@ def bench_workload(w, args, device, peaks, headline):
             roof["frac_of_measured"] = round(roof["achieved"] / peaks["bf16_gemm_tflops"], 4)
         value, unit, hib = w.total_q / (ms_step * 1e-3), "tok/s", True
         attn_bytes = None
-    roof = {"kernel": "sa::attn_mfma_kernel" if buckets else DOMINANT.get(w.name, "attention"), **roof}
-    sel_amount, sel_bound = select_work(w, buckets)
+    kname = "sa::attn_mfma_kernel" if (buckets or (decode and not step.fused_step)) else \
+        DOMINANT.get(w.name, "attention")
+    roof = {"kernel": kname, **roof}
     if w.name in SELECT_DOMINANT and score_ms and not buckets:
         # the selection's scoring kernel dominates these steps: the roofline is its own,
         # the attention kernel's figure is kept beside it
@@ -665,10 +685,17 @@ def bench_workload(w, args, device, peaks, headline):
                       "pool_overlap": w.pool_overlap, "selector": "lsa_buckets" if buckets else "blocks",
                       **({"append": "sparse_attn_append_select (one launch for decode rows)"} if decode else {}),
                       "parallelism": "single-gpu"},
-           "roofline": roof, "attn_kernel_ms": round(attn_ms, 5)}
+           "roofline": roof}
+    out["step_kernel_ms" if step.fused_step else "attn_kernel_ms"] = round(attn_ms, 5)
     if score_ms:
         out["score_kernel_ms"] = round(score_ms, 5)
-    if decode and score_ms and sel_bound == "hbm":
+    if step.fused_step:
+        # the step's one launch reads the pooled keys and the gathered K/V
+        out["select_plus_attn"] = {"bytes": int(sel_amount + attn_bytes), "kernel_ms": round(attn_ms, 5),
+                                   "kernel": "sa::decode_step_kernel", "bound": "hbm",
+                                   "achieved": roof["achieved"], "unit": "GB/s", "frac": roof["frac"],
+                                   "frac_of_measured": roof["frac_of_measured"]}
+    elif decode and score_ms and sel_bound == "hbm":
         # the two kernels that read the step's data, by their launch durations
         tot = sel_amount + attn_bytes
         ach = tot / ((score_ms + attn_ms) * 1e-3) / 1e9

@@ -299,6 +299,23 @@ sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, cons
                           const int32_t *idx, const int32_t *n_idx, void *out, float *lse,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* One decode step: the same results as sparse_attn_append_kv(p, k_new, v_new, k, v,
+ * k_cmp), then sparse_attn_select(p, q, k_cmp, k, idx, n_idx, NULL, ...), then
+ * sparse_attn_fwd(p, q, k, v, idx, n_idx, out, lse, ...) -- the selector query is the
+ * attention query.  For bf16 decode rows (one query per sequence, block > 1 with k_cmp,
+ * window >= block, the default group score, G <= 8, a batch whose rows x KV heads fill
+ * the GPU, attended sets of at most 8192 tokens) one launch does all three: the
+ * workgroup of a (sequence, KV head) appends, selects and then attends with its
+ * selection kept in LDS (the selection equals the separate calls' bit for bit; the
+ * output and lse agree with sparse_attn_fwd's to fp32 rounding of a different
+ * summation order).  Otherwise the three calls run in turn.  idx and n_idx are
+ * written either way.  ws: at least the larger of select_bytes and fwd_bytes
+ * (sparse_attn_workspace_size), or none when the step runs in one launch.
+ * timing_events bracket the one launch, or the attention kernel otherwise. */
+sa_status sparse_attn_decode_step(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
+                                  float *k_cmp, const void *q, int32_t *idx, int32_t *n_idx, void *out,
+                                  float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* sparse_attn_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same kernels and results, with the split partials kept in a fixed 32 MiB

@@ -29,7 +29,7 @@ from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM
                    SaParams, SparseAttnError, check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select",
-           "append_select", "fwd", "fwd_noalloc", "BucketIndex", "bucket_build", "bucket_select",
+           "append_select", "fwd", "fwd_noalloc", "decode_step", "BucketIndex", "bucket_build", "bucket_select",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
            "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
 
@@ -235,6 +235,35 @@ def fwd(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch
         _set_events(p, None)
     check("sparse_attn_fwd", st)
     return (out, lse) if want_lse else out
+
+
+def decode_step(p: Params, k_new: torch.Tensor, v_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                k_cmp: Optional[torch.Tensor], q: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                n_idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = False, ws: Optional[torch.Tensor] = None,
+                stream=None, events=None):
+    """append_kv, select (q as the selector query) and fwd of one decode step, in one launch
+    where the step fits it.  Returns (out, idx, n_idx) or, with want_lse, (out, lse, idx, n_idx)."""
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((p.s.h_kv, p.rows, max(p.s.topk, 1)), dtype=torch.int32, device=dev)
+    if n_idx is None:
+        n_idx = torch.empty((p.s.h_kv, p.rows), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((p.s.h_q, p.s.total_q), dtype=torch.float32, device=dev)
+    sel_b, fwd_b = workspace_size(p)
+    ws, nbytes = _ws(max(sel_b, fwd_b), dev, ws)
+    _set_events(p, events)
+    try:
+        st = lib().sparse_attn_decode_step(p.ref(), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v), _ptr(k_cmp),
+                                           _ptr(q), _ptr(idx), _ptr(n_idx), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+                                           _stream(stream))
+    finally:
+        _set_events(p, None)
+    check("sparse_attn_decode_step", st)
+    return (out, lse, idx, n_idx) if want_lse else (out, idx, n_idx)
 
 
 def fwd_noalloc(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,

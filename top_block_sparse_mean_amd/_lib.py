@@ -23,7 +23,7 @@ EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
            "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_append_select",
            "sparse_attn_fwd", "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select",
-           "sparse_attn_fwd_noalloc")
+           "sparse_attn_fwd_noalloc", "sparse_attn_decode_step")
 
 
 class SaParams(ctypes.Structure):
@@ -106,6 +106,7 @@ def lib():
         L.sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sparse_attn_append_kv.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.sparse_attn_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         BX = ctypes.POINTER(SaBucketIndex)
         L.sparse_attn_bucket_build.argtypes = [P, vp, BX, vp]
         L.sparse_attn_bucket_workspace_size.argtypes = [P, BX, ctypes.c_int32, ctypes.POINTER(sz)]

@@ -426,6 +426,39 @@ sa_status sparse_attn_fwd(const sa_params *p, const void *q, const void *k, cons
                          "fwd launch");
 }
 
+sa_status sparse_attn_decode_step(const sa_params *p, const void *k_new, const void *v_new, void *k, void *v,
+                                  float *k_cmp, const void *q, int32_t *idx, int32_t *n_idx, void *out, float *lse,
+                                  void *ws, size_t ws_bytes, void *stream)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK)
+        return s;
+    if (!k_new || !v_new || !k || !v || !q || !out || !n_idx || (!idx && p->topk > 0))
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k, v, q, out, idx and n_idx are required");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(v) || !aligned16(q) ||
+        !aligned16(out) || (k_cmp && !aligned16(k_cmp)))
+        return fail(SA_ERR_INVALID_ARG, "k_new, v_new, k, v, q, out and k_cmp must be 16-byte aligned");
+    if (p->select_mode == SA_SELECT_ATTN)
+        return fail(SA_ERR_INVALID_ARG, "SA_SELECT_ATTN selects from a verify pass: use sparse_attn_select");
+    if (p->block > 1 && !k_cmp)
+        return fail(SA_ERR_INVALID_ARG, "block > 1 scores pooled keys: k_cmp is required");
+    sa::KP kp = make_kp(p);
+    const int splits = sa::fwd_splits(kp);
+    size_t need = 0;
+    if (!sa::decode_step_fused_ok(kp, p->dtype, k_cmp != nullptr)) {
+        const size_t sb = sa::select_workspace_bytes(kp, sa::select_plan(kp));
+        const size_t fb = sa::fwd_workspace_bytes(kp, splits);
+        need = sb > fb ? sb : fb;
+    }
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SA_ERR_WORKSPACE, "decode_step needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    return device_status(sa::launch_decode_step(kp, p->dtype, k_new, v_new, k, v, k_cmp, q, idx, n_idx, out, lse,
+                                                ws, splits, (hipStream_t)stream, p->timing_events[0],
+                                                p->timing_events[1]),
+                         "decode_step launch");
+}
+
 sa_status sparse_attn_fwd_noalloc(const sa_params *p, const void *q, const void *k, const void *v,
                                   const int32_t *idx, const int32_t *n_idx, void *out, float *lse, void *stream)
 {

@@ -61,6 +61,12 @@ hipError_t launch_fwd(const KP &P, int dtype, const void *q, const void *k, cons
                       const int32_t *n_idx, void *out, float *lse, void *ws, int splits, void *ev_begin,
                       void *ev_end, hipStream_t st);
 
+// A decode step (append, select, attend) in one launch where it fits, else the three.
+bool decode_step_fused_ok(const KP &P, int dtype, bool have_k_cmp);
+hipError_t launch_decode_step(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
+                              float *k_cmp, const void *q, int32_t *idx, int32_t *n_idx, void *out, float *lse,
+                              void *ws, int fwd_splits_n, hipStream_t st, void *ev0, void *ev1);
+
 // Fixed device scratch of sparse_attn_fwd_noalloc (one array per device).
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 hipError_t noalloc_scratch(void **ptr);

@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "append_common.hpp"
+#include "mfma_common.hpp"
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
@@ -1010,19 +1011,24 @@ __global__ __launch_bounds__(256) void select_merge_kernel(KP P, const uint32_t 
 // round) and every wavefront takes the largest digit whose count still reaches
 // need.  A count of exactly need ends the search early: the keys at or above the
 // returned value are then exactly the need largest.
-template <int KPL>
+template <int KPL, int NW = 16>
 __device__ __forceinline__ uint32_t block_threshold16(const uint32_t (&kr)[KPL], int n, int need, uint32_t tau,
                                                       int shift, int (*sh_cnt)[16])
 {
+    static_assert(16 % NW == 0, "wavefronts must divide the 16 digits of a round");
     const int lane = lane_id(), w = threadIdx.x / kWave;
     for (int rd = 0; shift >= 0; rd++, shift -= 4) {
-        const uint32_t cand = tau | ((uint32_t)w << shift);
-        int cnt = 0;
+        // with NW < 16 wavefronts, wavefront w counts digits w, w + NW, ...
 #pragma unroll
-        for (int m = 0; m < KPL; m++)
-            cnt += __popcll(__ballot(m * kWave + lane < n && kr[m] >= cand));
-        if (lane == 0)
-            sh_cnt[rd & 1][w] = cnt;
+        for (int j = 0; j < 16 / NW; j++) {
+            const uint32_t cand = tau | ((uint32_t)(w + j * NW) << shift);
+            int cnt = 0;
+#pragma unroll
+            for (int m = 0; m < KPL; m++)
+                cnt += __popcll(__ballot(m * kWave + lane < n && kr[m] >= cand));
+            if (lane == 0)
+                sh_cnt[rd & 1][w + j * NW] = cnt;
+        }
         __syncthreads();
         const int cl = sh_cnt[rd & 1][lane & 15];
         // digit 0 keeps tau itself, which always has >= need keys at or above it
@@ -1038,9 +1044,10 @@ __device__ __forceinline__ uint32_t block_threshold16(const uint32_t (&kr)[KPL],
 // Selection among a row's n <= 64 * KPL keys in LDS by the 16 wavefronts of a
 // workgroup: the threshold by block_threshold16, then wavefront 0 emits the
 // selection in ascending index (keys above it, then the lowest-index keys equal to it).
-template <int KPL>
+template <int KPL, int NW = 16>
 __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, int (*sh_cnt)[16], const RowGeo &r,
-                                           int32_t *out, int32_t *n_idx_row, uint32_t *sh_bits, long long row, int c)
+                                           int32_t *out, int32_t *n_idx_row, uint32_t *sh_bits, long long row, int c,
+                                           int *lds_sel)
 {
     const int lane = lane_id(), n = r.n_cand, need = r.need;
     uint32_t kr[KPL];
@@ -1049,7 +1056,7 @@ __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, 
         const int i = m * kWave + lane;
         kr[m] = i < n ? sh_key[i] : 0u;
     }
-    const uint32_t tau = block_threshold16<KPL>(kr, n, need, 0u, 28, sh_cnt);
+    const uint32_t tau = block_threshold16<KPL, NW>(kr, n, need, 0u, 28, sh_cnt);
     if (threadIdx.x >= kWave)
         return;
     if (lane == 0)
@@ -1062,6 +1069,8 @@ __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, 
     }
     emit_above<KPL>(kr, n, need, tau, [&](int slot, int i) {
         out[slot] = r.j_lo + i;
+        if (lds_sel)
+            lds_sel[slot] = r.j_lo + i;
         if (audit)
             mark_selected(sh_bits, i);
     });
@@ -1078,29 +1087,40 @@ __device__ __forceinline__ void row_select(const KP &P, const uint32_t *sh_key, 
 // passes of kRowPass (U rounds of 16 x GPW key rows, all loads of a pass issued
 // before any is reduced), then wavefront 0 selects the row's need best.  Same
 // per-candidate arithmetic as select_part; no workspace and one launch instead of
-// part + merge.  grid: (rows, h_kv).
+// part + merge.  grid: rows x h_kv, the KV head fastest.
 constexpr int kRowPass = 512;
 
-template <typename T, typename KT, int D>
-__global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
-                                                          const KT *__restrict__ kbase, int32_t *__restrict__ idx,
-                                                          int32_t *__restrict__ n_idx, SelAppend app)
+// The row plan's work for (row, KV head c), called by all NW * 64 threads of the
+// workgroup: the step's append for the row's sequence (app.n_blk > 0), the row's
+// candidates scored into sh_key, the selection written to idx / n_idx (and to
+// lds_sel, in ascending order, when given), the audit when asked.  before_search()
+// runs on every thread once the keys are scored (after the append and a barrier),
+// before the threshold search, when the row ranks its candidates.  Returns the
+// row's selection count.  The threads return from it at different points: a
+// caller that goes on must meet at a barrier first.
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+template <typename T, typename KT, int D, int NW = 16, typename Hook = NoHook>
+__device__ __forceinline__ int row_plan_select(const KP &P, const T *__restrict__ q, const KT *__restrict__ kbase,
+                                               int32_t *__restrict__ idx, int32_t *__restrict__ n_idx,
+                                               const SelAppend &app, long long row, int c, uint32_t *sh_key,
+                                               uint32_t *sh_bits, int (*sh_cnt)[16], int *lds_sel,
+                                               Hook before_search = Hook())
 {
     using RD = RowDot<KT, D>;
     constexpr int L = RD::L, VPL = RD::VPL;
-    constexpr int GPW = kWave / L, NG = 16 * GPW;
+    constexpr int GPW = kWave / L, NG = NW * GPW;
     constexpr int U = kRowPass / NG;
-    __shared__ uint32_t sh_key[kRowMaxCand];
-    __shared__ uint32_t sh_bits[kRowMaxCand / 32];
-    __shared__ int sh_cnt[2][16];
-    const long long row = blockIdx.x;
-    const int c = blockIdx.y, tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
+    const int tid = threadIdx.x, lane = lane_id(), sub = lane % L, grp = (tid / kWave) * GPW + lane / L;
     RowGeo r = row_geo(P, row);
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     // the step's append for this row's sequence and KV head (one query per sequence):
     // its new token's rows and the blocks whose pooling window holds it, none of which
     // is a candidate of the row (the launcher checks window >= block).  It runs first:
-    // beside the key loads in flight its registers would spill.
+    // run beside the key loads in flight, its registers spill (with 16 wavefronts) or
+    // it costs more than it hides (8 wavefronts of the decode step: 82.6 against 75.8 us).
     auto append = [&]() {
         if (app.n_blk == 0)
             return;
@@ -1127,7 +1147,10 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
                 out[s2] = -1;
         else
             write_all(P, out, r, tid, blockDim.x);
-        return;
+        if (lds_sel)
+            for (int s2 = tid; s2 < r.need; s2 += blockDim.x)
+                lds_sel[s2] = r.j_lo + s2;
+        return r.need;
     }
     float qv[VPL];
     SelBuf<T, VPL> sb;
@@ -1151,11 +1174,176 @@ __global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restr
         }
     }
     __syncthreads();
+    before_search();
     if (r.n_cand <= 8 * kWave)
-        row_select<8>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row, sh_bits, row, c);
+        row_select<8, NW>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row, sh_bits, row, c, lds_sel);
     else
-        row_select<kRowMaxCand / kWave>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row, sh_bits,
-                                        row, c);
+        row_select<kRowMaxCand / kWave, NW>(P, sh_key, sh_cnt, r, out, n_idx + (long long)c * P.rows + row,
+                                            sh_bits, row, c, lds_sel);
+    return r.need;
+}
+
+template <typename T, typename KT, int D>
+__global__ __launch_bounds__(1024) void select_row_kernel(KP P, const T *__restrict__ q,
+                                                          const KT *__restrict__ kbase, int32_t *__restrict__ idx,
+                                                          int32_t *__restrict__ n_idx, SelAppend app)
+{
+    __shared__ uint32_t sh_key[kRowMaxCand];
+    __shared__ uint32_t sh_bits[kRowMaxCand / 32];
+    __shared__ int sh_cnt[2][16];
+    // consecutive workgroups take the KV heads of one row (each XCD serves one head):
+    // 19.9 against 21.5 us per decode selection with rows in consecutive workgroups
+    row_plan_select<T, KT, D>(P, q, kbase, idx, n_idx, app, blockIdx.x / P.h_kv, blockIdx.x % P.h_kv, sh_key, sh_bits,
+                              sh_cnt, nullptr);
+}
+
+// ---------------------------------------------------------------- decode step (one launch)
+
+// A decode step in one launch for (row = sequence, KV head c): the row plan's append
+// and selection (row_plan_select on 8 wavefronts: the same arithmetic and results as
+// the 16-wavefront row kernel, with all of the row's key loads in flight at once),
+// then attention over the row's set by the 8 wavefronts with the selection read from
+// LDS.  Each wavefront walks 32-token chunks with the gather kernel's load/compute
+// steps, the next chunk's loads in flight while one is computed (16 chunks per
+// compute unit); the wavefronts' (max, sum, output) partials are merged through LDS
+// in wavefront order.  The host checks: bf16, one query per sequence, pooled keys,
+// G <= kStepRows, the set fits the LDS token list.
+constexpr int kStepRows = 8;
+constexpr int kStepWaves = 8;
+
+template <int D>
+__global__ __launch_bounds__(kStepWaves * 64) void decode_step_kernel(KP P, const uint16_t *__restrict__ q,
+                                                           const float *__restrict__ k_cmp,
+                                                           const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v,
+                                                           int32_t *__restrict__ idx, int32_t *__restrict__ n_idx,
+                                                           uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                           SelAppend app)
+{
+    constexpr int KS = D / 32;
+    __shared__ uint32_t sh_key[kRowMaxCand];
+    __shared__ uint32_t sh_bits[kRowMaxCand / 32];
+    __shared__ int sh_cnt[2][16];
+    __shared__ int sh_sel[kRowMaxCand];
+    __shared__ float sh_m[kStepWaves][kStepRows], sh_l[kStepWaves][kStepRows];
+    __shared__ int sh_buf[kTokCap > kStepWaves * kStepRows * D ? kTokCap : kStepWaves * kStepRows * D];
+    // (the token list, then the wavefronts' outputs)
+    __shared__ int sh_pre[32 * kStepWaves];                  // rows of the fixed positions loaded early
+    // consecutive workgroups take the KV heads of one row: the XCDs (which receive
+    // workgroups in turn) each serve one head
+    const long long row = blockIdx.x / P.h_kv;
+    const int c = blockIdx.x % P.h_kv, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int rr = lane & 15, g4 = lane >> 4;
+    const int b = seq_of_query(P, row);
+    const Seq s = seq_info(P, b);
+    const int p = s.q0 + (int)(row - s.q_off);
+    const KvMap kmap = kv_map(P, b);
+    const long long tstride = (long long)P.h_kv * D;
+    const uint16_t *kb = k + (kv_base(P, s) * P.h_kv + c) * D;
+    const uint16_t *vb = v + (kv_base(P, s) * P.h_kv + c) * D;
+    // The attended list runs init | window | selected blocks (the softmax does not
+    // depend on the order).  Its first n_fix positions (init and window) are known
+    // before the selection: their first chunks are loaded while the selection's
+    // threshold search runs, when HBM would otherwise idle.
+    const ASet a0 = aset_make(P, s.n_k, p, p, nullptr, 0);
+    const int n_fix = a0.n1 + a0.n3;
+    const int n_pre = min(n_fix, 32 * kStepWaves);
+    for (int x = tid; x < n_pre; x += blockDim.x)
+        sh_pre[x] = kmap.row(aset_token(a0, nullptr, x));   // no selection: init, then window
+    ChunkRegs<D> ra, rb;
+    bool loaded = false;                                      // ra holds this wavefront's first chunk
+    auto prefetch = [&]() {
+        if (32 * w + 32 <= n_pre) {                           // the chunk lies wholly in the fixed part
+            load_chunk<D>(ra, sh_pre, 32 * w, n_pre, kb, vb, tstride, rr, g4, n_pre);
+            loaded = true;
+        }
+    };
+    const int nsel = row_plan_select<uint16_t, float, D, kStepWaves>(P, q, k_cmp, idx, n_idx, app, row, c, sh_key,
+                                                                     sh_bits, sh_cnt, sh_sel, prefetch);
+    // the append wrote this sequence's new rows for head c, which the set reaches (its
+    // window ends at the query); this workgroup alone reads them back, and the barrier's
+    // workgroup-scope fences make its own stores visible to all its wavefronts (one
+    // compute unit, one L1).  A device-scope fence here would write back and invalidate
+    // the L2 once per workgroup (measured: +30 us per step).
+    __syncthreads();
+
+    const ASet a = aset_make(P, s.n_k, p, p, sh_sel, nsel);
+    const int n = a.total;                                   // <= kTokCap (checked by the host)
+    int *sh_tok = sh_buf;
+    for (int x = tid; x < n; x += blockDim.x)
+        sh_tok[x] = kmap.row(aset_token(a, sh_sel, x < n_fix ? (x < a.n1 ? x : x + a.n2) : x - a.n3));
+    const int R = P.G;
+    bf16x8 qop[KS];
+    if (rr < R) {
+        const uint16_t *qp = q + (row * P.h_q + c * P.G + rr) * D + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    __syncthreads();
+
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int pp = 0; pp < 8; pp++)
+        acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (32 * w < n && !loaded)
+        load_chunk<D>(ra, sh_tok, 32 * w, n, kb, vb, tstride, rr, g4, n);
+    for (int ch = w; 32 * ch < n; ch += 2 * kStepWaves) {
+        const int c1 = ch + kStepWaves;
+        if (32 * c1 < n)
+            load_chunk<D>(rb, sh_tok, 32 * c1, n, kb, vb, tstride, rr, g4, n);
+        compute_chunk<D>(ra, ra.live, qop, P.scale_log2, g4, m_run, l_part, acc);
+        if (32 * c1 >= n)
+            break;
+        const int c2 = c1 + kStepWaves;
+        if (32 * c2 < n)
+            load_chunk<D>(ra, sh_tok, 32 * c2, n, kb, vb, tstride, rr, g4, n);
+        compute_chunk<D>(rb, rb.live, qop, P.scale_log2, g4, m_run, l_part, acc);
+    }
+    float l_row = l_part + __shfl_xor(l_part, 16, kWave);
+    l_row += __shfl_xor(l_row, 32, kWave);
+    __syncthreads();                                         // every wavefront is done with the token list
+    float *sh_o = reinterpret_cast<float *>(sh_buf);         // [waves][rows < R][D]
+    if (g4 == 0 && rr < R) {
+        sh_m[w][rr] = m_run;
+        sh_l[w][rr] = l_row;
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+        const int rw = 4 * g4 + qq;
+        if (rw < R && (D == 128 || rr < D / 8)) {
+            float *dst = sh_o + (w * kStepRows + rw) * D + 8 * rr;
+#pragma unroll
+            for (int pp = 0; pp < 8; pp++)
+                dst[pp] = acc[pp][qq];
+        }
+    }
+    __syncthreads();
+    for (int it = tid; it < R * D; it += blockDim.x) {
+        const int r = it / D, e = it % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kStepWaves; ww++)
+            M = fmaxf(M, sh_m[ww][r]);
+        float Ls = 0.f, O = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < kStepWaves; ww++) {
+                const float f = exp2f(sh_m[ww][r] - M);
+                Ls += sh_l[ww][r] * f;
+                O += sh_o[(ww * kStepRows + r) * D + e] * f;
+            }
+        }
+        const int h = c * P.G + r;
+        out[(row * P.h_q + h) * D + e] = f32_to_bf16(O / Ls);
+        if (lse && e == 0)
+            lse[(long long)h * P.total_q + row] = (M + log2f(Ls)) * 0.69314718055994531f;
+    }
 }
 
 // ---------------------------------------------------------------- score_tile (MFMA fp32)
@@ -2015,7 +2203,7 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         return hipGetLastError();
     }
     if (plan == kSelectRowFused) {
-        dim3 grid((unsigned)P.rows, (unsigned)P.h_kv);
+        dim3 grid((unsigned)(P.rows * P.h_kv));
         mark(ev0);
         if (P.g == 1)
             select_row_kernel<T, T, D><<<grid, dim3(1024), 0, st>>>(P, q, (const T *)k, idx, n_idx, app);
@@ -2176,6 +2364,45 @@ hipError_t launch_append_select(const KP &P, int dtype, const void *k_new, const
     if (e != hipSuccess)
         return e;
     return launch_select(P, dtype, q_sel, k_cmp, k, idx, n_idx, ws, st, ev0, ev1);
+}
+
+// The decode step in one launch (decode_step_kernel) when the step fits it: bf16 decode
+// rows (one query per sequence) of the row plan with pooled keys and window >= block
+// (the append's blocks are never candidates), the default group score, at most
+// kStepRows heads per group, and an attended set that fits the LDS token list.
+bool decode_step_fused_ok(const KP &P, int dtype, bool have_k_cmp)
+{
+    const long long a_max = (long long)P.n_init + (long long)P.topk * P.g + P.window;
+    return dtype == 1 && have_k_cmp && P.g > 1 && !P.shared && P.max_q == 1 && P.window >= P.g &&
+           P.select_mode == 0 && P.bucket_nb == 0 && P.G <= kStepRows && (P.d == 128 || P.d == 64) &&
+           select_plan(P) == kSelectRowFused && a_max <= kTokCap && !getenv("SPARSE_ATTN_NO_STEP");
+}
+
+hipError_t launch_decode_step(const KP &P, int dtype, const void *k_new, const void *v_new, void *k, void *v,
+                              float *k_cmp, const void *q, int32_t *idx, int32_t *n_idx, void *out, float *lse,
+                              void *ws, int fwd_splits_n, hipStream_t st, void *ev0, void *ev1)
+{
+    if (!decode_step_fused_ok(P, dtype, k_cmp != nullptr)) {
+        hipError_t e = launch_append_select(P, dtype, k_new, v_new, k, v, k_cmp, q, idx, n_idx, ws, st);
+        if (e != hipSuccess)
+            return e;
+        return launch_fwd(P, dtype, q, k, v, idx, n_idx, out, lse, ws, fwd_splits_n, ev0, ev1, st);
+    }
+    const SelAppend app{k_new, v_new, k, v, k_cmp, append_pool_blocks(P)};
+    dim3 grid((unsigned)(P.rows * P.h_kv));
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev0, st);
+    if (P.d == 128)
+        decode_step_kernel<128><<<grid, dim3(kStepWaves * 64), 0, st>>>(P, (const uint16_t *)q, k_cmp, (const uint16_t *)k,
+                                                             (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
+                                                             app);
+    else
+        decode_step_kernel<64><<<grid, dim3(kStepWaves * 64), 0, st>>>(P, (const uint16_t *)q, k_cmp, (const uint16_t *)k,
+                                                            (const uint16_t *)v, idx, n_idx, (uint16_t *)out, lse,
+                                                            app);
+    if (ev0 && ev1)
+        (void)hipEventRecord((hipEvent_t)ev1, st);
+    return hipGetLastError();
 }
 
 } // namespace sa

@@ -125,6 +125,24 @@ def check_select(w, x_host, kc_ora, gpu_idx, gpu_n, rows=None, heads=None):
     return sel, len(flagged)
 
 
+def check_select_every_row(w, x_host, kc_ora, gpu_idx, gpu_n):
+    """check_select over every (row, KV head) of a full-size workload: the oracle selects
+    every row, the tables are compared at once, and only the rows that differ go through
+    the near-tie rule (with the oracle's scores of those rows).  Returns the number of
+    rows that differ (each a legitimate near tie)."""
+    sel = oracle.select(w, x_host["q"], kc_ora, x_host["k"])
+    o_idx, o_n = oracle.table(w, sel)
+    k = o_idx.shape[2]
+    g_idx = gpu_idx[:, :, :k]
+    same = (gpu_n == o_n) & np.all(g_idx == o_idx, axis=2)
+    if k < gpu_idx.shape[2]:
+        same &= np.all(gpu_idx[:, :, k:] == -1, axis=2)
+    heads, rows = np.nonzero(~same)
+    if len(rows):
+        check_select(w, x_host, kc_ora, gpu_idx, gpu_n, rows=rows, heads=heads)
+    return len(rows)
+
+
 def check_output(w, gpu_out, ora_out, what="output"):
     g = gpu_out.reshape(ora_out.shape).double().numpy() if isinstance(gpu_out, torch.Tensor) else gpu_out
     err = np.abs(g - ora_out)

@@ -2,7 +2,8 @@
 
 Small workloads: every row and every (query, head) compared.  Full-size
 workloads: the launch configuration the benchmark times, compared on sampled
-rows and requests the oracle computes one by one.  Edge cases: k = 0, k >=
+rows and requests the oracle computes one by one; the two prefill workloads
+also have every one of their selections compared.  Edge cases: k = 0, k >=
 |C| (dense), no sink, sequences with no candidates, ragged tails, head_dim
 64, GQA group 1, explicit query offsets.
 """
@@ -289,7 +290,7 @@ def test_full_decode_32k_sampled():
 
 
 def test_full_prefill_128k_sampled():
-    _sampled(FULL["bf16_prefill_128k"](), n_rows=96, n_req=384)
+    _sampled(FULL["bf16_prefill_128k"](), n_rows=96, n_req=4096)
 
 
 def test_full_draft_decode_sampled():
@@ -297,4 +298,29 @@ def test_full_draft_decode_sampled():
 
 
 def test_full_chunked_prefill_1m_sampled():
-    _sampled(FULL["bf16_chunked_prefill_1m"](), n_rows=24, n_req=256)
+    _sampled(FULL["bf16_chunked_prefill_1m"](), n_rows=24, n_req=2048)
+
+
+# ---------------------------------------------------------------- full size, every row
+
+def _every_row(name):
+    w = FULL[name]()
+    x, xg = parity.gen_pair(w, gen_on_device=True)
+    p = parity.params_for(w)
+    kc = sa.compress(p, xg["k"])
+    idx, n_idx = sa.select(p, xg["q"], kc, xg["k"])
+    torch.cuda.synchronize()
+    n_diff = parity.check_select_every_row(w, x, oracle.compress(w, x["k"]), idx.cpu().numpy(),
+                                           n_idx.cpu().numpy())
+    print(f"{name}: {w.rows * w.h_kv} (row, KV head) selections, {n_diff} near ties that differ")
+    return n_diff
+
+
+def test_full_prefill_128k_every_row():
+    """Every one of the 131072 x 8 selections of the 128K prefill against the oracle."""
+    _every_row("bf16_prefill_128k")
+
+
+def test_full_chunked_prefill_1m_every_row():
+    """Every one of the 4096 selections (262144 candidate groups each) of the 1M-token chunk."""
+    _every_row("bf16_chunked_prefill_1m")

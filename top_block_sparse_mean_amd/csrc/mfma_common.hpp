@@ -125,8 +125,10 @@ constexpr int kTokCap = 8192;
 // Splits of one attended set: attn_combine reads one split per lane of a wavefront.
 constexpr int kMaxSplits = 64;
 
-// Exclusive scan of one int per thread over a 512-thread workgroup; (exclusive, total).
-__device__ __forceinline__ int2 block_scan_int_512(int v, int *sh)
+// Exclusive scan of one int per thread over an NT-thread workgroup; (exclusive, total).
+// sh holds NT / 64 ints.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int2 block_scan_int_nt(int v, int *sh)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int incl = v;
@@ -141,7 +143,7 @@ __device__ __forceinline__ int2 block_scan_int_512(int v, int *sh)
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < NT / kWave; i++) {
         int c = sh[i];
         off += i < w ? c : 0;
         tot += c;

@@ -1589,6 +1589,210 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(KP P, const T *__res
     }
 }
 
+// ---------------------------------------------------------------- score_tile on bf16 matrix cores
+
+// fp32-accurate products on the bf16 matrix cores (16x the fp32 MFMA rate on gfx950):
+// each fp32 operand x is split into three bf16 parts, x = x1 + x2 + x3 up to 2^-27
+// relative (x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2); the differences
+// are exact in fp32), and a.b is the sum of the six partial products whose part
+// indices add to at most 4 (the dropped ones are below 2^-23 of |a b|), each exact in
+// fp32 and summed by the MFMA in fp32: the error is of the order of an fp32 dot
+// product's rounding.
+__device__ __forceinline__ void split3_bf16(float x, __bf16 &h, __bf16 &m, __bf16 &l)
+{
+    h = (__bf16)x;
+    const float r1 = x - (float)h;
+    m = (__bf16)r1;
+    l = (__bf16)(r1 - (float)m);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Pooled fp32 keys, d = 128, 512 threads: 128 rows x 64 candidates per tile, 8
+// wavefronts in 4 x 2, each a 32 x 32 block of 2 x 2 MFMA 16x16x32 bf16 tiles.  The
+// selector rows' three bf16 planes stay in registers; each staged key tile is split
+// into three bf16 planes once, as it is written to LDS (two buffers, one barrier per
+// tile).  Same output (order keys, group maxima) and layout as score_tile_kernel.
+constexpr int kSplitPitch = 272;                         // bytes per 128-element bf16 plane row
+constexpr int kSplitPlane = 64 * kSplitPitch;
+
+__global__ __launch_bounds__(512, 1) void score_tile3_kernel(KP P, const uint16_t *__restrict__ q,
+                                                             const float *__restrict__ kbase,
+                                                             uint32_t *__restrict__ ws, long long stride,
+                                                             int col_tiles, uint32_t *__restrict__ gmax,
+                                                             long long gstride)
+{
+    constexpr int D = 128, NT = 512, KS = D / 32;
+    constexpr int kPieces = 64 * D / 4 / NT;              // 16-byte fp32 pieces per thread per tile: 4
+    __shared__ __attribute__((aligned(16))) unsigned char sh_k[2][3 * kSplitPlane];
+    const int b = blockIdx.z % P.batch, c = blockIdx.z / P.batch;
+    const Seq s = seq_info(P, b);
+    const int r0 = blockIdx.y * 128;
+    if (r0 >= s.n_q)
+        return;
+    const int r_end = min(r0 + 128, s.n_q);
+    int jlo_last, jhi_last;
+    row_cands(P, s.n_k, s.q0 + r_end - 1, jlo_last, jhi_last);
+    jhi_last = min(jhi_last, (int)stride);
+    const int jc_base = jlo_last;
+    const int jc0 = jc_base + blockIdx.x * col_tiles * 64;
+    if (jc0 >= jhi_last)
+        return;
+    const int jc1 = min(jc0 + col_tiles * 64, jhi_last);
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int li = lane % 16, lk = lane / 16;
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+
+    // selector operands: rows r0 + wr + 16a + li, elements 32ks + 8lk .. +8, three planes
+    bf16x8_t qa[2][KS][3];
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+        const int rl = r0 + wr + 16 * a + li;
+        float qs[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                qs[ks][e] = 0.f;
+        if (rl < r_end) {
+            const long long i = s.q_off + rl;
+            for (int h = 0; h < P.G; h++) {
+                const uint16_t *qp = q + (i * P.h_q + (long long)c * P.G + h) * D + 8 * lk;
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * ks);
+                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        qs[ks][2 * e] += __uint_as_float(wd[e] << 16);
+                        qs[ks][2 * e + 1] += __uint_as_float(wd[e] & 0xffff0000u);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                __bf16 h, m, l;
+                split3_bf16(qs[ks][e], h, m, l);
+                qa[a][ks][0][e] = h;
+                qa[a][ks][1][e] = m;
+                qa[a][ks][2][e] = l;
+            }
+    }
+    int jh_row[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int rl = r0 + wr + 16 * a + 4 * lk + i;
+            int jl = 0, jh = 0;
+            if (rl < r_end)
+                row_cands(P, s.n_k, s.q0 + rl, jl, jh);
+            jh_row[a][i] = jh > jl ? min(jh, (int)stride) : 0;
+        }
+    const int j_first = first_cand(P);
+    const float *kb0 = kbase + (((long long)c * P.batch + b) * P.nb_max) * D;
+    // staging: thread tid holds fp32 pieces tid + NT u (row = piece / 32, 4 elements at 4 (piece % 32))
+    float4 stage[kPieces];
+    auto issue = [&](int jt) {
+#pragma unroll
+        for (int u = 0; u < kPieces; u++) {
+            const int piece = tid + NT * u, row = piece >> 5, col = piece & 31;
+            const int j = min(jt + row, jhi_last - 1);       // rows past the end re-read the last one
+            stage[u] = *reinterpret_cast<const float4 *>(kb0 + (long long)j * D + 4 * col);
+        }
+    };
+    auto write = [&](unsigned char *buf) {
+#pragma unroll
+        for (int u = 0; u < kPieces; u++) {
+            const int piece = tid + NT * u, row = piece >> 5, col = piece & 31;
+            const float x[4] = {stage[u].x, stage[u].y, stage[u].z, stage[u].w};
+            bf16x4_t ph, pm, pl;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                __bf16 h, m, l;
+                split3_bf16(x[e], h, m, l);
+                ph[e] = h;
+                pm[e] = m;
+                pl[e] = l;
+            }
+            unsigned char *dst = buf + row * kSplitPitch + 8 * col;
+            *reinterpret_cast<bf16x4_t *>(dst) = ph;
+            *reinterpret_cast<bf16x4_t *>(dst + kSplitPlane) = pm;
+            *reinterpret_cast<bf16x4_t *>(dst + 2 * kSplitPlane) = pl;
+        }
+    };
+    auto tile = [&](const unsigned char *buf, int jt) {
+        floatx4 acc[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++)
+                acc[a][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            bf16x8_t kv[2][3];
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++)
+#pragma unroll
+                for (int pl = 0; pl < 3; pl++)
+                    kv[bb][pl] = *reinterpret_cast<const bf16x8_t *>(buf + pl * kSplitPlane +
+                                                                     (wc + 16 * bb + li) * kSplitPitch + 64 * ks +
+                                                                     16 * lk);
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) {
+                    // smallest terms first: (3,1), (2,2), (1,3), (2,1), (1,2), (1,1)
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][2], kv[bb][0], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][1], kv[bb][1], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][2], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][1], kv[bb][0], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][1], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][0], acc[a][bb], 0, 0, 0);
+                }
+        }
+        uint32_t mx[8];
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int rl = r0 + wr + 16 * a + 4 * lk + i;
+                uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride + key_col0(P);
+                mx[4 * a + i] = 0u;
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) {
+                    const int j = jt + wc + 16 * bb + li;
+                    const uint32_t key = order_key(acc[a][bb][i]);
+                    const bool ok = j >= j_first && j < jh_row[a][i];
+                    if (ok)
+                        dst[j] = key;
+                    mx[4 * a + i] = max(mx[4 * a + i], ok ? key : 0u);
+                }
+            }
+        }
+        if (gmax && jt + wc < jc1) {
+            const uint32_t m = row16_max8(mx, li);
+            const int t = li & 7, rl = r0 + wr + 16 * (t >> 2) + 4 * lk + (t & 3);
+            if (li < 8 && rl < r_end)
+                gmax[((long long)c * P.rows + s.q_off + rl) * gstride + (unsigned)(jt + wc - jc_base) / kGroupCols] = m;
+        }
+    };
+    const int n_t = (jc1 - jc0 + 63) / 64;
+    issue(jc0);
+    write(sh_k[0]);
+    issue(jc0 + 64);
+    for (int t = 0; t < n_t; t++) {
+        __syncthreads();                                  // buffer t&1 holds tile t
+        tile(sh_k[t & 1], jc0 + 64 * t);
+        write(sh_k[(t + 1) & 1]);
+        issue(jc0 + 64 * (t + 2));
+    }
+}
+
 // ---------------------------------------------------------------- top-k over the workspace
 
 // 4 wavefronts per workgroup, one row each (<= 64 * KPL candidates).  grid: (ceil(rows/4), h_kv).
@@ -2289,11 +2493,16 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
             score_rows_kernel<T, float, D, kSplitChunk, 8><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride,
                                                                                      n_chunk);
     } else {
-        const long long row_tiles = (long long)((P.max_q + 63) / 64) * P.h_kv * P.batch;
+        const bool split3 = P.g > 1 && sizeof(T) == 2 && D == 128 && !getenv("SPARSE_ATTN_SCORE_FP32");
+        const int rt = split3 ? 128 : 64;                       // rows per workgroup
+        const long long row_tiles = (long long)((P.max_q + rt - 1) / rt) * P.h_kv * P.batch;
         const int col_tiles = score_col_tiles(stride, row_tiles);
-        dim3 grid((unsigned)((stride + col_tiles * 64 - 1) / (col_tiles * 64)), (unsigned)((P.max_q + 63) / 64),
+        dim3 grid((unsigned)((stride + col_tiles * 64 - 1) / (col_tiles * 64)), (unsigned)((P.max_q + rt - 1) / rt),
                   (unsigned)(P.h_kv * P.batch));
-        if (P.g == 1)
+        if (split3)
+            score_tile3_kernel<<<grid, dim3(512), 0, st>>>(P, (const uint16_t *)q, k_cmp, wsk, stride, col_tiles, gm,
+                                                           gms);
+        else if (P.g == 1)
             score_tile_kernel<T, T, D><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, col_tiles, gm,
                                                                    gms);
         else

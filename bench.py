@@ -358,12 +358,14 @@ KERNEL_SOURCES = {
                                CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
     "sa::attn_wg_kernel": [CSRC + "attn_prefill.hip", CSRC + "mfma_common.hpp", CSRC + "sa_common.hpp",
                            CSRC + "sa_internal.hpp"],
-    "sa::score_rows_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
-    "sa::score_tile_kernel": [CSRC + "select.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
+    "sa::score_rows_kernel": [CSRC + "select.hip", CSRC + "append_common.hpp", CSRC + "mfma_common.hpp",
+                              CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
+    "sa::score_tile3_kernel": [CSRC + "select.hip", CSRC + "append_common.hpp", CSRC + "mfma_common.hpp",
+                               CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
     "sa::attn_valu_kernel": [CSRC + "attn.hip", CSRC + "sa_common.hpp", CSRC + "sa_internal.hpp"],
 }
 DOMINANT = {"bf16_decode_32k": "sa::decode_step_kernel", "bf16_prefill_128k": "sa::attn_wg_kernel",
-            "bf16_draft_decode": "sa::score_rows_kernel", "bf16_chunked_prefill_1m": "sa::score_tile_kernel",
+            "bf16_draft_decode": "sa::score_rows_kernel", "bf16_chunked_prefill_1m": "sa::score_tile3_kernel",
             "tiny_fp32_prefill": "sa::attn_valu_kernel"}
 # workloads whose step is dominated by the selection's scoring kernel (rocprofv3 kernel stats)
 SELECT_DOMINANT = ("bf16_draft_decode", "bf16_chunked_prefill_1m")

@@ -612,6 +612,13 @@ def bench_workload(w, args, device, peaks, headline):
         step(events=kev.pairs[i])
     torch.cuda.synchronize()
     attn_ms = kev.mean_ms(2, 3)
+    bracket_ms = attn_ms
+    if step.fused_step:
+        # the step is that one launch: the timed steps' mean (launch plus the gap to the
+        # next) and the bracketed launches' mean are both upper bounds of its duration.
+        # The events around this launch read about 4 us above it (rocprofv3 sees the
+        # bracketed launches run no longer than the others), so the smaller is used
+        attn_ms = min(attn_ms, ms_step)
     score_ms = kev.mean_ms(0, 1) if step.time_select else None
     kev.close()
 
@@ -689,6 +696,8 @@ def bench_workload(w, args, device, peaks, headline):
                       "parallelism": "single-gpu"},
            "roofline": roof}
     out["step_kernel_ms" if step.fused_step else "attn_kernel_ms"] = round(attn_ms, 5)
+    if step.fused_step:
+        out["bracketed_kernel_ms"] = round(bracket_ms, 5)
     if score_ms:
         out["score_kernel_ms"] = round(score_ms, 5)
     if step.fused_step:

@@ -244,13 +244,19 @@ template <int NT>
 __device__ __forceinline__ void wg_issue(WgStage<NT> &st, const uint16_t *kb, const uint16_t *vb, long long tstride,
                                          const KvMap &map, int t0, int n_k, int tid)
 {
+    // 2048 chunks: 128 rows (64 K, 64 V) x 16; chunk c + 1024 is the V piece of K
+    // piece c (same token, same column), so each token offset serves both
+    constexpr int UH = 1024 / NT;
 #pragma unroll
-    for (int u = 0; u < 2048 / NT; u++) {
-        const int chunk = tid + NT * u;        // 2048 chunks: 128 rows (64 K, 64 V) x 16
+    for (int u = 0; u < UH; u++) {
+        const int chunk = tid + NT * u;
         const int row = chunk >> 4, col = chunk & 15;
-        const int t = min(max(t0 + (row & 63), 0), n_k - 1);
-        const uint16_t *base = row < 64 ? kb : vb;
-        st.c[u] = ld16(base + (long long)map.row(t) * tstride + 8 * col);
+        const int t = min(max(t0 + row, 0), n_k - 1);
+        // row and stride are non-negative 32-bit values: one 32 x 32 -> 64-bit product
+        const unsigned long long off =
+            (unsigned long long)(unsigned)map.row(t) * (unsigned)tstride + (unsigned)(8 * col);
+        st.c[u] = ld16(kb + off);
+        st.c[u + UH] = ld16(vb + off);
     }
 }
 
@@ -332,6 +338,21 @@ __device__ __forceinline__ void wg_pv(const unsigned char *buf, int h, int rr, i
 // (results below 2^-126 flush to zero, which the sum cannot see next to the
 // reference term).  Row sums come from the P V product itself (a ones column
 // tile), so the accumulators carry them and their rescaling.
+// Maximum with lane i ^ 16 / lane i ^ 32 (gfx950 lane swaps between 16-lane rows /
+// 32-lane halves, no LDS permute): each lane ends up with its own value in one
+// result and its partner's in the other.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int MT>
 __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4, const bf16x8 (&qop)[MT][4],
                                         const uint32_t (&live)[2][MT], bool partial, float scale_log2, float lazy,
@@ -356,16 +377,19 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
     bool bump[MT];
 #pragma unroll
     for (int a = 0; a < MT; a++) {
-        float mc = -INFINITY;
+        float mhv[2];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+        for (int h = 0; h < 2; h++) {                     // chained three-way maxima
             const f32x4 *x = st[h][a];
-            const float mh = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-            mc = live[h][a] != 0u ? fmaxf(mc, mh) : mc;
+            float mh = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
+            mh = fmaxf(fmaxf(mh, x[0][3]), x[1][0]);
+            mh = fmaxf(fmaxf(mh, x[1][1]), x[1][2]);
+            mh = fmaxf(mh, x[1][3]);
+            mhv[h] = live[h][a] != 0u ? mh : -INFINITY;
         }
-        mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
-        mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
+        float mc = fmaxf(mhv[0], mhv[1]);
+        mc = max_xor16(mc);
+        mc = max_xor32(mc);
         bump[a] = mc > m_run[a] + lazy;
         m_old[a] = m_run[a];
         m_run[a] = bump[a] ? mc : m_run[a];

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 9
+#define SPARSE_ATTN_ABI_VERSION 10
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -330,6 +330,31 @@ sa_status sparse_attn_decode_step(const sa_params *p, const void *k_new, const v
 sa_status sparse_attn_fwd_noalloc(const sa_params *p, const void *q, const void *k, const void *v,
                                   const int32_t *idx, const int32_t *n_idx, void *out, float *lse,
                                   void *stream);
+
+/* Contract checks, a debugging aid (no passage of the pages defines it).  The
+ * library built with contract checks (libsparse_attn_checked.so: every kernel
+ * compiled with SA_CHECKED) validates what its kernels read through the caller's
+ * device tables and, for each kind of violation it meets, sets one bit in a word
+ * it keeps on each GPU; the access then takes a clamped index inside the caller's
+ * buffers, so a call with broken tables returns wrong numbers, not a fault:
+ *   SA_CHECK_SEQ    sequence geometry: cu_seqlens not non-decreasing, a length
+ *                   above max_q / max_k or past total_q / total_k, q_pos0 + M_b > N_b
+ *   SA_CHECK_TABLE  selection table: n_idx outside [0, topk], an entry outside its
+ *                   row's candidate blocks, entries not ascending
+ *   SA_CHECK_PAGE   block table: a negative page id (pages past the end of the
+ *                   pool cannot be seen: the pool size is not passed)
+ *   SA_CHECK_TOKEN  a gathered token outside [0, p] of its query
+ * sparse_attn_check_flags copies the current GPU's word into *flags (host memory)
+ * and zeroes it when clear != 0.  The copy is synchronous: call it once the
+ * checked work is done (its streams synchronised).  In a build without checks it
+ * sets *flags = 0 and returns SA_ERR_UNSUPPORTED; NULL flags gives
+ * SA_ERR_INVALID_ARG, a failed HIP call SA_ERR_DEVICE.  Checked builds are for
+ * tests and debugging: the checks cost time in every kernel that gathers. */
+#define SA_CHECK_SEQ 1u
+#define SA_CHECK_TABLE 2u
+#define SA_CHECK_PAGE 4u
+#define SA_CHECK_TOKEN 8u
+sa_status sparse_attn_check_flags(uint32_t *flags, int clear);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def status(fn, *args):
 
 def test_library_loads_and_version():
     assert _lib.lib() is not None
-    assert sa.abi_version() == 9
+    assert sa.abi_version() == 10
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -67,6 +67,30 @@ def test_every_declared_symbol_is_exported():
     assert not missing, missing
     for s in decl:
         assert hasattr(_lib.lib(), s)
+
+
+def test_checked_build_exports_the_same_symbols():
+    """The debugging build with contract checks is a drop-in replacement."""
+    from top_block_sparse_mean_amd import build
+    assert os.path.exists(build.CHECKED_OUT), "libsparse_attn_checked.so is not built"
+    out = subprocess.run(["nm", "-D", "--defined-only", build.CHECKED_OUT], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sparse_attn_\w+)", out))
+    assert set(declared_symbols()) <= exported
+
+
+def test_check_flags_without_checks():
+    """The plain build carries no contract checks: the call says so (flags zeroed) and
+    touches no device; a NULL output is rejected first."""
+    v = ctypes.c_uint32(7)
+    if _lib.LIB_PATH.endswith("libsparse_attn_checked.so"):
+        pytest.skip("the checked build is loaded")
+    assert status("sparse_attn_check_flags", ctypes.byref(v), 1) == UNSUPPORTED
+    assert v.value == 0
+    assert "without contract checks" in _lib.lib().sparse_attn_last_error().decode()
+    assert status("sparse_attn_check_flags", None, 1) == INVALID
+    assert "NULL" in _lib.lib().sparse_attn_last_error().decode()
+    with pytest.raises(sa.SparseAttnError):
+        sa.check_flags()
 
 
 def test_every_export_has_a_c_signature():

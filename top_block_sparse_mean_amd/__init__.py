@@ -24,14 +24,15 @@ from typing import Optional, Sequence
 
 import torch
 
-from ._lib import (EXPORTS, LIB_PATH, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM,  # noqa: F401
-                   SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaBucketIndex,
+from ._lib import (EXPORTS, LIB_PATH, SA_CHECK_PAGE, SA_CHECK_SEQ, SA_CHECK_TABLE,  # noqa: F401
+                   SA_CHECK_TOKEN, SA_DTYPE_BF16, SA_DTYPE_F32, SA_POOL_L2SUM, SA_POOL_MEAN, SA_SELECT_ATTN, SA_SELECT_MAX, SA_SELECT_SOFTMAX, SA_SELECT_SUM, SaBucketIndex,
                    SaParams, SparseAttnError, check, lib)
 
 __all__ = ["Params", "validate", "workspace_size", "compress", "compress_tail", "append_kv", "select",
            "append_select", "fwd", "fwd_noalloc", "decode_step", "BucketIndex", "bucket_build", "bucket_select",
            "abi_version", "SparseAttnError", "SA_POOL_MEAN", "SA_POOL_L2SUM", "SA_SELECT_SUM", "SA_SELECT_SOFTMAX",
-           "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS"]
+           "SA_SELECT_MAX", "SA_SELECT_ATTN", "LIB_PATH", "EXPORTS", "check_flags", "SA_CHECK_SEQ",
+           "SA_CHECK_TABLE", "SA_CHECK_PAGE", "SA_CHECK_TOKEN"]
 
 _DT = {torch.float32: SA_DTYPE_F32, torch.bfloat16: SA_DTYPE_BF16}
 
@@ -116,6 +117,15 @@ class Params:
 
 def abi_version() -> int:
     return lib().sparse_attn_abi_version()
+
+
+def check_flags(clear: bool = True) -> int:
+    """The contract-check bits the checked library has set on the current GPU since they
+    were last cleared (SA_CHECK_*); clears them unless clear is False.  Synchronise the
+    streams that ran the checked work first.  Raises in a library built without checks."""
+    v = ctypes.c_uint32(0)
+    check("sparse_attn_check_flags", lib().sparse_attn_check_flags(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)
 
 
 def validate(p: Params) -> None:

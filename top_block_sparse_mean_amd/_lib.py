@@ -17,13 +17,14 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_DEVICE =
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_POOL_MEAN, SA_POOL_L2SUM = 0, 1
 SA_SELECT_SUM, SA_SELECT_SOFTMAX, SA_SELECT_MAX, SA_SELECT_ATTN = 0, 1, 2, 3
+SA_CHECK_SEQ, SA_CHECK_TABLE, SA_CHECK_PAGE, SA_CHECK_TOKEN = 1, 2, 4, 8
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTS = ("sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_last_error",
            "sparse_attn_validate", "sparse_attn_workspace_size", "sparse_attn_compress",
            "sparse_attn_compress_tail", "sparse_attn_append_kv", "sparse_attn_select", "sparse_attn_append_select",
            "sparse_attn_fwd", "sparse_attn_bucket_build", "sparse_attn_bucket_workspace_size", "sparse_attn_bucket_select",
-           "sparse_attn_fwd_noalloc", "sparse_attn_decode_step")
+           "sparse_attn_fwd_noalloc", "sparse_attn_decode_step", "sparse_attn_check_flags")
 
 
 class SaParams(ctypes.Structure):
@@ -111,6 +112,7 @@ def lib():
         L.sparse_attn_bucket_build.argtypes = [P, vp, BX, vp]
         L.sparse_attn_bucket_workspace_size.argtypes = [P, BX, ctypes.c_int32, ctypes.POINTER(sz)]
         L.sparse_attn_bucket_select.argtypes = [P, vp, BX, ctypes.c_int32, vp, vp, vp, sz, vp]
+        L.sparse_attn_check_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L

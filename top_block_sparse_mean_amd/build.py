@@ -17,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsparse_attn.so")
 BUILD = os.path.join(PKG, "_build")
+# The debugging build with contract checks (SA_CHECKED: gathers through the caller's
+# device tables flag violations; sparse_attn_check_flags reads the flags).
+CHECKED_OUT = os.path.join(PKG, "libsparse_attn_checked.so")
+CHECKED_BUILD = os.path.join(PKG, "_build_checked")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -52,12 +56,16 @@ def _compile(src: str, build_dir: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, sanitize: bool = False, out: str = OUT, build_dir: str = BUILD) -> str:
+def build(verbose: bool = False, sanitize: bool = False, out: str = OUT, build_dir: str = BUILD,
+          checked: bool = False) -> str:
     """Compile every source for gfx950 and link the library at `out`.  sanitize: host code
-    with address and undefined-behaviour checks (a test build; see SANITIZE)."""
+    with address and undefined-behaviour checks (a test build; see SANITIZE).  checked:
+    kernels with contract checks (SA_CHECKED), by default at CHECKED_OUT."""
+    if checked and out == OUT:
+        out, build_dir = CHECKED_OUT, CHECKED_BUILD
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
-    extra = SANITIZE if sanitize else []
+    extra = (SANITIZE if sanitize else []) + (["-DSA_CHECKED"] if checked else [])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
     tmp = out + ".tmp"
@@ -75,4 +83,5 @@ def build(verbose: bool = False, sanitize: bool = False, out: str = OUT, build_d
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, checked=True)
     sys.exit(0)

@@ -135,6 +135,12 @@ sa::KP make_kp(const sa_params *p)
     k.attn_lse = p->attn_lse;
     k.bucket_c = k.bucket_nb = k.bucket_nblk = 0;
     k.boundary = nullptr;
+    k.check = nullptr;
+    if (sa::contract_checked()) {
+        uint32_t *w = nullptr;
+        if (sa::contract_word(&w) == hipSuccess)
+            k.check = w;
+    }
     // boundary scores in the select mode's units: the default mode ranks by the unscaled dot
     k.boundary_scale = p->select_mode == SA_SELECT_SUM ? 1.0f / std::sqrt((float)p->head_dim) : 1.0f;
     k.block_table = p->block_table;
@@ -481,6 +487,35 @@ sa_status sparse_attn_fwd_noalloc(const sa_params *p, const void *q, const void 
     return device_status(sa::launch_fwd(kp, p->dtype, q, k, v, idx, n_idx, out, lse, scratch, splits,
                                         p->timing_events[0], p->timing_events[1], (hipStream_t)stream),
                          "fwd_noalloc launch");
+}
+
+static_assert(SA_CHECK_SEQ == sa::kCheckSeq && SA_CHECK_TABLE == sa::kCheckTable && SA_CHECK_PAGE == sa::kCheckPage &&
+                  SA_CHECK_TOKEN == sa::kCheckToken,
+              "contract-check bits of the header and the kernels");
+
+sa_status sparse_attn_check_flags(uint32_t *flags, int clear)
+{
+    if (!flags)
+        return fail(SA_ERR_INVALID_ARG, "check_flags: flags is NULL");
+    *flags = 0u;
+    if (!sa::contract_checked())
+        return fail(SA_ERR_UNSUPPORTED, "check_flags: this library is built without contract checks");
+    uint32_t *word = nullptr;
+    hipError_t e = sa::contract_word(&word);
+    if (e != hipSuccess)
+        return device_status(e, "check_flags: check word lookup");
+    uint32_t v = 0u;
+    e = hipMemcpy(&v, word, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return device_status(e, "check_flags: read");
+    if (clear) {
+        const uint32_t zero = 0u;
+        e = hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice);
+        if (e != hipSuccess)
+            return device_status(e, "check_flags: clear");
+    }
+    *flags = v;
+    return ok();
 }
 
 } // extern "C"

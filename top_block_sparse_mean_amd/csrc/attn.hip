@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(KP P, const T *__restric
     const int p_sel = P.shared ? s.q0 - 1 : p;
     const int32_t *sel = idx + ((long long)c * P.rows + row) * P.topk;
     int nsel = n_idx[(long long)c * P.rows + row];
-    nsel = nsel < 0 ? 0 : (nsel > P.topk ? P.topk : nsel);
+    nsel = clamp_nsel(P, nsel);
     const ASet a = aset_make(P, s.n_k, p, p_sel, sel, nsel);
     const long long k_base = kv_base(P, s);
     const KvMap kmap = kv_map(P, b);

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(KP P, const uint16_t 
     }
     const int R = nq_u * P.G;                 // <= 16 (checked by the host)
     (void)row;
-    nsel = nsel < 0 ? 0 : (nsel > P.topk ? P.topk : nsel);
+    nsel = clamp_nsel(P, nsel);
     __syncthreads();                          // sh_sel complete
     const int32_t *sel = sel_in_lds ? sh_sel : sel_g;
     const ASet a = aset_make(P, s.n_k, p_max, p_sel, sel, nsel);

@@ -98,8 +98,15 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(KP P, const uint16_t 
         const long long qi = s.q_off + qw0 + qq;
         const int32_t *sel = idx + ((long long)c * P.rows + qi) * P.topk;
         int ns = n_idx[(long long)c * P.rows + qi];
-        ns = ns < 0 ? 0 : (ns > P.topk ? P.topk : ns);
+        ns = clamp_nsel(P, ns);
+#ifdef SA_CHECKED
+        int cj_lo, cj_hi;
+        cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + qw0 + qq, cj_lo, cj_hi);
+#endif
         for (int e = lane; e < ns * tpb; e += kWave) {
+#ifdef SA_CHECKED
+            contract_flag(P.check, sel[e / tpb] < cj_lo || sel[e / tpb] >= cj_hi, kCheckTable);
+#endif
             int tile = sel[e / tpb] * tpb + e % tpb;
             if (tile >= 0 && tile < ntile) {
                 atomicOr(&sh_sel[w][qq][tile >> 5], 1u << (tile & 31));
@@ -455,7 +462,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_wg_kernel(KP P, const uint16_
     __shared__ unsigned short sh_list[kWgMaxTiles];
     __shared__ __attribute__((aligned(16))) unsigned char sh_kv[2][kWgStep * 128 * kWgPitch];
     __shared__ int sh_scan[NW];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its spans and tests stay scalar
     const int rr = lane & 15, g4 = lane >> 4;
     // Workgroups in launch order: each (sequence, KV head) in turn, its query tiles
     // from the last (the longest sets) to the first, so the short ones fill the tail
@@ -483,9 +491,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_wg_kernel(KP P, const uint16_
         const int qq = x / P.topk, e = x % P.topk;
         const long long qi = s.q_off + q_lo + qq;
         int ns = n_idx[(long long)c * P.rows + qi];
-        ns = ns < 0 ? 0 : (ns > P.topk ? P.topk : ns);
+        ns = clamp_nsel(P, ns);
         if (e < ns) {
             const int j = idx[((long long)c * P.rows + qi) * P.topk + e];
+#ifdef SA_CHECKED
+            int cj_lo, cj_hi;
+            cand_range(P.g, P.n_init, P.window, s.n_k, s.q0 + q_lo + qq, cj_lo, cj_hi);
+            contract_flag(P.check, j < cj_lo || j >= cj_hi, kCheckTable);
+#endif
             if (j >= 0 && j < ntile)
                 atomicOr(&sh_qm[j], 1ull << qq);
         }

@@ -37,7 +37,32 @@ struct KP {
     // scores (the smallest kept, the largest left out) times boundary_scale, or nullptr
     float *boundary;
     float boundary_scale;
+    // contract-check word of this device (builds with SA_CHECKED), else nullptr
+    uint32_t *check;
 };
+
+// Contract checks.  A build with SA_CHECKED defined validates what the kernels read
+// from the caller's device tables: a gather whose index breaks the contract ORs its
+// bit into *P.check and takes a clamped, in-range index instead.  Other builds
+// compile every check away (the clamps they always apply stay).
+enum : uint32_t {
+    kCheckSeq = 1u,     // sequence geometry: cu_seqlens, lengths, q_pos0
+    kCheckTable = 2u,   // selection table: an entry outside the row's blocks, or n_idx outside [0, topk]
+    kCheckPage = 4u,    // block table: a negative page id
+    kCheckToken = 8u    // a gathered token outside [0, p] of its query
+};
+
+__device__ __forceinline__ void contract_flag(uint32_t *word, bool bad, uint32_t bit)
+{
+#ifdef SA_CHECKED
+    if (bad && word)
+        atomicOr(word, bit);
+#else
+    (void)word;
+    (void)bad;
+    (void)bit;
+#endif
+}
 
 struct Seq {
     long long k_off, q_off;
@@ -52,6 +77,21 @@ __device__ __forceinline__ Seq seq_info(const KP &P, int b)
     s.n_k = P.cu_k[b + 1] - P.cu_k[b];
     s.n_q = P.cu_q[b + 1] - P.cu_q[b];
     s.q0 = P.q_pos0 ? P.q_pos0[b] : s.n_k - s.n_q;
+#ifdef SA_CHECKED
+    // offsets into [0, total], lengths into [0, max] and the rows' span, queries
+    // inside their sequence
+    const Seq r = s;
+    s.k_off = s.k_off < 0 ? 0 : (s.k_off > P.total_k ? P.total_k : s.k_off);
+    s.q_off = s.q_off < 0 ? 0 : (s.q_off > P.total_q ? P.total_q : s.q_off);
+    const long long kmax = P.block_table ? (long long)P.max_k : min((long long)P.max_k, P.total_k - s.k_off);
+    const long long qmax = min((long long)P.max_q, P.total_q - s.q_off);
+    s.n_k = (int)(s.n_k < 0 ? 0 : (s.n_k > kmax ? kmax : s.n_k));
+    s.n_q = (int)(s.n_q < 0 ? 0 : (s.n_q > qmax ? qmax : s.n_q));
+    s.n_q = s.n_q > s.n_k ? s.n_k : s.n_q;
+    s.q0 = s.q0 < 0 ? 0 : (s.q0 > s.n_k - s.n_q ? s.n_k - s.n_q : s.q0);
+    contract_flag(P.check, r.k_off != s.k_off || r.q_off != s.q_off || r.n_k != s.n_k || r.n_q != s.n_q ||
+                               r.q0 != s.q0, kCheckSeq);
+#endif
     return s;
 }
 
@@ -61,10 +101,23 @@ __device__ __forceinline__ Seq seq_info(const KP &P, int b)
 struct KvMap {
     const int32_t *pt;  // the sequence's block-table row, or nullptr (packed)
     int shift;
+#ifdef SA_CHECKED
+    uint32_t *check;
+    __device__ __forceinline__ int row(int t) const
+    {
+        if (!pt)
+            return t;
+        int page = pt[t >> shift];
+        contract_flag(check, page < 0, kCheckPage);
+        page = page < 0 ? 0 : page;
+        return (page << shift) | (t & ((1 << shift) - 1));
+    }
+#else
     __device__ __forceinline__ int row(int t) const
     {
         return pt ? (pt[t >> shift] << shift) | (t & ((1 << shift) - 1)) : t;
     }
+#endif
 };
 
 __device__ __forceinline__ KvMap kv_map(const KP &P, int b)
@@ -72,7 +125,17 @@ __device__ __forceinline__ KvMap kv_map(const KP &P, int b)
     KvMap m;
     m.pt = P.block_table ? P.block_table + (long long)b * P.max_pages : nullptr;
     m.shift = P.page_shift;
+#ifdef SA_CHECKED
+    m.check = P.check;
+#endif
     return m;
+}
+
+// A row's selection count clamped into [0, topk] (out of range: flagged by checked builds).
+__device__ __forceinline__ int clamp_nsel(const KP &P, int ns)
+{
+    contract_flag(P.check, ns < 0 || ns > P.topk, kCheckTable);
+    return ns < 0 ? 0 : (ns > P.topk ? P.topk : ns);
 }
 
 __device__ __forceinline__ long long kv_base(const KP &P, const Seq &s) { return P.block_table ? 0 : s.k_off; }
@@ -139,6 +202,10 @@ struct ASet {
     int nsel, g;
     int start_f, len_f;   // first selected block, clipped
     int p;                // query position (tokens are clamped to <= p)
+#ifdef SA_CHECKED
+    uint32_t *check;
+    int j_lo, j_hi;       // the row's candidate blocks: every listed block must lie in them
+#endif
 };
 
 __device__ __forceinline__ ASet aset_make(const KP &P, int n_k, int p, int p_sel, const int32_t *sel, int nsel)
@@ -173,6 +240,16 @@ __device__ __forceinline__ ASet aset_make(const KP &P, int n_k, int p, int p_sel
         }
     }
     a.total = a.n1 + a.n2 + a.n3;
+#ifdef SA_CHECKED
+    a.check = P.check;
+    contract_flag(P.check, p < 0 || p >= n_k, kCheckSeq);
+    a.p = a.p < 0 ? 0 : a.p;
+    cand_range(P.g, P.n_init, P.window, n_k, p_sel, a.j_lo, a.j_hi);
+    if (a.nsel > 0)
+        contract_flag(P.check, sel[0] < a.j_lo || sel[0] >= a.j_hi || sel[a.nsel - 1] < a.j_lo ||
+                                   sel[a.nsel - 1] >= a.j_hi || (a.nsel > 1 && sel[a.nsel - 1] <= sel[0]),
+                      kCheckTable);
+#endif
     return a;
 }
 
@@ -189,14 +266,23 @@ __device__ __forceinline__ int aset_token(const ASet &a, const int32_t *sel, int
         } else {
             r -= a.len_f;
             int m = r / a.g;
-            if (m < a.nsel - 2)
-                t = sel[1 + m] * a.g + (r - m * a.g);
-            else
+            if (m < a.nsel - 2) {
+                const int j = sel[1 + m];
+#ifdef SA_CHECKED
+                // a listed block inside the row's candidates, after the one before it
+                contract_flag(a.check, j < a.j_lo || j >= a.j_hi || j <= sel[m], kCheckTable);
+#endif
+                t = j * a.g + (r - m * a.g);
+            } else {
                 t = sel[a.nsel - 1] * a.g + (r - (a.nsel - 2) * a.g);
+            }
         }
     } else {
         t = a.lo_w + (pos - a.n1 - a.n2);
     }
+#ifdef SA_CHECKED
+    contract_flag(a.check, t < 0 || t > a.p, kCheckToken);
+#endif
     return t < 0 ? 0 : (t > a.p ? a.p : t);   // never leave [0, p], whatever the table holds
 }
 

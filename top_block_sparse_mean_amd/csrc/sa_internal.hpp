@@ -71,4 +71,9 @@ hipError_t launch_decode_step(const KP &P, int dtype, const void *k_new, const v
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 hipError_t noalloc_scratch(void **ptr);
 
+// Contract checks: whether this build carries them, and the current device's
+// check word (hipErrorNotSupported in a build without them).
+bool contract_checked();
+hipError_t contract_word(uint32_t **ptr);
+
 } // namespace sa

@@ -345,19 +345,36 @@ __device__ __forceinline__ void wg_pv(const unsigned char *buf, int h, int rr, i
 // (results below 2^-126 flush to zero, which the sum cannot see next to the
 // reference term).  Row sums come from the P V product itself (a ones column
 // tile), so the accumulators carry them and their rescaling.
+// Maxima of matrix-core results as single instructions: fmaxf first quiets both
+// operands of a two-way maximum (two more instructions each), which a logit that
+// is never a signalling NaN does not need.
+__device__ __forceinline__ float max2(float a, float b)
+{
+    float r;
+    __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c)
+{
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Maximum with lane i ^ 16 / lane i ^ 32 (gfx950 lane swaps between 16-lane rows /
 // 32-lane halves, no LDS permute): each lane ends up with its own value in one
 // result and its partner's in the other.
 __device__ __forceinline__ float max_xor16(float x)
 {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float max_xor32(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int MT>
@@ -388,13 +405,13 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
 #pragma unroll
         for (int h = 0; h < 2; h++) {                     // chained three-way maxima
             const f32x4 *x = st[h][a];
-            float mh = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
-            mh = fmaxf(fmaxf(mh, x[0][3]), x[1][0]);
-            mh = fmaxf(fmaxf(mh, x[1][1]), x[1][2]);
-            mh = fmaxf(mh, x[1][3]);
+            float mh = max3(x[0][0], x[0][1], x[0][2]);
+            mh = max3(mh, x[0][3], x[1][0]);
+            mh = max3(mh, x[1][1], x[1][2]);
+            mh = max2(mh, x[1][3]);
             mhv[h] = live[h][a] != 0u ? mh : -INFINITY;
         }
-        float mc = fmaxf(mhv[0], mhv[1]);
+        float mc = max2(mhv[0], mhv[1]);
         mc = max_xor16(mc);
         mc = max_xor32(mc);
         bump[a] = mc > m_run[a] + lazy;

@@ -1795,7 +1795,24 @@ __global__ __launch_bounds__(512, 1) void score_tile3_kernel(KP P, const uint16_
 
 // ---------------------------------------------------------------- top-k over the workspace
 
+// One row's selection by one wavefront, its keys held K per lane.
+template <int K>
+__device__ __forceinline__ void topk_wave_row(const uint32_t *src, const RowGeo &r, int32_t *out, uint32_t *sk,
+                                              int *si)
+{
+    const int lane = lane_id();
+    uint32_t kr[K];
+#pragma unroll
+    for (int m = 0; m < K; m++) {
+        const int i = m * kWave + lane;
+        kr[m] = i < r.n_cand ? src[r.j_lo + i] : 0u;
+    }
+    wave_select<K>(kr, r.n_cand, r.need, EmitIdx{out, r.j_lo}, sk, si);
+}
+
 // 4 wavefronts per workgroup, one row each (<= 64 * KPL candidates).  grid: (ceil(rows/4), h_kv).
+// A row takes the smallest keys-per-lane count that holds it, so a wavefront's work
+// follows its row's length (the rows of a causal prefill range from none to the stride).
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__restrict__ ws,
                                                         long long stride, int32_t *__restrict__ idx,
@@ -1809,13 +1826,6 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     // the stride: on average half of it)
     RowGeo r = row_geo(P, row);
     const uint32_t *src = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
-    const bool pick = r.need != r.n_cand;
-    uint32_t kr[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; m++) {
-        const int i = m * kWave + lane;
-        kr[m] = pick && i < r.n_cand ? src[r.j_lo + i] : 0u;
-    }
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
     if (lane == 0)
         n_idx[(long long)c * P.rows + row] = r.need;
@@ -1826,7 +1836,14 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(KP P, const uint32_t *__
     __shared__ uint32_t sh_k[4][kFilterCap];
     __shared__ int sh_i[4][kFilterCap];
     const int wv = threadIdx.x / kWave;
-    wave_select<KPL>(kr, r.n_cand, r.need, EmitIdx{out, r.j_lo}, sh_k[wv], sh_i[wv]);
+    if (KPL > 4 && r.n_cand <= 4 * kWave)
+        topk_wave_row<(KPL > 4 ? 4 : KPL)>(src, r, out, sh_k[wv], sh_i[wv]);
+    else if (KPL > 8 && r.n_cand <= 8 * kWave)
+        topk_wave_row<(KPL > 8 ? 8 : KPL)>(src, r, out, sh_k[wv], sh_i[wv]);
+    else if (KPL > 16 && r.n_cand <= 16 * kWave)
+        topk_wave_row<(KPL > 16 ? 16 : KPL)>(src, r, out, sh_k[wv], sh_i[wv]);
+    else
+        topk_wave_row<KPL>(src, r, out, sh_k[wv], sh_i[wv]);
     for (int s = r.need + lane; s < P.topk; s += kWave)
         out[s] = -1;
 }

@@ -1682,17 +1682,17 @@ __global__ __launch_bounds__(512, 1) void score_tile3_kernel(KP P, const uint16_
                 qa[a][ks][2][e] = l;
             }
     }
-    int jh_row[2][4];
+    // the products come out transposed (candidates down, rows across): lane (li, lk)
+    // holds four consecutive candidates 4 lk .. +3 of row li of each 16 x 16 tile
+    int jh_row[2];
 #pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int rl = r0 + wr + 16 * a + 4 * lk + i;
-            int jl = 0, jh = 0;
-            if (rl < r_end)
-                row_cands(P, s.n_k, s.q0 + rl, jl, jh);
-            jh_row[a][i] = jh > jl ? min(jh, (int)stride) : 0;
-        }
+    for (int a = 0; a < 2; a++) {
+        const int rl = r0 + wr + 16 * a + li;
+        int jl = 0, jh = 0;
+        if (rl < r_end)
+            row_cands(P, s.n_k, s.q0 + rl, jl, jh);
+        jh_row[a] = jh > jl ? min(jh, (int)stride) : 0;
+    }
     const int j_first = first_cand(P);
     const float *kb0 = kbase + (((long long)c * P.batch + b) * P.nb_max) * D;
     // staging: thread tid holds fp32 pieces tid + NT u (row = piece / 32, 4 elements at 4 (piece % 32))
@@ -1746,38 +1746,47 @@ __global__ __launch_bounds__(512, 1) void score_tile3_kernel(KP P, const uint16_
             for (int a = 0; a < 2; a++)
 #pragma unroll
                 for (int bb = 0; bb < 2; bb++) {
-                    // smallest terms first: (3,1), (2,2), (1,3), (2,1), (1,2), (1,1)
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][2], kv[bb][0], acc[a][bb], 0, 0, 0);
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][1], kv[bb][1], acc[a][bb], 0, 0, 0);
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][2], acc[a][bb], 0, 0, 0);
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][1], kv[bb][0], acc[a][bb], 0, 0, 0);
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][1], acc[a][bb], 0, 0, 0);
-                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks][0], kv[bb][0], acc[a][bb], 0, 0, 0);
+                    // S^T = K Q^T (keys as the A operand); smallest terms first:
+                    // (3,1), (2,2), (1,3), (2,1), (1,2), (1,1)
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][0], qa[a][ks][2], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][1], qa[a][ks][1], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][2], qa[a][ks][0], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][0], qa[a][ks][1], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][1], qa[a][ks][0], acc[a][bb], 0, 0, 0);
+                    acc[a][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[bb][0], qa[a][ks][0], acc[a][bb], 0, 0, 0);
                 }
         }
-        uint32_t mx[8];
 #pragma unroll
         for (int a = 0; a < 2; a++) {
+            const int rl = r0 + wr + 16 * a + li;
+            uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride + key_col0(P);
+            uint32_t m = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int rl = r0 + wr + 16 * a + 4 * lk + i;
-                uint32_t *dst = ws + ((long long)c * P.rows + s.q_off + rl) * stride + key_col0(P);
-                mx[4 * a + i] = 0u;
+            for (int bb = 0; bb < 2; bb++) {
+                // candidates j0 .. j0+3: key_col0 + j0 is a multiple of 4 (the span starts at
+                // the first candidate), so four valid keys are one 16-byte store
+                const int j0 = jt + wc + 16 * bb + 4 * lk;
+                uint32_t kk[4];
+                bool ok[4];
 #pragma unroll
-                for (int bb = 0; bb < 2; bb++) {
-                    const int j = jt + wc + 16 * bb + li;
-                    const uint32_t key = order_key(acc[a][bb][i]);
-                    const bool ok = j >= j_first && j < jh_row[a][i];
-                    if (ok)
-                        dst[j] = key;
-                    mx[4 * a + i] = max(mx[4 * a + i], ok ? key : 0u);
+                for (int i = 0; i < 4; i++) {
+                    kk[i] = order_key(acc[a][bb][i]);
+                    ok[i] = j0 + i >= j_first && j0 + i < jh_row[a];
+                    m = max(m, ok[i] ? kk[i] : 0u);
+                }
+                if (ok[0] && ok[3]) {                     // the valid candidates are one range
+                    *reinterpret_cast<uint4 *>(dst + j0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (ok[i])
+                            dst[j0 + i] = kk[i];
                 }
             }
-        }
-        if (gmax && jt + wc < jc1) {
-            const uint32_t m = row16_max8(mx, li);
-            const int t = li & 7, rl = r0 + wr + 16 * (t >> 2) + 4 * lk + (t & 3);
-            if (li < 8 && rl < r_end)
+            // the wavefront's 32 columns of row li are one group: its lanes li, li+16, li+32, li+48
+            m = max(m, (uint32_t)__shfl_xor((int)m, 16, kWave));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 32, kWave));
+            if (gmax && lk == 0 && rl < r_end && jt + wc < jc1)
                 gmax[((long long)c * P.rows + s.q_off + rl) * gstride + (unsigned)(jt + wc - jc_base) / kGroupCols] = m;
         }
     };

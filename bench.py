@@ -157,25 +157,20 @@ class Step:
             if self.k_cmp is not None:
                 sa.compress(self.p, x["k"], self.k_cmp)   # the cache's pooled keys, built before decoding
 
-    def __call__(self, events=None, stages=None):
+    def __call__(self, events=None):
         """events: four events, recorded around the selection's scoring kernel ([0], [1])
         and the main attention kernel ([2], [3]) -- around the one launch ([2], [3]) of a
-        fused decode step.  stages: (TimingEvents, four events) recorded before compress,
-        after compress, after select and after fwd (a decode step then runs as the three
-        calls it fuses)."""
+        fused decode step."""
         x = self.x
-        mark = (lambda i: stages[0].record(stages[1][i])) if stages else (lambda i: None)
-        mark(0)
-        # decode: append + select in one call (one launch for decode rows); the stage
-        # pass times them as two calls
-        joined = self.decode and stages is None and self.index is None
+        # decode: append + select in one call (one launch for decode rows), or the whole
+        # step in one call
+        joined = self.decode and self.index is None
         if self.decode and not joined:
             sa.append_kv(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp)
         elif self.k_cmp is not None and not self.decode:
             sa.compress(self.p, x["k"], self.k_cmp)
             if self.index is not None:      # the chunk's new cluster blocks; earlier ones are frozen
                 sa.bucket_build(self.p, self.k_cmp, self.index, build_from=self.build_from)
-        mark(1)
         if joined and self.fused_step:
             sa.decode_step(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp, x["q"], self.idx, self.n_idx,
                            out=self.out, ws=self.ws_step, events=None if events is None else events[2:4])
@@ -188,10 +183,30 @@ class Step:
         else:
             sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel,
                       events=events[0:2] if events is not None and self.time_select else None)
-        mark(2)
         sa.fwd(self.p, x["q"], x["k"], x["v"], self.idx, self.n_idx, out=self.out, ws=self.ws_fwd,
                events=None if events is None else events[2:4])
-        mark(3)
+
+
+    def stage(self, i):
+        """One of the three calls a step is made of, alone (as the stage pass times them):
+        0 compress (decode: append; with the bucket index: compress and the chunk's
+        clustering), 1 select, 2 fwd.  Each rewrites the same values, so repeating one
+        leaves the inputs of the others unchanged."""
+        x = self.x
+        if i == 0:
+            if self.decode:
+                sa.append_kv(self.p, self.k_new, self.v_new, x["k"], x["v"], self.k_cmp)
+            elif self.k_cmp is not None:
+                sa.compress(self.p, x["k"], self.k_cmp)
+                if self.index is not None:
+                    sa.bucket_build(self.p, self.k_cmp, self.index, build_from=self.build_from)
+        elif i == 1:
+            if self.index is not None:
+                sa.bucket_select(self.p, x["q"], self.index, self.w.bucket_topk, self.idx, self.n_idx, ws=self.ws_bkt)
+            else:
+                sa.select(self.p, x["q"], self.k_cmp, x["k"], self.idx, self.n_idx, ws=self.ws_sel)
+        else:
+            sa.fwd(self.p, x["q"], x["k"], x["v"], self.idx, self.n_idx, out=self.out, ws=self.ws_fwd)
 
 
 def attended_total_exact(w, idx_host, n_idx_host, per_unit=False):
@@ -575,8 +590,9 @@ def bench_workload(w, args, device, peaks, headline):
     """One workload at full size: W untimed steps, K timed steps bracketed by two events
     (nothing else recorded inside), then a kernel pass of the same steps with events
     around the selection's scoring kernel and the attention kernel (their launch
-    durations, on the stream they run on), a stage pass (events between the calls), and
-    the oracle on a bounded sample.  Returns the workload's figures."""
+    durations, on the stream they run on), a stage pass (each call of the step repeated
+    alone between two events), and the oracle on a bounded sample.  Returns the
+    workload's figures."""
     x = generate(w, device=device)
     torch.cuda.synchronize()
     if args.copy_probe_mib and headline:
@@ -622,12 +638,19 @@ def bench_workload(w, args, device, peaks, headline):
     score_ms = kev.mean_ms(0, 1) if step.time_select else None
     kev.close()
 
-    # per-stage times, from events recorded between the three calls, in a pass of its own
-    sev = TimingEvents(n_k, width=4)
-    for i in range(n_k):
-        step(stages=(sev, sev.pairs[i]))
-    torch.cuda.synchronize()
-    stage_ms = [sev.mean_ms(0, 1), sev.mean_ms(1, 2), sev.mean_ms(2, 3)]
+    # per-stage times: each of the three calls repeated n_k times back to back between two
+    # events (events between the calls of a step would also time the host's launch gaps
+    # once the recording host falls behind the GPU)
+    sev = TimingEvents(3, width=2)
+    stage_ms = []
+    for i in range(3):
+        step.stage(i)                                  # warm
+        sev.record(sev.pairs[i][0])
+        for _ in range(n_k):
+            step.stage(i)
+        sev.record(sev.pairs[i][1])
+        torch.cuda.synchronize()
+        stage_ms.append(sev.elapsed_ms(*sev.pairs[i]) / n_k)
     sev.close()
 
     idx_h, n_h = step.idx.cpu().numpy(), step.n_idx.cpu().numpy()

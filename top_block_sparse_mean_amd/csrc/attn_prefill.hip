@@ -337,9 +337,10 @@ __device__ __forceinline__ void wg_pv(const unsigned char *buf, int h, int rr, i
 // lazily, at most once per tile: only when the tile's max exceeds it by more than
 // `lazy` (2^8 after scaling), so unnormalised weights stay below 256 and the
 // output accumulators are rescaled rarely (a wavefront-uniform branch).  Any
-// reference gives the same normalised result.  A lane whose 8 logits of a half
-// are all masked gets scale 0 and offset -inf there, so its weights are
-// exp2(-inf) = 0 without a select per logit; per-logit masks (a -1e30 sentinel,
+// reference gives the same normalised result (the offset -m_run * scale is kept
+// with it, so the common path only compares).  A lane whose 8 logits of a half
+// are all masked gets offset -inf there, so its weights are exp2(-inf) = 0
+// without a select per logit; per-logit masks (a -1e30 sentinel,
 // which underflows to 0) are applied only when some lane has a partly live half
 // (causal edge, window or sink boundary).  exp2 is the hardware instruction
 // (results below 2^-126 flush to zero, which the sum cannot see next to the
@@ -380,12 +381,12 @@ __device__ __forceinline__ float max_xor32(float x)
 template <int MT>
 __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4, const bf16x8 (&qop)[MT][4],
                                         const uint32_t (&live)[2][MT], bool partial, float scale_log2, float lazy,
-                                        float (&m_run)[MT], f32x4 (&acc)[MT][9])
+                                        float (&m_run)[MT], float (&neg)[MT], f32x4 (&acc)[MT][9])
 {
     f32x4 st[2][MT][2];                                   // [half][row tile][16-token subtile]
     wg_qk<MT>(buf, 0, rr, g4, qop, st[0]);
     wg_qk<MT>(buf, 1, rr, g4, qop, st[1]);
-    if (partial) {                       // finite sentinel: a dead lane multiplies it by scale 0
+    if (partial) {                       // finite sentinel: far below any live logit
         // keep this a branch: executed unconditionally (as selects) it costs ~100
         // vector instructions per tile, and it is needed only at set boundaries
         __asm__ volatile("" ::);
@@ -397,7 +398,7 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
                 for (int i = 0; i < 8; i++)
                     st[h][a][i >> 2][i & 3] = (live[h][a] >> i) & 1u ? st[h][a][i >> 2][i & 3] : -1e30f;
     }
-    float neg[MT], m_old[MT];
+    float mcs[MT];
     bool bump[MT];
 #pragma unroll
     for (int a = 0; a < MT; a++) {
@@ -414,19 +415,21 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
         float mc = max2(mhv[0], mhv[1]);
         mc = max_xor16(mc);
         mc = max_xor32(mc);
+        mcs[a] = mc;
         bump[a] = mc > m_run[a] + lazy;
-        m_old[a] = m_run[a];
-        m_run[a] = bump[a] ? mc : m_run[a];
-        neg[a] = m_run[a] == -INFINITY ? 0.f : -m_run[a] * scale_log2;
     }
     bool any_bump = false;
 #pragma unroll
     for (int a = 0; a < MT; a++)
         any_bump = any_bump || bump[a];
     if (__ballot(any_bump)) {
+        // the reference moves (rarely): the offset -m_run * scale and the accumulators follow
 #pragma unroll
         for (int a = 0; a < MT; a++) {
-            const float alpha = bump[a] ? __builtin_amdgcn_exp2f(fmaf(m_old[a], scale_log2, neg[a])) : 1.f;
+            const float m_old = m_run[a];
+            m_run[a] = bump[a] ? mcs[a] : m_run[a];
+            neg[a] = bump[a] ? -m_run[a] * scale_log2 : neg[a];
+            const float alpha = bump[a] ? __builtin_amdgcn_exp2f(fmaf(m_old, scale_log2, neg[a])) : 1.f;
 #pragma unroll
             for (int qq = 0; qq < 4; qq++) {
                 const float f = __shfl(alpha, 4 * g4 + qq, kWave);
@@ -441,12 +444,11 @@ __device__ __forceinline__ void wg_tile(const unsigned char *buf, int rr, int g4
         bf16x8 aop[MT];
 #pragma unroll
         for (int a = 0; a < MT; a++) {
-            const bool lv = live[h][a] != 0u;
-            const float s_eff = lv ? scale_log2 : 0.f;
-            const float n_eff = lv ? neg[a] : -INFINITY;
+            // a dead half gets offset -inf: its (finite) logits weigh exp2(-inf) = 0
+            const float n_eff = live[h][a] != 0u ? neg[a] : -INFINITY;
 #pragma unroll
             for (int i = 0; i < 8; i++)
-                aop[a][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[h][a][i >> 2][i & 3], s_eff, n_eff));
+                aop[a][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[h][a][i >> 2][i & 3], scale_log2, n_eff));
         }
         wg_pv<MT>(buf, h, rr, g4, aop, acc);
     }
@@ -586,12 +588,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_wg_kernel(KP P, const uint16_
     // the wave's rows' window starts span [w_lo_min, w_lo_max]
     const int w_lo_min = max(P.n_init, wp_first - P.window + 1), w_lo_max = max(P.n_init, wp_last - P.window + 1);
 
-    float m_run[MT];
+    float m_run[MT], neg_run[MT];                         // reference max (raw logits), -m_run * scale
     const float lazy = 8.f / P.scale_log2;
     f32x4 acc[MT][9];                                     // [8]: row sums (ones column tile)
 #pragma unroll
     for (int a = 0; a < MT; a++) {
         m_run[a] = -INFINITY;
+        neg_run[a] = 0.f;                                 // set with m_run at a row's first live tile
 #pragma unroll
         for (int p = 0; p < 9; p++)
             acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_wg_kernel(KP P, const uint16_
             }
         }
         if (__ballot(any) != 0ull)
-            wg_tile<MT>(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, acc);
+            wg_tile<MT>(buf, rr, g4, qop, live, __ballot(part) != 0ull, P.scale_log2, lazy, m_run, neg_run, acc);
     };
     // whether this wavefront's rows can attend listed tile e at all
     auto needs = [&](int e) {

@@ -1,8 +1,9 @@
 """Scenarios for the library built with contract checks (run by test_gpu_contract_checks.py
 in a child process whose SPARSE_ATTN_LIB names libsparse_attn_checked.so).
 
-Valid calls on every workload's small shape (packed and paged, the full pass and a decode
-step) must set no check bit and still meet the oracle's bars; then three contract
+Valid calls on every workload's small shape (packed and paged, the full pass, the
+one-launch decode step and the append) must set no check bit and still meet the oracle's
+bars (the full passes); then three contract
 violations that the kernels clamp are planted one at a time in a decode table -- a
 selection entry far outside its row's candidate blocks, a selection count above topk,
 a negative page id -- and each must set its bit while the output stays finite.
@@ -52,6 +53,22 @@ def main():
     idx, n_idx = sa.select(p, xg["q"], kc, xg["k"])
     out = sa.fwd(p, xg["q"], xg["k"], xg["v"], idx, n_idx)
     report("valid_decode_calls")
+
+    # valid: the one-launch decode step (forced at this size) and the append, on a cache
+    # that already holds the step's tokens (they are rewritten with the same values)
+    last, off = [], 0
+    for nk in w.seqlens_k:
+        off += nk
+        last.append(off - 1)
+    last = torch.tensor(last, device="cuda")
+    k_new, v_new = xg["k"][last].contiguous(), xg["v"][last].contiguous()
+    os.environ["SPARSE_ATTN_SELECT_PLAN"] = "5"
+    out_s, _, idx_s, n_s = sa.decode_step(p, k_new, v_new, xg["k"], xg["v"], kc, xg["q"], want_lse=True)
+    del os.environ["SPARSE_ATTN_SELECT_PLAN"]
+    sa.append_kv(p, k_new, v_new, xg["k"], xg["v"], kc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_s.float()).all() and (n_s > 0).all()
+    report("valid_decode_step")
 
     layout = page_layout(w.seqlens_k, 16, w.seed + 7)   # valid: paged
     pp = paged_params(w, layout)

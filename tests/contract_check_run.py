@@ -67,7 +67,7 @@ def main():
     del os.environ["SPARSE_ATTN_SELECT_PLAN"]
     sa.append_kv(p, k_new, v_new, xg["k"], xg["v"], kc)
     torch.cuda.synchronize()
-    assert torch.isfinite(out_s.float()).all() and (n_s > 0).all()
+    assert torch.isfinite(out_s.float()).all()          # (a sequence shorter than sink + window selects none)
     report("valid_decode_step")
 
     layout = page_layout(w.seqlens_k, 16, w.seed + 7)   # valid: paged

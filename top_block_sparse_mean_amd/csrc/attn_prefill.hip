@@ -727,7 +727,7 @@ hipError_t launch_fwd_wg(const KP &P, const void *q, const void *k, const void *
                          const int32_t *n_idx, void *out, float *lse, void *ev0, void *ev1, hipStream_t st)
 {
     // 8 wavefronts of two row tiles: 16 wavefronts of one (four per SIMD, twice the LDS
-    // operand traffic per MFMA) measured 24.1 against 23.8 ms at 128K
+    // operand traffic per MFMA) measured 21.7 against 21.4 ms at 128K
     constexpr int NW = 8, MT = 2;
     const int qwg = NW * (16 * MT / P.G);
     const int n_qtile = (P.max_q + qwg - 1) / qwg;

@@ -1214,8 +1214,8 @@ constexpr int kStepWaves = 8;
 template <int D>
 __global__ __launch_bounds__(kStepWaves * 64) void decode_step_kernel(KP P, const uint16_t *__restrict__ q,
                                                            const float *__restrict__ k_cmp,
-                                                           const uint16_t *__restrict__ k,
-                                                           const uint16_t *__restrict__ v,
+                                                           const uint16_t *k,    // written too (the append)
+                                                           const uint16_t *v,
                                                            int32_t *__restrict__ idx, int32_t *__restrict__ n_idx,
                                                            uint16_t *__restrict__ out, float *__restrict__ lse,
                                                            SelAppend app)
@@ -1229,6 +1229,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void decode_step_kernel(KP P, cons
     __shared__ int sh_buf[kTokCap > kStepWaves * kStepRows * D ? kTokCap : kStepWaves * kStepRows * D];
     // (the token list, then the wavefronts' outputs)
     __shared__ int sh_pre[32 * kStepWaves];                  // rows of the fixed positions loaded early
+    __shared__ float sh_app[2048];                           // the append's partial sums (TG x D)
     // consecutive workgroups take the KV heads of one row: the XCDs (which receive
     // workgroups in turn) each serve one head
     const long long row = blockIdx.x / P.h_kv;
@@ -1250,22 +1251,59 @@ __global__ __launch_bounds__(kStepWaves * 64) void decode_step_kernel(KP P, cons
     const int n_pre = min(n_fix, 32 * kStepWaves);
     for (int x = tid; x < n_pre; x += blockDim.x)
         sh_pre[x] = kmap.row(aset_token(a0, nullptr, x));   // no selection: init, then window
+    // The step's append (the new token's cache rows, the re-pooled block that holds it)
+    // feeds no candidate of this selection (the block lies in the window), only the
+    // attention, which reads the new token: its loads go out with the prefetch, before
+    // the threshold search, and it is finished after the selection.  Run first, it held
+    // back every score load by its memory latency (about 6 us of a 72 us step).
+    const bool defer = app.n_blk > 0 && append_split_fits<D>(P);
+    SelAppend app_sel = app;
+    if (defer)
+        app_sel.n_blk = 0;
+    AppendSplit<D> aps;
+    uint4 aps_knew, aps_vnew;
+    long long aps_crow = -1;
+    bool aps_issued = false;
     ChunkRegs<D> ra, rb;
     bool loaded = false;                                      // ra holds this wavefront's first chunk
     auto prefetch = [&]() {
-        if (32 * w + 32 <= n_pre) {                           // the chunk lies wholly in the fixed part
+        if (defer) {
+            append_split_issue<D, 4>(P, s, kmap, (const uint16_t *)app.k_new, (const uint16_t *)app.v_new, k,
+                                     app.n_blk, c, aps, aps_knew, aps_vnew, aps_crow);
+            aps_issued = true;
+        }
+        // the chunk lies wholly in the fixed part (and, with the append still to come,
+        // before its last entry, the new token)
+        if (32 * w + 32 <= n_pre && (!defer || 32 * w + 32 < n_fix)) {
             load_chunk<D>(ra, sh_pre, 32 * w, n_pre, kb, vb, tstride, rr, g4, n_pre);
             loaded = true;
         }
     };
-    const int nsel = row_plan_select<uint16_t, float, D, kStepWaves>(P, q, k_cmp, idx, n_idx, app, row, c, sh_key,
-                                                                     sh_bits, sh_cnt, sh_sel, prefetch);
+    const int nsel = row_plan_select<uint16_t, float, D, kStepWaves>(P, q, k_cmp, idx, n_idx, app_sel, row, c,
+                                                                     sh_key, sh_bits, sh_cnt, sh_sel, prefetch);
+    if (defer) {
+        if (!aps_issued)                                      // a row that ranks nothing skips the hook
+            append_split_issue<D, 4>(P, s, kmap, (const uint16_t *)app.k_new, (const uint16_t *)app.v_new, k,
+                                     app.n_blk, c, aps, aps_knew, aps_vnew, aps_crow);
+        if (P.pool == 1)
+            append_split_commit<D, 4, 1>(aps, aps_knew, aps_vnew, aps_crow, (uint16_t *)app.k, (uint16_t *)app.v,
+                                         sh_app);
+        else
+            append_split_commit<D, 4, 0>(aps, aps_knew, aps_vnew, aps_crow, (uint16_t *)app.k, (uint16_t *)app.v,
+                                         sh_app);
+    }
     // the append wrote this sequence's new rows for head c, which the set reaches (its
     // window ends at the query); this workgroup alone reads them back, and the barrier's
     // workgroup-scope fences make its own stores visible to all its wavefronts (one
     // compute unit, one L1).  A device-scope fence here would write back and invalidate
     // the L2 once per workgroup (measured: +30 us per step).
     __syncthreads();
+    if (defer) {
+        if (P.pool == 1)
+            append_split_store<D, 4, 1>(P, aps, app.k_cmp, b, c, sh_app);
+        else
+            append_split_store<D, 4, 0>(P, aps, app.k_cmp, b, c, sh_app);
+    }
 
     const ASet a = aset_make(P, s.n_k, p, p, sh_sel, nsel);
     const int n = a.total;                                   // <= kTokCap (checked by the host)

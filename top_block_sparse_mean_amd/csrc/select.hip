@@ -548,7 +548,10 @@ __device__ __forceinline__ float slice_dot(const uint4 &raw, const float (&qv)[V
 }
 
 // grid: (rows * n_chunk, h_kv), CH candidates per workgroup in rounds of U x NG rows;
-// writes order keys to ws[(c*rows+row)*stride + j].  The loads of round r+1 are
+// writes order keys to ws[(c*rows+row)*stride + j].  n_chunk = 0: packed, workgroup
+// x takes the x-th chunk of the rows' actual chunks in row order (a row's chunks cover
+// its candidates; rows that keep every candidate have none), so rows far shorter than
+// the longest launch no empty workgroups.  The loads of round r+1 are
 // issued before round r is reduced; the selector slice is built while the first
 // round is in flight.  U = 8 key rows per lane group and round; 4 through a block
 // table (each key row waits for its page entry, and shorter rounds keep more of
@@ -562,8 +565,44 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     constexpr int L = RD::L, VPL = RD::VPL;
     constexpr int GPW = kWave / L, NG = 4 * GPW;
     constexpr int RW = U * NG;
-    const long long row = blockIdx.x / n_chunk;
-    const int chunk = (int)(blockIdx.x % n_chunk);
+    long long row;
+    int chunk;
+    if (n_chunk == 0) {
+        // every wavefront finds the same (row, chunk): the rows' chunk counts, 64 rows
+        // at a time, prefix-summed across the lanes
+        const int lane = lane_id(), x = (int)blockIdx.x;
+        int base = 0;
+        row = -1;
+        chunk = 0;
+        for (int r0 = 0; r0 < P.rows; r0 += kWave) {
+            const int rl = r0 + lane;
+            int nch = 0;
+            if (rl < P.rows) {
+                const RowGeo g = row_geo(P, rl);
+                nch = g.need == g.n_cand ? 0 : (g.n_cand + CH - 1) / CH;
+            }
+            int incl = nch;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int t = __shfl_up(incl, o, kWave);
+                if (lane >= o)
+                    incl += t;
+            }
+            const int tot = __shfl(incl, kWave - 1, kWave);
+            if (x < base + tot) {
+                const int l = __ffsll((long long)__ballot(base + incl > x)) - 1;
+                row = r0 + l;
+                chunk = x - base - (__shfl(incl, l, kWave) - __shfl(nch, l, kWave));
+                break;
+            }
+            base += tot;
+        }
+        if (row < 0)
+            return;
+    } else {
+        row = blockIdx.x / n_chunk;
+        chunk = (int)(blockIdx.x % n_chunk);
+    }
     const int c = blockIdx.y;
     RowGeo r = row_geo(P, row);
     if (r.need == r.n_cand)
@@ -2547,6 +2586,16 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
     } else if (plan == kSelectSplit) {
         int n_chunk = (int)((stride + kSplitChunk - 1) / kSplitChunk);
         dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
+        // One row per sequence, packed cache: the rows' candidates number at most
+        // total_k / g + rows, so at most (total_k / g + rows) / CH + rows chunks; launch
+        // those only (packed mapping) when that is fewer.
+        if (P.shared && !P.block_table && P.rows <= 1024) {
+            const long long bound = (P.total_k / P.g + P.rows) / kSplitChunk + P.rows + 1;
+            if (bound < (long long)P.rows * n_chunk && !getenv("SPARSE_ATTN_SPLIT_GRID")) {
+                grid.x = (unsigned)bound;
+                n_chunk = 0;
+            }
+        }
         if (P.g == 1 && P.block_table)
             score_rows_kernel<T, T, D, kSplitChunk, 4><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,
                                                                                  n_chunk);

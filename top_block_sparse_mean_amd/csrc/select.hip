@@ -548,15 +548,16 @@ __device__ __forceinline__ float slice_dot(const uint4 &raw, const float (&qv)[V
 }
 
 // grid: (rows * n_chunk, h_kv), CH candidates per workgroup in rounds of U x NG rows;
-// writes order keys to ws[(c*rows+row)*stride + j].  n_chunk = 0: packed, workgroup
-// x takes the x-th chunk of the rows' actual chunks in row order (a row's chunks cover
-// its candidates; rows that keep every candidate have none), so rows far shorter than
-// the longest launch no empty workgroups.  The loads of round r+1 are
+// writes order keys to ws[(c*rows+row)*stride + j].  PACKED: workgroup x takes the x-th
+// chunk of the rows' actual chunks in row order (a row's chunks cover its candidates;
+// rows that keep every candidate have none), so rows far shorter than the longest
+// launch no empty workgroups (n_chunk unused).  A variant of its own: the mapping's
+// registers would lower the rows x chunks kernel's occupancy (62 -> 77 VGPRs at U = 4).  The loads of round r+1 are
 // issued before round r is reduced; the selector slice is built while the first
 // round is in flight.  U = 8 key rows per lane group and round; 4 through a block
 // table (each key row waits for its page entry, and shorter rounds keep more of
 // those two-step loads in the pipeline: 237 against 253 us for the paged drafts).
-template <typename T, typename KT, int D, int CH, int U>
+template <typename T, typename KT, int D, int CH, int U, bool PACKED = false>
 __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restrict__ q,
                                                          const KT *__restrict__ kbase,
                                                          uint32_t *__restrict__ ws, long long stride, int n_chunk)
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
     constexpr int RW = U * NG;
     long long row;
     int chunk;
-    if (n_chunk == 0) {
+    if constexpr (PACKED) {
         // every wavefront finds the same (row, chunk): the rows' chunk counts, 64 rows
         // at a time, prefix-summed across the lanes
         const int lane = lane_id(), x = (int)blockIdx.x;
@@ -591,8 +592,8 @@ __global__ __launch_bounds__(256) void score_rows_kernel(KP P, const T *__restri
             const int tot = __shfl(incl, kWave - 1, kWave);
             if (x < base + tot) {
                 const int l = __ffsll((long long)__ballot(base + incl > x)) - 1;
-                row = r0 + l;
-                chunk = x - base - (__shfl(incl, l, kWave) - __shfl(nch, l, kWave));
+                row = __builtin_amdgcn_readfirstlane(r0 + l);
+                chunk = __builtin_amdgcn_readfirstlane(x - base - (__shfl(incl, l, kWave) - __shfl(nch, l, kWave)));
                 break;
             }
             base += tot;
@@ -2599,9 +2600,15 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         if (P.g == 1 && P.block_table)
             score_rows_kernel<T, T, D, kSplitChunk, 4><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,
                                                                                  n_chunk);
+        else if (P.g == 1 && n_chunk == 0)
+            score_rows_kernel<T, T, D, kSplitChunk, 8, true><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk,
+                                                                                       stride, n_chunk);
         else if (P.g == 1)
             score_rows_kernel<T, T, D, kSplitChunk, 8><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,
                                                                                  n_chunk);
+        else if (n_chunk == 0)
+            score_rows_kernel<T, float, D, kSplitChunk, 8, true><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk,
+                                                                                           stride, n_chunk);
         else
             score_rows_kernel<T, float, D, kSplitChunk, 8><<<grid, dim3(256), 0, st>>>(P, q, k_cmp, wsk, stride,
                                                                                      n_chunk);

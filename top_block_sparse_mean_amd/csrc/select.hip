@@ -2009,7 +2009,9 @@ __device__ __forceinline__ void for_each_key(const uint32_t *row, int j_lo, int 
 // maxima of the scoring (gmax, rows of >= 4k groups of 32 keys), step 0 instead
 // takes t0 = a value that k group maxima reach and reads only the groups whose
 // maximum reaches it (about k of them, k x 128 bytes instead of the whole row).
-__global__ __launch_bounds__(1024) void topk_compact_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
+// Two workgroups per CU (8 wavefronts per SIMD): the launch bounds keep the SGPRs at or
+// below the 100 that allows (102 without them held it to 7, one workgroup per CU).
+__global__ __launch_bounds__(1024, 8) void topk_compact_kernel(KP P, const uint32_t *__restrict__ ws, long long stride,
                                                             int32_t *__restrict__ idx, int32_t *__restrict__ n_idx,
                                                             const uint32_t *__restrict__ gmax, long long gstride)
 {

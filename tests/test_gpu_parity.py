@@ -246,6 +246,39 @@ def test_compress_tail_matches_full():
         assert torch.isnan(tail[:, b, :lo]).all()
 
 
+# ---------------------------------------------------------------- long tile unions
+
+def test_prefill_long_tile_union():
+    """Shared-tile prefill attention over long tile unions: iid scores over 768 blocks with
+    k = 64, so a 64-query workgroup walks most of the sequence's tiles, each tile live for
+    only some of its rows.  Sampled outputs and lse against the oracle on the GPU's own table."""
+    w = Workload(name="long_union", dtype=DTYPE_BF16, h_q=8, h_kv=2, head_dim=128, seqlens_k=[49152],
+                 seqlens_q=[512], block=64, pool=POOL_MEAN, topk=64, n_init=64, window=512, seed=31)
+    x, xg = parity.gen_pair(w)
+    gp = parity.run_gpu(w, xg)
+    # the union a 64-query workgroup walks: selected blocks + init + window tiles
+    q0 = w.seqlens_k[0] - w.seqlens_q[0]
+    longest = 0
+    for c in range(w.h_kv):
+        for t in range(0, w.seqlens_q[0], 64):
+            tiles = set()
+            for r in range(t, t + 64):
+                tiles.update(gp["idx"][c, r, :gp["n_idx"][c, r]].tolist())
+            p_first, p_last = q0 + t, q0 + t + 63
+            tiles.update(range(0, (min(w.n_init, p_last + 1) + 63) // 64))
+            tiles.update(range(max(w.n_init, p_first - w.window + 1) // 64, p_last // 64 + 1))
+            longest = max(longest, len(tiles))
+    assert longest > 700, f"the longest union has only {longest} tiles"
+    rng = np.random.default_rng(3)
+    reqs = rng.choice(w.total_q, size=384, replace=False)
+    hs = rng.integers(0, w.h_q, size=len(reqs))
+    att = oracle.attend(w, x["q"], x["k"], x["v"], gp["idx"], gp["n_idx"], reqs=reqs, heads=hs)
+    gout = gp["out"].reshape(w.total_q, w.h_q, w.head_dim)[reqs, hs].double().numpy()
+    parity.check_output(w, gout, att["out"])
+    lse_g = gp["lse"][torch.from_numpy(hs), torch.from_numpy(reqs)].double().numpy()
+    assert np.abs(lse_g - att["lse"]).max() < parity.lse_tol(w)
+
+
 # ---------------------------------------------------------------- full size, sampled
 
 def _sampled(w, n_rows, n_req, seed=0):

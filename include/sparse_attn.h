@@ -99,7 +99,8 @@ typedef struct sa_params {
     const int32_t *q_pos0;     /* device [batch] absolute position of query 0, or NULL  */
     int32_t block;             /* g >= 1 tokens per pooled block (g = 1: token level)   */
     int32_t pool;              /* sa_pool                                               */
-    int32_t topk;              /* k >= 0 blocks per row; the row capacity of `idx`      */
+    int32_t topk;              /* k in [0, 2^24] blocks per row; the row capacity of `idx`
+                                  (larger: SA_ERR_UNSUPPORTED)                          */
     const int32_t *topk_per_seq; /* device [batch] per-sequence k (each <= topk), or NULL */
     int32_t n_init;            /* sink tokens >= 0                                      */
     int32_t window;            /* local window in tokens >= 1                           */

@@ -111,7 +111,7 @@ def test_status_strings():
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, INVALID), ("h_q", 7, INVALID), ("h_kv", 0, INVALID), ("head_dim", 96, UNSUPPORTED),
     ("max_q", 0, INVALID), ("max_k", 0, INVALID), ("total_k", 0, INVALID), ("total_q", 0, INVALID), ("cu_seqlens_q", None, INVALID),
-    ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID),
+    ("cu_seqlens_k", None, INVALID), ("block", 0, INVALID), ("pool", 7, INVALID), ("topk", -1, INVALID), ("topk", (1 << 24) + 1, UNSUPPORTED),
     ("n_init", -2, INVALID), ("window", 0, INVALID), ("shared_selection", 2, INVALID), ("dtype", 5, INVALID),
     ("softmax_scale", -1.0, INVALID), ("softmax_scale", float("inf"), INVALID),
     ("pool_overlap", -1, INVALID), ("pool_overlap", (1 << 20) + 1, INVALID),

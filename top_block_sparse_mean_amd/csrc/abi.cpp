@@ -67,6 +67,8 @@ sa_status check_params(const sa_params *p)
         return fail(SA_ERR_INVALID_ARG, "unknown pool mode %d", p->pool);
     if (p->topk < 0)
         return fail(SA_ERR_INVALID_ARG, "topk must be >= 0 (got %d)", p->topk);
+    if (p->topk > (1 << 24))                       // kernels index a row group's entries in 32 bits
+        return fail(SA_ERR_UNSUPPORTED, "topk above 2^24 is not supported (got %d)", p->topk);
     if (p->n_init < 0)
         return fail(SA_ERR_INVALID_ARG, "n_init must be >= 0 (got %d)", p->n_init);
     if (p->window < 1)

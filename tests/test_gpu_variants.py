@@ -134,6 +134,13 @@ def test_attention_mass_refresh(name):
     parity.check_select(w, x, None, idx.cpu().numpy(), n_idx.cpu().numpy())
 
 
+def test_attention_mass_refresh_vector_kernel(monkeypatch):
+    """Draft rows (bf16 token keys, <= 16 (query, head) pairs) take the matrix-core scorer;
+    the vector scorer, which serves every other shape, on the same rows."""
+    monkeypatch.setenv("SPARSE_ATTN_ATTN_VALU", "1")
+    test_attention_mass_refresh("bf16_draft_decode")
+
+
 def test_attention_mass_refresh_paged():
     w = small("bf16_draft_decode").scaled(select_mode=SELECT_ATTN)
     x, xg = parity.gen_pair(w)

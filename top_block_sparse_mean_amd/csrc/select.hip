@@ -835,6 +835,105 @@ __global__ __launch_bounds__(256) void score_attn_kernel(KP P, const T *__restri
     }
 }
 
+// SA_SELECT_ATTN for token candidates (g = 1) of bf16 keys (d = 128) and rows of at
+// most 16 (query, head) pairs -- an S3R refresh after a draft round.  Same grid and
+// output as score_attn_kernel; the dot products run on the bf16 matrix cores instead:
+// S^T = K Q^T per 16-token chunk (16 tokens x 32 of d per product, the keys loaded
+// straight from HBM in operand layout, the row's pairs resident as B operands; bf16
+// products are exact and accumulate in fp32, as in the vector kernel's fp32 FMAs).
+// Lane (rr, g4) ends with tokens 4 g4 .. 4 g4 + 3 of a chunk against pair rr; each
+// takes exp2(s scale log2e - lse) and the 16 pairs of a token are summed by fixed
+// 16-lane DPP exchanges.  Wavefront w takes chunks w, w + 4, ... of the workgroup's span,
+// U chunks per round, one round's loads in flight while the previous is reduced.
+template <int CH>
+__global__ __launch_bounds__(256) void score_attn_mfma_kernel(KP P, const uint16_t *__restrict__ q,
+                                                              const uint16_t *__restrict__ k,
+                                                              uint32_t *__restrict__ ws, long long stride,
+                                                              int n_chunk)
+{
+    constexpr int D = 128, KS = D / 32, U = 2, NWV = 4;
+    const long long row = blockIdx.x / n_chunk;
+    const int chunk = (int)(blockIdx.x % n_chunk);
+    const int c = blockIdx.y;
+    const RowGeo r = row_geo(P, row);
+    if (r.need == r.n_cand)
+        return;
+    const int j0 = r.j_lo + chunk * CH;
+    const int j1 = min(j0 + CH, r.j_hi);
+    if (j0 >= j1)
+        return;
+    const int lane = lane_id(), w = threadIdx.x / kWave, rr = lane & 15, g4 = lane >> 4;
+    const int R = (int)(r.q_last - r.q_first) * P.G;        // <= 16 (checked by the host)
+    constexpr float kLog2e = 1.4426950408889634f;
+    bf16x8 qop[KS];
+    float lb = INFINITY;                                     // pairs past R weigh exp2(-inf) = 0
+    if (rr < R) {
+        const long long i = r.q_first + rr / P.G;
+        const long long h = (long long)c * P.G + rr % P.G;
+        const uint16_t *qp = q + (i * P.h_q + h) * D + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
+        lb = P.attn_lse[h * P.total_q + i] * kLog2e;
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    const float sc = P.scale * kLog2e;
+    const KvMap kmap = kv_map(P, r.b);
+    const uint16_t *kb = k + (P.block_table ? 0 : r.k_off * P.h_kv) * D + (long long)c * D + 8 * g4;
+    uint32_t *keys = ws + ((long long)c * P.rows + row) * stride + key_col0(P);
+    const int n16 = (j1 - j0 + 15) / 16;
+    const int rounds = (n16 + NWV * U - 1) / (NWV * U);
+    u32x4 ra[U][KS], rb[U][KS];
+    auto load = [&](u32x4 (&a)[U][KS], int rd) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int ch = (rd * U + u) * NWV + w;
+            const int t = min(min(j0 + 16 * ch + rr, j1 - 1), r.n_k - 1);   // g = 1: candidate j is token j
+            const uint16_t *kp = kb + (long long)kmap.row(t) * P.h_kv * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                a[u][ks] = ld16(kp + 32 * ks);
+        }
+    };
+    auto reduce = [&](const u32x4 (&a)[U][KS], int rd) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][ks]), qop[ks], sv, 0, 0,
+                                                             0);
+            float m[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                m[e] = exp2f(sv[e] * sc - lb);
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                m[e] = group_sum<16>(m[e]);                   // the 16 pairs of token 4 g4 + e
+            const int jb = j0 + 16 * ((rd * U + u) * NWV + w) + 4 * g4;
+            if (rr == 0)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if (jb + e < j1)
+                        keys[jb + e] = order_key(m[e]);
+        }
+    };
+    load(ra, 0);
+    for (int rd = 0; rd < rounds; rd += 2) {
+        if (rd + 1 < rounds)
+            load(rb, rd + 1);
+        reduce(ra, rd);
+        if (rd + 1 >= rounds)
+            break;
+        if (rd + 2 < rounds)
+            load(ra, rd + 2);
+        reduce(rb, rd + 1);
+    }
+}
+
 // Sum over a 256-thread workgroup (or max), in a fixed order: the result does not
 // depend on timing.  Every thread gets the result.
 template <bool MAX>
@@ -2560,7 +2659,17 @@ static hipError_t launch_select_t(const KP &P, const void *q_sel, const float *k
         const int n_chunk = (int)((stride + ch - 1) / ch);
         dim3 grid((unsigned)(P.rows * n_chunk), (unsigned)P.h_kv);
         if (P.select_mode == 3) {
-            if (small)
+            // bf16 token keys and rows of <= 16 (query, head) pairs: the matrix-core scorer
+            const bool mma = sizeof(T) == 2 && D == 128 && P.g == 1 &&
+                             (long long)(P.shared ? P.max_q : 1) * P.G <= 16 && !getenv("SPARSE_ATTN_ATTN_VALU");
+            if (mma && small)
+                score_attn_mfma_kernel<128><<<grid, dim3(256), 0, st>>>(P, (const uint16_t *)q, (const uint16_t *)k,
+                                                                      wsk, stride, n_chunk);
+            else if (mma)
+                score_attn_mfma_kernel<kSplitChunk><<<grid, dim3(256), 0, st>>>(P, (const uint16_t *)q,
+                                                                              (const uint16_t *)k, wsk, stride,
+                                                                              n_chunk);
+            else if (small)
                 score_attn_kernel<T, D, 128><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride, n_chunk);
             else
                 score_attn_kernel<T, D, kSplitChunk><<<grid, dim3(256), 0, st>>>(P, q, (const T *)k, wsk, stride,

@@ -117,9 +117,11 @@ class Step:
             self.w = w
         self.p = make_params(w, device, self.layout)
         self.decode = w.name in DECODE
-        # decode rows: the step is one sparse_attn_decode_step call (append, select and
-        # attend in one launch); the kernel pass brackets that launch
-        self.fused_step = self.decode and not w.shared_selection and w.block > 1 and not buckets
+        # decode rows with the summed group score: the step is one sparse_attn_decode_step
+        # call (append, select and attend in one launch); the kernel pass brackets that
+        # launch.  The variant group scores run append+select, then fwd.
+        self.fused_step = self.decode and not w.shared_selection and w.block > 1 and not buckets and \
+            w.select_mode == 0
         # the kernel pass brackets the selection's scoring kernel (not with the bucket
         # index, nor when the step is one launch)
         self.time_select = not buckets and not self.fused_step
@@ -769,6 +771,40 @@ def bench_workload(w, args, device, peaks, headline):
 # draft round is the other decode-shaped workload.  The tiny fp32 workload is a parity case.
 SECONDARY = ("bf16_prefill_128k", "bf16_chunked_prefill_1m", "bf16_draft_decode")
 
+# The pieces that come after the path, each at full size on the workload it serves: a
+# paged cache, the selector variants, the LSA bucket index and the rest of an S3R round
+# (name: workload, option overrides, workload field overrides).
+NEXT_ROWS = (
+    ("paged16_decode", "bf16_decode_32k", {"page_size": 16}, {}),
+    ("select_max_decode", "bf16_decode_32k", {}, {"select_mode": 2}),
+    ("select_softmax_decode", "bf16_decode_32k", {}, {"select_mode": 1}),
+    ("pool_overlap32_decode", "bf16_decode_32k", {}, {"pool_overlap": 32}),
+    ("lsa_buckets_1m", "bf16_chunked_prefill_1m", {"lsa_buckets": True}, {}),
+    ("s3r_round", "bf16_draft_decode", {"s3r_refresh": True}, {}),
+)
+
+
+def next_rows(args, device, peaks):
+    """The NEXT_ROWS variants, each one bench_workload run without the oracle baseline;
+    per row its value, its dominant kernel's roofline and, for the S3R round, the verify
+    and refresh legs."""
+    rows = {}
+    for key, name, opts, fields in NEXT_ROWS:
+        a = argparse.Namespace(**{**vars(args), "page_size": 0, "lsa_buckets": False, "s3r_refresh": False,
+                                  "copy_probe_mib": 0, "no_cpu_baseline": True, **opts})
+        r = bench_workload(FULL[name]().scaled(**fields), a, device, peaks, headline=True)
+        print(f"# {key}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
+        roof = r["roofline"]
+        row = {"workload": name, "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
+               "config": {k: r["config"][k] for k in ("kv_layout", "select_mode", "pool_overlap", "selector")},
+               "roofline": {k: roof.get(k) for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")}}
+        if "select_plus_attn" in r:
+            row["select_plus_attn_frac"] = r["select_plus_attn"]["frac"]
+        if "s3r" in r:
+            row["s3r"] = r["s3r"]
+        rows[key] = row
+    return rows
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -850,6 +886,8 @@ def main():
         res["prefill"] = prefill
     if other:
         res["other_decode"] = other
+    if not args.workload:
+        res["next_rows"] = next_rows(args, device, peaks)
     print(json.dumps(res), flush=True)
 
 

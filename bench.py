@@ -806,7 +806,7 @@ def next_rows(args, device, peaks):
     return rows
 
 
-def main():
+def arg_parser():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -835,7 +835,11 @@ def main():
     ap.add_argument("--record-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: write the workload's counter record under profiles/ from the output "
                          "directories of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = arg_parser().parse_args()
     if args.record_counters:
         if args.workload is None:
             raise SystemExit("--record-counters needs --workload")

@@ -44,3 +44,17 @@ def test_attended_totals_match_the_oracle(name):
         q_off = np.cumsum([0] + list(w.seqlens_q))
         want = sum(int(per_qkv[q_off[b]:q_off[b + 1], c].max()) for b in range(w.batch) for c in range(w.h_kv))
         assert bench.attended_total_exact(w, idx, n, per_unit=True) == want
+
+
+def test_next_rows_name_real_options():
+    """Every variant the default line measures names a workload, options the script parses
+    and workload fields that exist."""
+    import dataclasses
+    dests = {a.dest for a in bench.arg_parser()._actions}
+    fields = {f.name for f in dataclasses.fields(FULL["bf16_decode_32k"]())}
+    assert {"page_size", "lsa_buckets", "s3r_refresh", "no_cpu_baseline"} <= dests
+    for key, name, opts, wfields in bench.NEXT_ROWS:
+        assert name in FULL, key
+        assert set(opts) <= dests, key
+        assert set(wfields) <= fields, key
+        assert FULL[name]().scaled(**wfields).name == name

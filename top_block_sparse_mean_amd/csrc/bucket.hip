@@ -37,11 +37,17 @@ __device__ __forceinline__ float ward_cost(const float *sa, int na, const float 
     return acc * (1.0f / (float)(na * nb * (na + nb)));
 }
 
-// grid: h_kv * batch * nblk workgroups of 256 threads, one per (KV head, sequence, block).
-template <int D>
-__global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__restrict__ k_cmp, BucketArgs B)
+// grid: h_kv * batch * nblk workgroups of NT threads, one per (KV head, sequence, block).
+// The sums and costs take most of a CU's LDS, so one workgroup runs per CU: NT = 1024
+// puts four wavefronts on each SIMD to cover the LDS latency of the cost loops (with one
+// wavefront per SIMD a round took about 125 us).  Member sums are kept at a pitch of
+// D + 1 floats, so the lanes of a wavefront, each on its own partner bucket, read
+// distinct LDS banks at every step of the cost loop.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__restrict__ k_cmp, BucketArgs B)
 {
-    __shared__ float sh_s[kBucketMaxM * D];
+    constexpr int PS = D + 1;
+    __shared__ float sh_s[kBucketMaxM * PS];
     __shared__ float sh_w[kBucketMaxM * kBucketMaxM];
     __shared__ int sh_size[kBucketMaxM], sh_alive[kBucketMaxM], sh_root[kBucketMaxM], sh_nn[kBucketMaxM];
     __shared__ int sh_into[kBucketMaxM], sh_pair[kBucketMaxM], sh_bk[kBucketMaxM], sh_off[kBucketMaxM + 1];
@@ -59,16 +65,16 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
     int32_t *off = B.offset + item * (NB + 1);
     float *cen = B.centroid + item * (long long)NB * D;
     if ((long long)(blk + 1) * B.C > s.n_k) {                 // incomplete block: no buckets
-        for (int x = tid; x < M; x += 256)
+        for (int x = tid; x < M; x += NT)
             mem[x] = -1;
-        for (int x = tid; x <= NB; x += 256)
+        for (int x = tid; x <= NB; x += NT)
             off[x] = 0;
         return;
     }
     const float *src = k_cmp + (((long long)c * P.batch + b) * P.nb_max + (long long)blk * M) * D;
-    for (int x = tid; x < M * D; x += 256)
-        sh_s[x] = src[x];
-    for (int x = tid; x < M; x += 256) {
+    for (int x = tid; x < M * D; x += NT)
+        sh_s[(x / D) * PS + x % D] = src[x];
+    for (int x = tid; x < M; x += NT) {
         sh_size[x] = 1;
         sh_alive[x] = 1;
         sh_root[x] = x;
@@ -79,13 +85,13 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
     while (count > NB) {
         // pair costs, lower name first; a pair of two unchanged buckets keeps its cost
         // (the same arithmetic on the same sums and sizes)
-        for (int pi = tid; pi < M * M; pi += 256) {
+        for (int pi = tid; pi < M * M; pi += NT) {
             const int a = pi / M, o = pi % M;
             if (o <= a || !(sh_chg[a] | sh_chg[o]))
                 continue;
             float wv = INFINITY;
             if (sh_alive[a] && sh_alive[o] && sh_size[a] + sh_size[o] <= capg)
-                wv = ward_cost(sh_s + a * D, sh_size[a], sh_s + o * D, sh_size[o], D);
+                wv = ward_cost(sh_s + a * PS, sh_size[a], sh_s + o * PS, sh_size[o], D);
             sh_w[a * M + o] = wv;
             sh_w[o * M + a] = wv;
         }
@@ -94,9 +100,10 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
             int best = -1;
             float bc = INFINITY;
             if (sh_alive[tid])
-                for (int o = 0; o < M; o++) {
+                for (int i = 0; i < M; i++) {
+                    const int o = (i + tid) % M;             // rotated: the lanes' rows hit distinct banks
                     const float wv = o == tid ? INFINITY : sh_w[tid * M + o];
-                    if (wv < bc) {
+                    if (wv < bc || (wv == bc && wv < INFINITY && o < best)) {
                         bc = wv;
                         best = o;
                     }
@@ -125,10 +132,10 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
                 sh_into[sh_nn[tid]] = tid;
         }
         __syncthreads();
-        for (int x = tid; x < M * D; x += 256) {             // S_a += S_o (pairs are disjoint)
+        for (int x = tid; x < M * D; x += NT) {             // S_a += S_o (pairs are disjoint)
             const int a = sh_into[x / D];
             if (a >= 0)
-                sh_s[a * D + x % D] += sh_s[x];
+                sh_s[a * PS + x % D] += sh_s[(x / D) * PS + x % D];
         }
         if (tid < M)
             sh_chg[tid] = 0;
@@ -175,18 +182,18 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(KP P, const float *__
         off[NB] = M;
     // centroids: one wavefront per bucket
     const int w = tid / kWave, lane = tid % kWave;
-    for (int a = w; a < M; a += 4) {
+    for (int a = w; a < M; a += NT / kWave) {
         if (!sh_alive[a] || sh_bk[a] >= NB)
             continue;
         float ss = 0.f;
         for (int e = lane; e < D; e += kWave)
-            ss += sh_s[a * D + e] * sh_s[a * D + e];
+            ss += sh_s[a * PS + e] * sh_s[a * PS + e];
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1)
             ss += __shfl_xor(ss, o, kWave);
         const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
         for (int e = lane; e < D; e += kWave)
-            cen[(long long)sh_bk[a] * D + e] = sh_s[a * D + e] * inv;
+            cen[(long long)sh_bk[a] * D + e] = sh_s[a * PS + e] * inv;
     }
 }
 
@@ -300,10 +307,11 @@ hipError_t launch_bucket_build(const KP &P, const float *k_cmp, const BucketArgs
     if (B.from >= B.nblk)
         return hipSuccess;
     const long long items = (long long)P.h_kv * P.batch * (B.nblk - B.from);
+    constexpr int NT = 1024;
     if (P.d == 128)
-        bucket_build_kernel<128><<<dim3((unsigned)items), dim3(256), 0, st>>>(P, k_cmp, B);
+        bucket_build_kernel<128, NT><<<dim3((unsigned)items), dim3(NT), 0, st>>>(P, k_cmp, B);
     else
-        bucket_build_kernel<64><<<dim3((unsigned)items), dim3(256), 0, st>>>(P, k_cmp, B);
+        bucket_build_kernel<64, NT><<<dim3((unsigned)items), dim3(NT), 0, st>>>(P, k_cmp, B);
     return hipGetLastError();
 }
 

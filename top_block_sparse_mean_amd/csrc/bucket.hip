@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__r
             float bc = INFINITY;
             if (sh_alive[tid])
                 for (int i = 0; i < M; i++) {
-                    const int o = (i + tid) % M;             // rotated: the lanes' rows hit distinct banks
+                    const int o = i + tid < M ? i + tid : i + tid - M;   // rotated: the lanes hit distinct banks
                     const float wv = o == tid ? INFINITY : sh_w[tid * M + o];
                     if (wv < bc || (wv == bc && wv < INFINITY && o < best)) {
                         bc = wv;

@@ -17,13 +17,13 @@
 // blocks that end at or before the row's selection position (the ordinary
 // scoring and top-k kernels, run over the centroid table), and the chosen buckets
 // are expanded to their member groups, sorted ascending into the row's table.
+#include "mfma_common.hpp"
 #include "sa_common.hpp"
 #include "sa_internal.hpp"
 
 namespace sa {
 
 constexpr int kBucketMaxM = 128;     // pooled groups per cluster block
-constexpr int kExpandMax = 4096;     // groups one row's table can hold
 
 __device__ __forceinline__ float ward_cost(const float *sa, int na, const float *sb, int nb, int d)
 {
@@ -201,15 +201,22 @@ __global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__r
 // to their member groups (block * M + member); groups wholly inside the sink or the
 // window are left out (they are attended anyway, as for block candidates), so the
 // table keeps the attention's shape: only its first group may reach into the sink
-// and only its last into the window.  Sorted ascending (bitonic, in LDS) and written
-// -1 padded to the row's table of width P.topk.
+// and only its last into the window.  Written ascending, -1 padded to the row's table
+// of width P.topk.  The chosen buckets ascend by block, so the groups of different
+// blocks are already in order and only a block's own buckets interleave: each block
+// of the row (a segment) marks its kept members in a 128-bit mask, and the segments
+// emit their set bits in order at offsets from a scan of their counts.  A group
+// belongs to one bucket, so the list has no repeats.  The host keeps the expansion
+// within the table (topk >= n_buckets * cap / g, topk <= 4096).
 __global__ __launch_bounds__(256) void bucket_expand_kernel(KP P, BucketArgs B, const int32_t *__restrict__ tbl,
                                                             const int32_t *__restrict__ tn, int kb,
                                                             int32_t *__restrict__ idx, int32_t *__restrict__ n_idx)
 {
-    __shared__ int sh_g[kExpandMax];
-    __shared__ int sh_scan[4];
-    __shared__ int sh_drop;
+    constexpr int NT = 256, PER = 4;                      // chosen buckets per thread (kb <= 1024)
+    constexpr int MW = kBucketMaxM / 32;                  // mask words per segment
+    __shared__ uint32_t sh_mask[NT * PER * MW];
+    __shared__ int sh_segblk[NT * PER];
+    __shared__ int sh_scan[NT / kWave];
     const long long row = blockIdx.x;
     const int c = blockIdx.y, tid = threadIdx.x;
     const int M = B.C / P.g, NB = B.NB;
@@ -221,83 +228,88 @@ __global__ __launch_bounds__(256) void bucket_expand_kernel(KP P, BucketArgs B, 
     int nsel = tn[(long long)c * P.rows + row];
     nsel = nsel < 0 ? 0 : (nsel > kb ? kb : nsel);
     const int32_t *t = tbl + ((long long)c * P.rows + row) * kb;
-    // each thread: up to 4 buckets (kb <= 1024); counts, then an exclusive scan
-    int cnt[4], first[4], blk_of[4];
-    int mine = 0;
+    // this thread's chosen buckets and whether each starts a new block (segment)
+    int blk_of[PER], lb_of[PER];
+    bool starts[PER];
+    int nstart = 0;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int sidx = tid * 4 + u;
-        cnt[u] = 0;
-        first[u] = 0;
-        blk_of[u] = 0;
+    for (int u = 0; u < PER; u++) {
+        const int sidx = tid * PER + u;
+        blk_of[u] = -1;
+        lb_of[u] = 0;
+        starts[u] = false;
         if (sidx < nsel) {
-            const int j = t[sidx], blk = j / NB, lb = j % NB;
-            const int32_t *off = B.offset + (base_bc + blk) * (NB + 1);
-            first[u] = off[lb];
-            cnt[u] = off[lb + 1] - off[lb];
-            blk_of[u] = blk;
+            const int j = t[sidx];
+            blk_of[u] = j / NB;
+            lb_of[u] = j % NB;
+            starts[u] = sidx == 0 || t[sidx - 1] / NB != blk_of[u];
+            nstart += starts[u] ? 1 : 0;
         }
+    }
+    const int2 ss = block_scan_int_nt<NT>(nstart, sh_scan);   // ends with a barrier
+    const int nseg = ss.y;
+    for (int x = tid; x < nseg * MW; x += NT)
+        sh_mask[x] = 0u;
+    int seg = ss.x - 1;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        seg += starts[u] ? 1 : 0;
+        if (starts[u])
+            sh_segblk[seg] = blk_of[u];
+    }
+    __syncthreads();
+    // each kept member sets its bit in its block's mask
+    seg = ss.x - 1;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        seg += starts[u] ? 1 : 0;
+        if (blk_of[u] < 0)
+            continue;
+        const int32_t *off = B.offset + (base_bc + blk_of[u]) * (NB + 1);
+        const int32_t *mem = B.member + (base_bc + blk_of[u]) * M;
+        for (int x = off[lb_of[u]]; x < off[lb_of[u] + 1]; x++) {
+            const int m = mem[x], grp = blk_of[u] * M + m;
+            if (grp * P.g < hi && (grp + 1) * P.g > P.n_init)
+                atomicOr(&sh_mask[seg * MW + (m >> 5)], 1u << (m & 31));
+        }
+    }
+    __syncthreads();
+    // segments in order: counts, a scan, then each segment's groups ascending
+    int cnt[PER], mine = 0;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        const int sg = tid * PER + u;
+        cnt[u] = 0;
+        if (sg < nseg)
+#pragma unroll
+            for (int q = 0; q < MW; q++)
+                cnt[u] += __popc(sh_mask[sg * MW + q]);
         mine += cnt[u];
     }
-    // block exclusive scan of `mine` over 256 threads
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_up(incl, o, kWave);
-        if ((tid % kWave) >= o)
-            incl += v;
-    }
-    if (tid % kWave == kWave - 1)
-        sh_scan[tid / kWave] = incl;
-    if (tid == 0)
-        sh_drop = 0;
-    __syncthreads();
-    int wbase = 0, total = 0;
-    for (int x = 0; x < 4; x++) {
-        wbase += x < tid / kWave ? sh_scan[x] : 0;
-        total += sh_scan[x];
-    }
-    int pos = wbase + incl - mine;
-    total = total < kExpandMax ? total : kExpandMax;
-    int drop = 0;
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int32_t *mem = B.member + (base_bc + blk_of[u]) * M;
-        for (int x = 0; x < cnt[u]; x++, pos++)
-            if (pos < kExpandMax) {
-                const int grp = blk_of[u] * M + mem[first[u] + x];
-                const bool keep = grp * P.g < hi && (grp + 1) * P.g > P.n_init;
-                sh_g[pos] = keep ? grp : 0x7fffffff;           // left-out groups sort to the end
-                drop += keep ? 0 : 1;
-            }
-    }
-    if (drop)
-        atomicAdd(&sh_drop, drop);
-    int n2 = 1;
-    while (n2 < total)
-        n2 <<= 1;
-    for (int x = total + tid; x < n2; x += 256)
-        sh_g[x] = 0x7fffffff;
-    __syncthreads();
-    const int kept = total - sh_drop;
-    for (int k = 2; k <= n2; k <<= 1)                       // bitonic sort, ascending
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < n2; i += 256) {
-                const int l = i ^ jj;
-                if (l > i) {
-                    const int a = sh_g[i], bv = sh_g[l];
-                    const bool up = (i & k) == 0;
-                    if ((a > bv) == up) {
-                        sh_g[i] = bv;
-                        sh_g[l] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    const int2 os = block_scan_int_nt<NT>(mine, sh_scan);
+    const int kept = os.y;
     int32_t *out = idx + ((long long)c * P.rows + row) * P.topk;
-    for (int x = tid; x < P.topk; x += 256)
-        out[x] = x < kept ? sh_g[x] : -1;
+    int pos = os.x;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        const int sg = tid * PER + u;
+        if (sg >= nseg)
+            continue;
+        const int gb = sh_segblk[sg] * M;
+#pragma unroll
+        for (int q = 0; q < MW; q++) {
+            uint32_t bits = sh_mask[sg * MW + q];
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1;
+                if (pos < P.topk)
+                    out[pos] = gb + 32 * q + bit;
+                pos++;
+            }
+        }
+    }
+    for (int x = kept + tid; x < P.topk; x += NT)
+        out[x] = -1;
     if (tid == 0)
         n_idx[(long long)c * P.rows + row] = kept;
 }

@@ -96,6 +96,16 @@ SHAPES = {
                                    seqlens_k=[3000, 1500, 700], seqlens_q=[1, 1, 1], block=8, pool=POOL_MEAN,
                                    topk=1, n_init=8, window=64, seed=91, bucket_block=256, bucket_count=16,
                                    bucket_cap=32, bucket_topk=5),
+    # 15 groups per cluster block (not a multiple of the 8 lanes a bucket's searches use)
+    "odd_groups": lambda: Workload(name="bkt3", dtype=DTYPE_BF16, h_q=8, h_kv=2, head_dim=128,
+                                   seqlens_k=[2400, 1100], seqlens_q=[1, 1], block=4, pool=POOL_MEAN,
+                                   topk=1, n_init=4, window=64, seed=93, bucket_block=60, bucket_count=8,
+                                   bucket_cap=16, bucket_topk=6),
+    # 6 groups per cluster block (fewer than those 8 lanes)
+    "few_groups": lambda: Workload(name="bkt4", dtype=DTYPE_BF16, h_q=4, h_kv=1, head_dim=64,
+                                   seqlens_k=[1500, 800], seqlens_q=[1, 1], block=4, pool=POOL_MEAN,
+                                   topk=1, n_init=4, window=32, seed=94, bucket_block=24, bucket_count=3,
+                                   bucket_cap=16, bucket_topk=5),
     # per-query rows of a prefill chunk, L2SUM, drafts-style shared rows off
     "prefill_rows": lambda: Workload(name="bkt2", dtype=DTYPE_BF16, h_q=4, h_kv=1, head_dim=128,
                                      seqlens_k=[6000], seqlens_q=[700], block=4, pool=POOL_L2SUM, topk=1, n_init=4,

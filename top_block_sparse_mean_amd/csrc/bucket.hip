@@ -81,6 +81,10 @@ __global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__r
         sh_chg[x] = 1;
     }
     int count = M;
+    // the per-bucket searches of a round: LP consecutive lanes per bucket
+    constexpr int LP = NT / kBucketMaxM;
+    static_assert(LP >= 1 && LP <= kWave && (LP & (LP - 1)) == 0, "lanes per bucket: a power of two within a wavefront");
+    const int r_lp = tid / LP, part_lp = tid % LP;
     __syncthreads();
     while (count > NB) {
         // pair costs, lower name first; a pair of two unchanged buckets keeps its cost
@@ -96,21 +100,36 @@ __global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__r
             sh_w[o * M + a] = wv;
         }
         __syncthreads();
-        if (tid < M) {                                       // cheapest partner, ties to the lower name
+        {   // cheapest partner, ties to the lower name: the (cost, name) minimum of a bucket's
+            // row, LP lanes each over the partners o = part (mod LP), then combined
             int best = -1;
             float bc = INFINITY;
-            if (sh_alive[tid])
-                for (int i = 0; i < M; i++) {
-                    const int o = i + tid < M ? i + tid : i + tid - M;   // rotated: the lanes hit distinct banks
-                    const float wv = o == tid ? INFINITY : sh_w[tid * M + o];
+            if (r_lp < M && part_lp < M && sh_alive[r_lp]) {
+                const int n8 = (M - part_lp + LP - 1) / LP;   // partners of this lane (>= 1)
+                const int rot = r_lp % n8;                    // rotated start: the rows hit distinct banks
+                for (int i = 0; i < n8; i++) {
+                    const int o = part_lp + LP * (i + rot < n8 ? i + rot : i + rot - n8);
+                    const float wv = o == r_lp ? INFINITY : sh_w[r_lp * M + o];
                     if (wv < bc || (wv == bc && wv < INFINITY && o < best)) {
                         bc = wv;
                         best = o;
                     }
                 }
-            sh_nn[tid] = best;
-            sh_nnc[tid] = bc;
-            sh_into[tid] = -1;
+            }
+#pragma unroll
+            for (int off = 1; off < LP; off <<= 1) {
+                const float oc = __shfl_xor(bc, off, kWave);
+                const int ob = __shfl_xor(best, off, kWave);
+                if (ob >= 0 && (oc < bc || (oc == bc && (best < 0 || ob < best)))) {
+                    bc = oc;
+                    best = ob;
+                }
+            }
+            if (r_lp < M && part_lp == 0) {
+                sh_nn[r_lp] = best;
+                sh_nnc[r_lp] = bc;
+                sh_into[r_lp] = -1;
+            }
         }
         __syncthreads();
         bool pr = false;
@@ -123,13 +142,20 @@ __global__ __launch_bounds__(NT) void bucket_build_kernel(KP P, const float *__r
         const int take = np < count - NB ? np : count - NB;
         if (take == 0)
             break;
-        if (pr) {                                            // rank by (cost, name) among the pairs
+        {   // rank by (cost, name) among the pairs: LP lanes per pair, each over every LP-th bucket
+            const bool rp = r_lp < M && sh_pair[r_lp];
             int rank = 0;
-            for (int a = 0; a < M; a++)
-                if (sh_pair[a] && (sh_nnc[a] < sh_nnc[tid] || (sh_nnc[a] == sh_nnc[tid] && a < tid)))
-                    rank++;
-            if (rank < take)
-                sh_into[sh_nn[tid]] = tid;
+            if (rp) {
+                const float cr = sh_nnc[r_lp];
+                for (int a = part_lp; a < M; a += LP)
+                    if (sh_pair[a] && (sh_nnc[a] < cr || (sh_nnc[a] == cr && a < r_lp)))
+                        rank++;
+            }
+#pragma unroll
+            for (int off = 1; off < LP; off <<= 1)
+                rank += __shfl_xor(rank, off, kWave);
+            if (rp && part_lp == 0 && rank < take)
+                sh_into[sh_nn[r_lp]] = r_lp;
         }
         __syncthreads();
         for (int x = tid; x < M * D; x += NT) {             // S_a += S_o (pairs are disjoint)
